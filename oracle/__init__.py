@@ -1,0 +1,7 @@
+"""CPU oracle of the LaCT layer: test infrastructure, never part of the product path.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it.
+"""
+from .lact_oracle import *  # noqa: F401,F403
+from .lact_oracle import Hyper, MUON_COEFFS  # noqa: F401
