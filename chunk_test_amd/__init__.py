@@ -1,0 +1,19 @@
+"""LaCT large-chunk test-time-training layer on MI355X (gfx950).
+
+The compute path is ``liblact.so`` (HIP kernels behind the C ABI in
+``include/lact.h``); ``chunk_test_amd.lact`` is its ctypes binding.
+"""
+
+from .lact import (  # noqa: F401
+    Config,
+    LactError,
+    alloc_workspace,
+    lact_apply,
+    lact_chunked_forward,
+    lact_update,
+    load_library,
+    mfma_path,
+    profile_enable,
+    profile_read,
+    workspace_bytes,
+)

@@ -1,0 +1,434 @@
+// Generic kernels of the LaCT layer: fp32 arithmetic for every supported
+// (d, h), fp32 or bf16 activations.  They serve the fp32 I/O mode and any
+// shape that has no MFMA kernel; every step of the layer has one here:
+//   chunk gradient (split over tokens), fixed-order split reduction with
+//   fused momentum, Newton-Schulz, step + row L2 normalisation, query read.
+// The method is the one of "LaCT: Large Chunk Test-Time Training"
+// (iplexlaw.co.kr review), section "Local attention and nonlinear memory
+// work together".
+#include "lact_device.h"
+#include "lact_internal.h"
+
+namespace lact {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTok = 32;  // tokens per LDS tile
+constexpr int kHS = 32;   // hidden units per workgroup
+
+// ---------------------------------------------------------------------------
+// Chunk gradient.  Grid (S splits, h/32 hidden slices, P pairs).  Each
+// workgroup owns 32 hidden units j and the tokens of one split:
+//   h1 = k.W1[j], h3 = k.W3[j], dg = u.W2[:, j]  (u = -eta v)
+//   a = silu(h1), g = a h3, dh3 = dg a, dh1 = dg h3 silu'(h1)
+//   dW1[j] += dh1 k,  dW3[j] += dh3 k,  dW2[:, j] += g u.
+// Tokens past the split end load as zero and contribute nothing.
+// ---------------------------------------------------------------------------
+template <bool BF16, int D>
+__global__ __launch_bounds__(kThreads) void k_grad_generic(GradArgs a) {
+  constexpr int NACC = 3 * kHS * D / kThreads;
+  __shared__ float sW1[kHS][D + 1];
+  __shared__ float sW3[kHS][D + 1];
+  __shared__ float sW2[D][kHS + 1];
+  __shared__ float sK[kTok][D + 1];
+  __shared__ float sU[kTok][D + 1];
+  __shared__ float sdh1[kTok][kHS + 1];
+  __shared__ float sdh3[kTok][kHS + 1];
+  __shared__ float sg[kTok][kHS + 1];
+
+  const int split = blockIdx.x;
+  const int j0 = blockIdx.y * kHS;
+  const int pair = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int h = a.h;
+  const int64_t hd = static_cast<int64_t>(h) * D;
+
+  const float* W1 = a.W1 + pair * hd;
+  const float* W2 = a.W2 + pair * hd;
+  const float* W3 = a.W3 + pair * hd;
+  for (int i = tid; i < kHS * D; i += kThreads) {
+    const int jj = i / D, e = i % D;
+    sW1[jj][e] = W1[(j0 + jj) * D + e];
+    sW3[jj][e] = W3[(j0 + jj) * D + e];
+  }
+  for (int i = tid; i < D * kHS; i += kThreads) {
+    const int e = i / kHS, jj = i % kHS;
+    sW2[e][jj] = W2[e * h + j0 + jj];
+  }
+
+  float acc[NACC];
+#pragma unroll
+  for (int q = 0; q < NACC; ++q) acc[q] = 0.f;
+
+  const int64_t t_begin = static_cast<int64_t>(split) * a.tps;
+  const int64_t t_end = min(a.n, t_begin + a.tps);
+  const int64_t kv_base = static_cast<int64_t>(pair) * a.kv_stride;
+  const float* eta = a.eta + static_cast<int64_t>(pair) * a.eta_stride;
+
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += kTok) {
+    __syncthreads();
+    for (int i = tid; i < kTok * D; i += kThreads) {
+      const int t = i / D, e = i % D;
+      const int64_t tok = t0 + t;
+      float kv = 0.f, u = 0.f;
+      if (tok < t_end) {
+        kv = load_io<BF16>(a.K, kv_base + tok * D + e);
+        u = -eta[tok] * load_io<BF16>(a.V, kv_base + tok * D + e);
+      }
+      sK[t][e] = kv;
+      sU[t][e] = u;
+    }
+    __syncthreads();
+    {
+      const int jj = tid % kHS;
+      const int tb = tid / kHS;
+#pragma unroll
+      for (int r = 0; r < kTok / (kThreads / kHS); ++r) {
+        const int t = tb + (kThreads / kHS) * r;
+        float h1 = 0.f, h3 = 0.f, dg = 0.f;
+        for (int e = 0; e < D; ++e) {
+          const float k = sK[t][e];
+          h1 += k * sW1[jj][e];
+          h3 += k * sW3[jj][e];
+          dg += sU[t][e] * sW2[e][jj];
+        }
+        const float s = sigmoid_f(h1);
+        const float act = h1 * s;
+        sg[t][jj] = act * h3;
+        sdh3[t][jj] = dg * act;
+        sdh1[t][jj] = dg * h3 * (s * (1.f + h1 * (1.f - s)));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NACC; ++q) {
+      const int idx = tid + kThreads * q;
+      float s = 0.f;
+      if (idx < kHS * D) {
+        const int jj = idx / D, e = idx % D;
+        for (int t = 0; t < kTok; ++t) s += sdh1[t][jj] * sK[t][e];
+      } else if (idx < 2 * kHS * D) {
+        const int i2 = idx - kHS * D;
+        const int jj = i2 / D, e = i2 % D;
+        for (int t = 0; t < kTok; ++t) s += sdh3[t][jj] * sK[t][e];
+      } else {
+        const int i3 = idx - 2 * kHS * D;
+        const int e = i3 / kHS, jj = i3 % kHS;
+        for (int t = 0; t < kTok; ++t) s += sU[t][e] * sg[t][jj];
+      }
+      acc[q] += s;
+    }
+  }
+
+  float* out = a.partials + (static_cast<int64_t>(pair) * a.S + split) * 3 * hd;
+#pragma unroll
+  for (int q = 0; q < NACC; ++q) {
+    const int idx = tid + kThreads * q;
+    if (idx < kHS * D) {
+      const int jj = idx / D, e = idx % D;
+      out[(j0 + jj) * D + e] = acc[q];
+    } else if (idx < 2 * kHS * D) {
+      const int i2 = idx - kHS * D;
+      const int jj = i2 / D, e = i2 % D;
+      out[2 * hd + (j0 + jj) * D + e] = acc[q];
+    } else {
+      const int i3 = idx - 2 * kHS * D;
+      const int e = i3 / kHS, jj = i3 % kHS;
+      out[hd + e * h + j0 + jj] = acc[q];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split reduction in fixed order s = 0..S-1, momentum fused.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_reduce(ReduceArgs a) {
+  const int64_t hd = static_cast<int64_t>(a.h) * a.d;
+  const int64_t per = 3 * hd;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= per * a.P) return;
+  const int64_t pair = i / per, e = i % per;
+  const float* src = a.partials + pair * a.S * per + e;
+  float g = 0.f;
+  for (int s = 0; s < a.S; ++s) g += src[static_cast<int64_t>(s) * per];
+  if (a.M1 != nullptr) {
+    float* M;
+    int64_t off;
+    if (e < hd) {
+      M = a.M1;
+      off = e;
+    } else if (e < 2 * hd) {
+      M = a.M2;
+      off = e - hd;
+    } else {
+      M = a.M3;
+      off = e - 2 * hd;
+    }
+    const float m = a.beta * M[pair * hd + off] + g;
+    M[pair * hd + off] = m;
+    g = m;
+  }
+  a.dir[i] = g;
+}
+
+// ---------------------------------------------------------------------------
+// Newton-Schulz, one workgroup per matrix, operands in global scratch.
+// X is s x l with s = min(rows, cols); X0 = G / (||G||_F + eps);
+//   A = X X^T;  B = b A + c A A;  X <- a X + B X.
+// ---------------------------------------------------------------------------
+constexpr int kNSThreads = 512;
+
+__global__ __launch_bounds__(kNSThreads) void k_ns_generic(NSArgs a) {
+  __shared__ float red[kNSThreads];
+  const int mat = blockIdx.x;
+  const int pair = mat / 3, which = mat % 3;  // 0: W1, 1: W2, 2: W3
+  const int64_t hd = static_cast<int64_t>(a.h) * a.d;
+  float* G = a.dir + pair * 3 * hd + which * hd;
+  const int rows = (which == 1) ? a.d : a.h;
+  const int cols = (which == 1) ? a.h : a.d;
+  const bool tr = rows > cols;
+  const int s = tr ? cols : rows;
+  const int l = tr ? rows : cols;
+  const int64_t sl = static_cast<int64_t>(s) * l, ss = static_cast<int64_t>(s) * s;
+  float* X = a.scratch + static_cast<int64_t>(mat) * (2 * sl + 2 * ss);
+  float* Xn = X + sl;
+  float* A = Xn + sl;
+  float* Bm = A + ss;
+  const int tid = threadIdx.x;
+
+  float part = 0.f;
+  for (int64_t i = tid; i < sl; i += kNSThreads) part += G[i] * G[i];
+  red[tid] = part;
+  __syncthreads();
+  for (int w = kNSThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
+    __syncthreads();
+  }
+  const float denom = sqrtf(red[0]) + a.eps;
+  for (int64_t idx = tid; idx < sl; idx += kNSThreads) {
+    const int i = static_cast<int>(idx / l), j = static_cast<int>(idx % l);
+    X[idx] = (tr ? G[static_cast<int64_t>(j) * cols + i] : G[static_cast<int64_t>(i) * cols + j]) / denom;
+  }
+  __syncthreads();
+  for (int it = 0; it < a.iters; ++it) {
+    for (int64_t idx = tid; idx < ss; idx += kNSThreads) {
+      const int i = static_cast<int>(idx / s), k = static_cast<int>(idx % s);
+      const float* xi = X + static_cast<int64_t>(i) * l;
+      const float* xk = X + static_cast<int64_t>(k) * l;
+      float acc = 0.f;
+      for (int j = 0; j < l; ++j) acc += xi[j] * xk[j];
+      A[idx] = acc;
+    }
+    __syncthreads();
+    for (int64_t idx = tid; idx < ss; idx += kNSThreads) {
+      const int i = static_cast<int>(idx / s), k = static_cast<int>(idx % s);
+      float acc = 0.f;
+      for (int m = 0; m < s; ++m) acc += A[static_cast<int64_t>(i) * s + m] * A[static_cast<int64_t>(m) * s + k];
+      Bm[idx] = a.b * A[idx] + a.c * acc;
+    }
+    __syncthreads();
+    for (int64_t idx = tid; idx < sl; idx += kNSThreads) {
+      const int i = static_cast<int>(idx / l), j = static_cast<int>(idx % l);
+      float acc = 0.f;
+      for (int m = 0; m < s; ++m) acc += Bm[static_cast<int64_t>(i) * s + m] * X[static_cast<int64_t>(m) * l + j];
+      Xn[idx] = a.a * X[idx] + acc;
+    }
+    __syncthreads();
+    float* t = X;
+    X = Xn;
+    Xn = t;
+  }
+  for (int64_t idx = tid; idx < sl; idx += kNSThreads) {
+    const int i = static_cast<int>(idx / l), j = static_cast<int>(idx % l);
+    if (tr) {
+      G[static_cast<int64_t>(j) * cols + i] = X[idx];
+    } else {
+      G[static_cast<int64_t>(i) * cols + j] = X[idx];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// W <- W - step * dir, then every row to unit L2 norm.  One wavefront per
+// row; rows of W1 and W3 have d entries, rows of W2 have h (<= 1024).
+// ---------------------------------------------------------------------------
+constexpr int kMaxRowPerLane = 16;
+
+__global__ __launch_bounds__(kThreads) void k_step_norm(StepArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  const int R = 2 * a.h + a.d;
+  const int64_t pair = row / R;
+  if (pair >= a.P) return;
+  const int r = static_cast<int>(row % R);
+  const int64_t hd = static_cast<int64_t>(a.h) * a.d;
+  float* W;
+  const float* dr;
+  int len;
+  if (r < a.h) {
+    W = a.W1 + pair * hd + static_cast<int64_t>(r) * a.d;
+    dr = a.dir + pair * 3 * hd + static_cast<int64_t>(r) * a.d;
+    len = a.d;
+  } else if (r < 2 * a.h) {
+    W = a.W3 + pair * hd + static_cast<int64_t>(r - a.h) * a.d;
+    dr = a.dir + pair * 3 * hd + 2 * hd + static_cast<int64_t>(r - a.h) * a.d;
+    len = a.d;
+  } else {
+    W = a.W2 + pair * hd + static_cast<int64_t>(r - 2 * a.h) * a.h;
+    dr = a.dir + pair * 3 * hd + hd + static_cast<int64_t>(r - 2 * a.h) * a.h;
+    len = a.h;
+  }
+  float v[kMaxRowPerLane];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxRowPerLane; ++k) {
+    const int e = lane + 64 * k;
+    v[k] = 0.f;
+    if (e < len) {
+      v[k] = W[e] - a.step * dr[e];
+      ss += v[k] * v[k];
+    }
+  }
+  ss = wave_sum(ss);
+  const float den = fmaxf(sqrtf(ss), a.norm_eps);
+#pragma unroll
+  for (int k = 0; k < kMaxRowPerLane; ++k) {
+    const int e = lane + 64 * k;
+    if (e < len) W[e] = v[k] / den;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Query read O = W2 (silu(W1 q) * (W3 q)).  Grid (ceil(m/32), P); hidden
+// units in slices of 256 staged through LDS.
+// ---------------------------------------------------------------------------
+constexpr int kQT = 32;
+constexpr int kApplyHS = 256;
+
+template <bool BF16, int D>
+__global__ __launch_bounds__(kThreads) void k_apply_generic(ApplyArgs a) {
+  constexpr int NACC = kQT * D / kThreads;
+  __shared__ float sQ[kQT][D + 1];
+  __shared__ float sG[kQT][kApplyHS + 1];
+  const int pair = blockIdx.y;
+  const int64_t q0 = static_cast<int64_t>(blockIdx.x) * kQT;
+  const int tid = threadIdx.x;
+  const int h = a.h;
+  const int64_t hd = static_cast<int64_t>(h) * D;
+  const int64_t base = static_cast<int64_t>(pair) * a.q_stride;
+  const float* W1 = a.W1 + pair * hd;
+  const float* W2 = a.W2 + pair * hd;
+  const float* W3 = a.W3 + pair * hd;
+
+  for (int i = tid; i < kQT * D; i += kThreads) {
+    const int t = i / D, e = i % D;
+    sQ[t][e] = (q0 + t < a.m) ? load_io<BF16>(a.Q, base + (q0 + t) * D + e) : 0.f;
+  }
+  float acc[NACC];
+#pragma unroll
+  for (int q = 0; q < NACC; ++q) acc[q] = 0.f;
+
+  for (int j0 = 0; j0 < h; j0 += kApplyHS) {
+    const int hs = min(kApplyHS, h - j0);
+    __syncthreads();
+    for (int i = tid; i < kQT * hs; i += kThreads) {
+      const int t = i / hs, jj = i % hs;
+      const float* w1 = W1 + static_cast<int64_t>(j0 + jj) * D;
+      const float* w3 = W3 + static_cast<int64_t>(j0 + jj) * D;
+      float h1 = 0.f, h3 = 0.f;
+      for (int e = 0; e < D; ++e) {
+        h1 += sQ[t][e] * w1[e];
+        h3 += sQ[t][e] * w3[e];
+      }
+      sG[t][jj] = h1 * sigmoid_f(h1) * h3;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < NACC; ++q) {
+      const int idx = tid + kThreads * q;
+      const int t = idx / D, e = idx % D;
+      const float* w2 = W2 + static_cast<int64_t>(e) * h + j0;
+      float s = 0.f;
+      for (int jj = 0; jj < hs; ++jj) s += sG[t][jj] * w2[jj];
+      acc[q] += s;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < NACC; ++q) {
+    const int idx = tid + kThreads * q;
+    const int t = idx / D, e = idx % D;
+    if (q0 + t < a.m) store_io<BF16>(a.O, base + (q0 + t) * D + e, acc[q]);
+  }
+}
+
+template <int D>
+hipError_t grad_d(const GradArgs& a, hipStream_t s) {
+  dim3 grid(a.S, a.h / kHS, a.P);
+  if (a.bf16) {
+    hipLaunchKernelGGL((k_grad_generic<true, D>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_grad_generic<false, D>), grid, dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t apply_d(const ApplyArgs& a, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>((a.m + kQT - 1) / kQT), a.P);
+  if (a.bf16) {
+    hipLaunchKernelGGL((k_apply_generic<true, D>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((k_apply_generic<false, D>), grid, dim3(kThreads), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool simple_shape_ok(int d, int h) {
+  return (d == 32 || d == 64 || d == 128) && h >= kHS && h <= 64 * kMaxRowPerLane && h % kHS == 0;
+}
+
+size_t ns_simple_scratch_floats(int P, int d, int h) {
+  const size_t s = d < h ? d : h, l = d < h ? h : d;
+  return static_cast<size_t>(3) * P * (2 * s * l + 2 * s * s);
+}
+
+hipError_t launch_grad_simple(const GradArgs& a, hipStream_t s) {
+  switch (a.d) {
+    case 32: return grad_d<32>(a, s);
+    case 64: return grad_d<64>(a, s);
+    case 128: return grad_d<128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_apply_simple(const ApplyArgs& a, hipStream_t s) {
+  switch (a.d) {
+    case 32: return apply_d<32>(a, s);
+    case 64: return apply_d<64>(a, s);
+    case 128: return apply_d<128>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
+  const int64_t total = static_cast<int64_t>(a.P) * 3 * a.h * a.d;
+  const unsigned blocks = static_cast<unsigned>((total + kThreads - 1) / kThreads);
+  hipLaunchKernelGGL(k_reduce, dim3(blocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_ns_simple(const NSArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_ns_generic, dim3(3 * a.P), dim3(kNSThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_norm(const StepArgs& a, hipStream_t s) {
+  const int64_t rows = static_cast<int64_t>(a.P) * (2 * a.h + a.d);
+  const unsigned blocks = static_cast<unsigned>((rows + 3) / 4);
+  hipLaunchKernelGGL(k_step_norm, dim3(blocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace lact

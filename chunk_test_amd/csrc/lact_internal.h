@@ -1,0 +1,75 @@
+// Internal interface between the C ABI host code and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lact {
+
+// Arguments of the chunk-gradient kernels: partial sums of
+//   dW1 = dH1^T K,  dW2 = U^T G,  dW3 = dH3^T K   (U = -eta * V)
+// over the tokens of one split, written to partials[pair][split][3hd] in the
+// order [W1 block (h x d) | W2 block (d x h) | W3 block (h x d)].
+struct GradArgs {
+  const void* K;
+  const void* V;
+  const float* eta;
+  int64_t n;           // keys in the chunk
+  int64_t kv_stride;   // elements between pairs in K and V
+  int64_t eta_stride;  // elements between pairs in eta
+  const float* W1;     // [P, h, d]
+  const float* W2;     // [P, d, h]
+  const float* W3;     // [P, h, d]
+  float* partials;     // [P, S, 3hd]
+  int P, d, h, S;
+  int64_t tps;         // tokens per split (the last split may be shorter)
+  int bf16;            // K, V are bfloat16
+};
+
+// Fixed-order sum of the split partials, with the momentum update fused:
+//   g = sum_s partials[p][s];  if M: M <- beta M + g, g <- M;  dir[p] = g.
+struct ReduceArgs {
+  const float* partials;  // [P, S, 3hd]
+  float* dir;             // [P, 3hd]
+  float *M1, *M2, *M3;    // momentum buffers or NULL
+  float beta;
+  int P, d, h, S;
+};
+
+// Newton-Schulz on each of the 3P matrices held in dir (in place).
+struct NSArgs {
+  float* dir;      // [P, 3hd]
+  float* scratch;  // simple path: 3P * (2 s l + 2 s s) floats
+  int P, d, h, iters;
+  float a, b, c, eps;
+};
+
+// W <- W - step * dir, then unit L2 rows.
+struct StepArgs {
+  float *W1, *W2, *W3;
+  const float* dir;  // [P, 3hd]
+  float step, norm_eps;
+  int P, d, h;
+};
+
+// O = f_W(Q) for m queries per pair.
+struct ApplyArgs {
+  const void* Q;
+  void* O;
+  int64_t m;
+  int64_t q_stride;
+  const float *W1, *W2, *W3;
+  int P, d, h;
+  int bf16;
+};
+
+// ---- generic kernels (fp32 arithmetic; any supported d, h) ----
+hipError_t launch_grad_simple(const GradArgs& a, hipStream_t s);
+hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
+hipError_t launch_ns_simple(const NSArgs& a, hipStream_t s);
+hipError_t launch_step_norm(const StepArgs& a, hipStream_t s);
+hipError_t launch_apply_simple(const ApplyArgs& a, hipStream_t s);
+bool simple_shape_ok(int d, int h);
+size_t ns_simple_scratch_floats(int P, int d, int h);
+
+}  // namespace lact

@@ -1,0 +1,161 @@
+/*
+ * lact.h - C ABI of the LaCT large-chunk test-time-training layer on gfx950.
+ *
+ * What the layer computes (the text of "LaCT: Large Chunk Test-Time
+ * Training", iplexlaw.co.kr review, sections "Local attention and nonlinear
+ * memory work together" and "Update order must respect the task"; "Test-Time
+ * Training Done Right", Abstract and project page Figure 2):
+ *
+ *   per (batch, head) pair the fast weights are a SwiGLU MLP
+ *       f_W(x) = W2 (silu(W1 x) * (W3 x)),  W1, W3: [h x d],  W2: [d x h];
+ *   for every chunk of keys/values (2K .. ~1M tokens) the layer
+ *     (1) reads f_W(q) for the chunk's queries,
+ *     (2) takes the gradient of L = - sum_i eta_i <f_W(k_i), v_i> over the
+ *         whole chunk (eta_i: a per-token learning rate),
+ *     (3) applies plain GD, heavy-ball momentum, or Muon (Newton-Schulz
+ *         orthogonalisation of each matrix gradient),
+ *     (4) L2-normalises every row of the updated W1, W3 (length d) and W2
+ *         (length h);
+ *   (1) runs before (2)-(4) for causal text/video (apply-then-update) and
+ *   after them for posed image sets (update-then-apply).  W is carried from
+ *   chunk to chunk.
+ *
+ * Conventions shared by every entry point
+ *   - All buffers are DEVICE memory owned by the caller.  The library never
+ *     allocates device memory and never synchronises the host: every call
+ *     validates its arguments on the host, then enqueues kernels on `stream`
+ *     (a hipStream_t; NULL = the null stream) and returns.  Errors of the
+ *     kernels themselves surface at the caller's next synchronisation.
+ *   - Layouts (row-major, elements, not bytes):
+ *       Q, O: [B, H, T_q, d];  K, V: [B, H, T_kv, d];  eta: [B, H, T_kv];
+ *       W1, W3, M1, M3: [B, H, h, d];  W2, M2: [B, H, d, h].
+ *     Rows of one pair are contiguous; consecutive pairs are `*_stride_bh`
+ *     elements apart (so chunk views of a longer sequence can be passed).
+ *   - io_dtype LACT_F32: Q, K, V, O are float.  LACT_BF16: they are
+ *     bfloat16 (raw 16-bit words); products use bf16 operands with fp32
+ *     accumulation.  eta, W and M are always float.
+ *   - The state is updated in place.  M1..M3 must be non-NULL (and are
+ *     read and written) exactly when the optimizer keeps a momentum buffer:
+ *     opt == LACT_OPT_MOMENTUM, or opt == LACT_OPT_MUON with beta > 0.
+ *     Zero them before the first chunk.
+ *   - Scratch: `ws` (device, 256-byte aligned) of at least
+ *     lact_workspace_bytes(...) bytes; its contents need no initialisation
+ *     and are not meaningful after the call.  Two calls in flight at once
+ *     must not share a workspace.
+ *   - Results are deterministic: a fixed launch plan derived from the
+ *     shapes only, and fixed-order reductions.
+ *   - Return value: LACT_OK or a negative lact_status.  Nothing is enqueued
+ *     when validation fails.  lact_last_error() gives a thread-local text.
+ *   - NaN / Inf inputs propagate; there is no device-side check.
+ */
+#ifndef LACT_H
+#define LACT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LACT_OK = 0,
+  LACT_ERR_INVALID_ARG = -1, /* NULL pointer, non-positive size, chunks that do not divide T, ... */
+  LACT_ERR_UNSUPPORTED = -2, /* a shape / dtype / optimizer combination that is not built      */
+  LACT_ERR_WORKSPACE = -3,   /* ws too small or misaligned                                       */
+  LACT_ERR_HIP = -4          /* a HIP launch error (text in lact_last_error())                  */
+} lact_status;
+
+typedef enum { LACT_F32 = 0, LACT_BF16 = 1 } lact_dtype;
+
+/* Read/update order ("Update order must respect the task"). */
+typedef enum { LACT_APPLY_THEN_UPDATE = 0, LACT_UPDATE_THEN_APPLY = 1 } lact_order;
+
+/* Update rule ("Local attention and nonlinear memory work together"). */
+typedef enum { LACT_OPT_GD = 0, LACT_OPT_MOMENTUM = 1, LACT_OPT_MUON = 2 } lact_opt;
+
+typedef struct {
+  int32_t B, H;      /* batch and heads: P = B*H independent pairs                        */
+  int32_t d, h;      /* head dim and SwiGLU hidden dim                                    */
+  int32_t io_dtype;  /* lact_dtype of Q, K, V, O                                          */
+  int32_t opt;       /* lact_opt                                                          */
+  float beta;        /* momentum coefficient in [0, 1): M <- beta M + grad               */
+  int32_t ns_iters;  /* Newton-Schulz iterations (Muon), 0..32                            */
+  float ns_a, ns_b, ns_c; /* X <- a X + (b A + c A A) X, A = X X^T                        */
+  float ns_eps;      /* X0 = G / (||G||_F + ns_eps)                                       */
+  float step;        /* W <- W - step * direction                                         */
+  float norm_eps;    /* row r <- r / max(||r||_2, norm_eps)                               */
+} lact_config;
+
+typedef struct {
+  float *W1, *W2, *W3; /* fast weights (in/out)                                           */
+  float *M1, *M2, *M3; /* momentum buffers (in/out) or NULL, see above                    */
+} lact_state;
+
+/* Defaults: opt GD, beta 0, ns_iters 5, (a,b,c) = (3.4445, -4.7750, 2.0315)
+ * (the quintic published with the Muon optimizer; the pages only name
+ * Newton-Schulz), ns_eps 1e-7, step 1, norm_eps 1e-12, io_dtype LACT_BF16.
+ * B, H, d, h are set to 0 and must be filled in. */
+void lact_config_default(lact_config* cfg);
+
+/* Bytes of scratch that lact_update / lact_apply / lact_chunked_forward
+ * need for chunks of at most `max_chunk_kv` keys and `max_chunk_q`
+ * queries.  Pure host function.  Returns 0 for an invalid or unsupported
+ * configuration. */
+size_t lact_workspace_bytes(const lact_config* cfg, int64_t max_chunk_kv, int64_t max_chunk_q);
+
+/* One large-chunk update of every pair: steps (2)-(4) above on n keys.
+ * K, V: pair p's rows start at K + p*kv_stride_bh (elements); eta: pair p
+ * starts at eta + p*eta_stride_bh.  n >= 1 (any n: ragged tails are
+ * handled).  The state is read and written. */
+int lact_update(const lact_config* cfg, const lact_state* st,
+                const void* K, const void* V, const float* eta,
+                int64_t n, int64_t kv_stride_bh, int64_t eta_stride_bh,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* Query read, step (1) above: O = f_W(Q) row by row for m queries of every
+ * pair.  Q and O rows of pair p start at p*q_stride_bh.  The state is only
+ * read.  m >= 1. */
+int lact_apply(const lact_config* cfg, const lact_state* st,
+               const void* Q, void* O, int64_t m, int64_t q_stride_bh,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* The whole layer: a sequential scan over N = T_kv / chunk_kv chunks
+ * (T_q / chunk_q must equal N).  Chunk c updates with keys
+ * [c*chunk_kv, (c+1)*chunk_kv) and reads for queries
+ * [c*chunk_q, (c+1)*chunk_q), in `order` (lact_order).  The last update
+ * always runs, so the state on return is W after all chunks.  Inputs are
+ * contiguous [B, H, T, d] (eta [B, H, T_kv]). */
+int lact_chunked_forward(const lact_config* cfg, const lact_state* st,
+                         const void* Q, const void* K, const void* V, const float* eta,
+                         void* O, int64_t T_kv, int64_t T_q, int64_t chunk_kv,
+                         int64_t chunk_q, int32_t order, void* ws, size_t ws_bytes,
+                         void* stream);
+
+/* Static text of a status code. */
+const char* lact_status_string(int status);
+
+/* Thread-local text of the last failure on this thread ("" if none). */
+const char* lact_last_error(void);
+
+/* 1 when the bf16 MFMA kernels serve (d, h); 0 when the generic fp32-math
+ * kernels do; -1 when (d, h) is not supported at all. */
+int lact_mfma_path(int32_t d, int32_t h, int32_t io_dtype);
+
+/* Kernel timing for measurement tools (not thread-safe; off by default).
+ * While enabled, every entry point records HIP events on its stream around
+ * each phase; lact_profile_read() waits for the recorded events, adds their
+ * durations into ms[phase] / launches[phase] (arrays of LACT_PROFILE_PHASES)
+ * and clears the record.  Phases: 0 gradient, 1 split reduction (+momentum),
+ * 2 Newton-Schulz, 3 step + row normalisation, 4 query read. */
+#define LACT_PROFILE_PHASES 5
+int lact_profile_enable(int on);
+int lact_profile_read(double* ms, int64_t* launches);
+
+int lact_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LACT_H */

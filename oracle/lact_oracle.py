@@ -360,23 +360,21 @@ def lact_chunked_forward(state, Q, K, V, eta, chunk_kv, chunk_q, order, hp: Hype
     other outputs stay zero and their state is copied unchanged); the pairs
     are independent, so this is how large configurations are sampled.
     """
-    Q = np.asarray(Q, dtype=dtype)
-    K = np.asarray(K, dtype=dtype)
-    V = np.asarray(V, dtype=dtype)
-    eta = np.asarray(eta, dtype=dtype)
     B, H = K.shape[:2]
     new = {k: np.array(v, dtype=dtype, copy=True) for k, v in state.items()}
     if hp.uses_momentum():
         for n in ("M1", "M2", "M3"):
             new.setdefault(n, np.zeros_like(new["W" + n[1]]))
-    O = np.zeros_like(Q)
+    O = np.zeros(Q.shape, dtype=dtype)
     todo = list(_pairs(B, H)) if pairs is None else list(pairs)
     for b, h in todo:
+        # inputs are cast one pair at a time to bound host memory
+        cast = lambda x: np.asarray(x[b, h], dtype=dtype)
         W = tuple(new[n][b, h] for n in ("W1", "W2", "W3"))
         M = (tuple(new[n][b, h] for n in ("M1", "M2", "M3"))
              if hp.uses_momentum() else None)
-        O[b, h], W, M = chunked_forward_pair(W, M, Q[b, h], K[b, h], V[b, h],
-                                             eta[b, h], chunk_kv, chunk_q, order, hp)
+        O[b, h], W, M = chunked_forward_pair(W, M, cast(Q), cast(K), cast(V), cast(eta),
+                                             chunk_kv, chunk_q, order, hp)
         for n, x in zip(("W1", "W2", "W3"), W):
             new[n][b, h] = x
         if M is not None:

@@ -1,0 +1,173 @@
+"""GPU parity of the HIP path against the float64 oracle.
+
+The library is called through the C ABI (ctypes binding).  Bars: max rel err
+(max_i |x_i - y_i| / max_i |y_i| per tensor) <= 1e-4 in fp32 I/O mode and
+<= 2e-2 in bf16 mode, on O and on the final W1, W2, W3 (and M), after all
+chunks.  Full-size workloads run every pair on the GPU and compare sampled
+(batch, head) pairs with the oracle (pairs are independent).
+"""
+
+import numpy as np
+import pytest
+
+import lact_synth as S
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+TINY = S.WORKLOADS["tiny"]
+
+
+def small(name, **kw):
+    return S.WORKLOADS[name].replace(name=f"{name}-small", **kw)
+
+
+SMALL_CASES = [
+    TINY,
+    TINY.replace(name="tiny-uta", order="update_then_apply"),
+    TINY.replace(name="tiny-momentum", opt="momentum", beta=0.9),
+    TINY.replace(name="tiny-muon", opt="muon"),
+    TINY.replace(name="tiny-muon-momentum", opt="muon", beta=0.5, order="update_then_apply"),
+    # ragged chunks: 3 chunks of 300 keys (not a multiple of any tile), 50 queries
+    TINY.replace(name="tiny-ragged", T_kv=900, chunk_kv=300, T_q=150, chunk_q=50, opt="muon"),
+    TINY.replace(name="fp32-d128", B=2, H=2, d=128, h=256, opt="momentum", beta=0.9),
+    TINY.replace(name="fp32-d32", B=1, H=3, d=32, h=64, opt="muon"),
+    TINY.replace(name="fp32-d64-h256", H=2, h=256, opt="gd", order="update_then_apply"),
+    small("lm", B=2, H=2, T_kv=4096, T_q=4096, chunk_kv=1024, chunk_q=1024),
+    small("posed", H=2, T_kv=16384, T_q=512, chunk_kv=16384, chunk_q=512),
+    small("video", H=2, T_kv=3 * 4096, T_q=3 * 4096),
+    small("million", H=2, T_kv=40000, T_q=1000, chunk_kv=40000, chunk_q=1000),
+]
+
+
+@pytest.mark.parametrize("w", SMALL_CASES, ids=[w.name for w in SMALL_CASES])
+def test_small_parity(w):
+    G.say(f"case {w.name}")
+    st = S.gen_weights(w)
+    x = S.gen_inputs(w)
+    O, st_gpu = G.run_gpu(w, x, st)
+    O_ref, st_ref = G.run_oracle(w, x, st)
+    _, bad = G.compare(w, O, st_gpu, O_ref, st_ref)
+    assert not bad, bad
+
+
+FULL = [
+    ("posed", [(0, 0), (0, 7)]),
+    ("million", [(0, 3)]),
+    ("lm", [(0, 0), (5, 3)]),
+    ("video", [(0, 0), (0, 39)]),
+]
+
+
+@pytest.mark.parametrize("name,pairs", FULL, ids=[f[0] for f in FULL])
+def test_full_size_sampled_parity(name, pairs):
+    w = S.WORKLOADS[name]
+    G.say(f"case {name} full size, oracle pairs {pairs}")
+    st = S.gen_weights(w)
+    x = S.gen_inputs(w)
+    O, st_gpu = G.run_gpu(w, x, st)
+    O_ref, st_ref = G.run_oracle(w, x, st, pairs=pairs)
+    _, bad = G.compare(w, O, st_gpu, O_ref, st_ref, pairs=pairs)
+    assert not bad, bad
+    # properties that hold for every pair: unit rows, finite outputs
+    for n in ("W1", "W2", "W3"):
+        norms = np.linalg.norm(st_gpu[n], axis=-1)
+        assert np.max(np.abs(norms - 1.0)) < 1e-4, n
+    assert np.all(np.isfinite(O))
+
+
+def test_deterministic_repeat():
+    w = SMALL_CASES[10]
+    st = S.gen_weights(w)
+    x = S.gen_inputs(w)
+    O1, s1 = G.run_gpu(w, x, st)
+    O2, s2 = G.run_gpu(w, x, st)
+    assert np.array_equal(O1, O2)
+    for n in s1:
+        assert np.array_equal(s1[n], s2[n]), n
+
+
+def test_resume_split_run_is_bitwise_equal():
+    import torch
+    import chunk_test_amd as L
+    w = small("lm", B=1, H=2, T_kv=4096, T_q=4096, chunk_kv=1024, chunk_q=1024)
+    st = S.gen_weights(w)
+    x = S.gen_inputs(w)
+    O_full, s_full = G.run_gpu(w, x, st)
+    cfg = G.config_of(w)
+    dst = G.device_state(w, st)
+    Q, K, V = (G.to_dev(x[n], w) for n in ("Q", "K", "V"))
+    eta = G.to_dev(x["eta"], w, io=False)
+    ws = L.alloc_workspace(cfg, w.chunk_kv, w.chunk_q)
+    O = torch.empty_like(Q)
+    for lo, hi in ((0, 2048), (2048, 4096)):
+        q, k, v = (t[:, :, lo:hi].contiguous() for t in (Q, K, V))
+        e = eta[:, :, lo:hi].contiguous()
+        o = torch.empty_like(q)
+        L.lact_chunked_forward(cfg, dst, q, k, v, e, o, w.chunk_kv, w.chunk_q, w.order, ws)
+        O[:, :, lo:hi] = o
+    torch.cuda.synchronize()
+    assert np.array_equal(O.float().cpu().numpy(), O_full)
+    for n in s_full:
+        assert np.array_equal(dst[n].cpu().numpy(), s_full[n]), n
+
+
+def test_update_and_apply_entry_points_and_strided_views():
+    import torch
+    import chunk_test_amd as L
+    w = TINY.replace(name="entry", H=2, opt="muon")
+    st = S.gen_weights(w)
+    x = S.gen_inputs(w)
+    cfg = G.config_of(w)
+    # one chunk via the scan
+    w1 = w.replace(T_kv=256, T_q=256)
+    x1 = {k: (v[:, :, :256] if v.ndim >= 3 else v).copy() for k, v in x.items()}
+    O_scan, s_scan = G.run_gpu(w1, x1, st)
+    # the same chunk through lact_apply + lact_update on strided views of
+    # the full-length tensors
+    dst = G.device_state(w, st)
+    Q, K, V = (G.to_dev(x[n], w) for n in ("Q", "K", "V"))
+    eta = G.to_dev(x["eta"], w, io=False)
+    ws = L.alloc_workspace(cfg, 256, 256)
+    O = torch.zeros_like(Q)
+    L.lact_apply(cfg, dst, Q, O, ws=ws, m=256, q_stride_bh=w.T_q * w.d)
+    L.lact_update(cfg, dst, K, V, eta, ws, n=256, kv_stride_bh=w.T_kv * w.d, eta_stride_bh=w.T_kv)
+    torch.cuda.synchronize()
+    assert np.array_equal(O[:, :, :256].cpu().numpy(), O_scan)
+    assert np.all(O[:, :, 256:].cpu().numpy() == 0)  # nothing written past m
+    for n in ("W1", "W2", "W3"):
+        assert np.array_equal(dst[n].cpu().numpy(), s_scan[n]), n
+
+
+def test_edge_sizes_one_token_one_query():
+    w = TINY.replace(name="one-token", T_kv=3, chunk_kv=1, T_q=3, chunk_q=1, opt="muon")
+    st = S.gen_weights(w)
+    x = S.gen_inputs(w)
+    O, s = G.run_gpu(w, x, st)
+    O_ref, s_ref = G.run_oracle(w, x, st)
+    _, bad = G.compare(w, O, s, O_ref, s_ref)
+    assert not bad, bad
+
+
+def test_eta_zero_leaves_normalised_initial_weights():
+    w = small("posed", H=2, T_kv=4096, T_q=256, chunk_kv=4096, chunk_q=256)
+    st = S.gen_weights(w)
+    x = S.gen_inputs(w)
+    x["eta"][:] = 0.0
+    O, s = G.run_gpu(w, x, st)
+    for n in ("W1", "W2", "W3"):
+        ref = st[n] / np.linalg.norm(st[n].astype(np.float64), axis=-1, keepdims=True)
+        assert G.rel_err(s[n], ref) < 1e-6, n
+
+
+def test_invalid_arguments_raise_without_launching():
+    import torch
+    import chunk_test_amd as L
+    import dataclasses
+    w = TINY
+    cfg = dataclasses.replace(G.config_of(w), d=60)
+    st = G.device_state(w, S.gen_weights(w))
+    Q = torch.zeros(1, 1, 8, 64, device="cuda")
+    with pytest.raises(L.LactError) as e:
+        L.lact_apply(cfg, st, Q, torch.empty_like(Q))
+    assert e.value.status == -2
