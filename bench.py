@@ -1,0 +1,188 @@
+"""Throughput of the LaCT layer on one MI355X.
+
+One step = one ``lact_chunked_forward`` call: every chunk's query read,
+chunk gradient, optimizer step and row normalisation over one batch of
+synthetic input that is already resident in HBM.  The default workload is
+the posed-image set (196,608 keys as one chunk, 12 heads, d=64, h=128,
+update-then-apply on 4,096 queries, Muon with 5 Newton-Schulz iterations).
+
+Prints ONE JSON line.  ``value`` is the layer's algorithmic TFLOP/s; the
+line also carries tokens/s, the fraction of the bf16 MFMA peak, per-phase
+kernel times from HIP events recorded on the launch stream, the roofline of
+the dominant kernel, and the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import lact_synth as S  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gradient_flops(w: S.Workload) -> float:
+    """Algorithmic flops of one launch of the chunk-gradient kernel (one chunk, all pairs)."""
+    return 12.0 * w.chunk_kv * w.d * w.h * w.pairs
+
+
+def cpu_baseline(w: S.Workload, x, st, budget_s: float = 15.0):
+    """The float32 oracle on a bounded sample: whole pairs of the workload,
+    as many as fit the time budget (at least one)."""
+    import oracle
+    hp = oracle.Hyper(opt=w.opt, beta=w.beta, ns_iters=w.ns_iters, token_block=65536)
+    per_pair = w.flops() / w.pairs
+    done, t_used, pairs = 0, 0.0, []
+    for b in range(w.B):
+        for h in range(w.H):
+            pairs.append((b, h))
+    t0 = time.perf_counter()
+    for p in pairs:
+        oracle.lact_chunked_forward(st, x["Q"], x["K"], x["V"], x["eta"], w.chunk_kv, w.chunk_q,
+                                    w.order, hp, dtype=np.float32, pairs=[p])
+        done += 1
+        t_used = time.perf_counter() - t0
+        if t_used > budget_s:
+            break
+    tflops = done * per_pair / t_used / 1e12
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {
+        "value": round(tflops, 6), "unit": "TFLOP/s", "cores": min(cores, threads), "kind": "oracle",
+        "sample": f"{done} of {w.pairs} (batch, head) pairs of the {w.name} workload, full length, "
+                  f"float32 NumPy oracle, {t_used:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="posed", choices=sorted(S.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is built for a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunk_test_amd as L
+
+    w = S.WORKLOADS[args.workload]
+    log(f"[bench] workload {w.name}: generating inputs")
+    st = S.gen_weights(w)
+    x = S.gen_inputs(w)
+    io = torch.bfloat16 if w.io_dtype == "bf16" else torch.float32
+    cfg = L.Config(B=w.B, H=w.H, d=w.d, h=w.h, io_dtype=w.io_dtype, opt=w.opt, beta=w.beta,
+                   ns_iters=w.ns_iters)
+    dev = {n: torch.from_numpy(st[n]).cuda() for n in ("W1", "W2", "W3")}
+    if cfg.uses_momentum():
+        for n in ("M1", "M2", "M3"):
+            dev[n] = torch.zeros_like(dev["W" + n[1]])
+    Q, K, V = (torch.from_numpy(x[n]).cuda().to(io) for n in ("Q", "K", "V"))
+    eta = torch.from_numpy(x["eta"]).cuda()
+    O = torch.empty_like(Q)
+    ws = L.alloc_workspace(cfg, w.chunk_kv, w.chunk_q)
+    torch.cuda.synchronize()
+
+    def step():
+        L.lact_chunked_forward(cfg, dev, Q, K, V, eta, O, w.chunk_kv, w.chunk_q, w.order, ws)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-phase kernel durations: HIP events recorded by the library on the
+    # launch stream around each phase, over the same number of steps
+    log("[bench] per-phase event timing")
+    L.profile_enable(True)
+    L.profile_read()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    phases = L.profile_read()
+    L.profile_enable(False)
+
+    flops = w.flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    grad_ms, grad_n = phases["gradient"]
+    grad_avg = grad_ms / max(grad_n, 1)
+    grad_tflops = gradient_flops(w) / (grad_avg * 1e-3) / 1e12 if grad_n else None
+    roof = {
+        "kernel": "chunk gradient (key projections, SwiGLU backward, token contractions)",
+        "bound": "mfma", "achieved": round(grad_tflops, 3) if grad_tflops else None,
+        "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(grad_tflops / PEAK_BF16_TFLOPS, 4) if grad_tflops else None,
+        "traffic": None, "avg_launch_ms": round(grad_avg, 5),
+        "flop_per_launch": gradient_flops(w),
+    }
+    line = {
+        "metric": "LaCT layer TFLOP/s (update+apply)",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.io_dtype == "bf16" else "fp32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "h": w.h,
+                   "T_kv": w.T_kv, "T_q": w.T_q, "chunk_kv": w.chunk_kv, "chunk_q": w.chunk_q,
+                   "order": w.order, "opt": w.opt, "beta": w.beta, "ns_iters": w.ns_iters,
+                   "mfma_path": L.mfma_path(w.d, w.h, w.io_dtype)},
+        "tokens_per_s": round(w.B * w.T_kv / (ms * 1e-3), 1),
+        "query_tokens_per_s": round(w.B * w.T_q / (ms * 1e-3), 1),
+        "peak_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "flop_per_step": flops,
+        "phase_ms_per_step": {k: round(v[0] / args.steps, 5) for k, v in phases.items()},
+        "phase_launches_per_step": {k: v[1] / args.steps for k, v in phases.items()},
+        "wall_s_timed": round(wall, 4),
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline (budget {args.cpu_budget} s)")
+        line["cpu_baseline"] = cpu_baseline(w, x, st, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

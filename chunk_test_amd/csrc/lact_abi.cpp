@@ -89,27 +89,40 @@ struct Plan {
 
 // Token splits of one chunk's gradient.  Derived from the shapes only (not
 // from the device), so results are reproducible on any GPU.
-constexpr int64_t kTargetWorkgroups = 1024;  // about 4 per CU on 256 CUs
-constexpr int64_t kMinTokensPerSplit = 256;
-constexpr int64_t kMaxSplits = 4096;
-constexpr int64_t kTokAlign = 128;
-
 struct Splits {
   int S;
   int64_t tps;
 };
 
-Splits plan_splits(const Plan& p, int64_t n) {
-  const int64_t per_split = static_cast<int64_t>(p.P) * (p.h / 32);
-  int64_t S = (kTargetWorkgroups + per_split - 1) / per_split;
-  const int64_t by_size = (n + kMinTokensPerSplit - 1) / kMinTokensPerSplit;
+struct SplitRule {
+  int64_t wgs_per_split;  // workgroups launched per split
+  int64_t target_wgs;     // aim for about this many workgroups in total
+  int64_t min_tokens;     // never split below this many tokens
+  int64_t align;          // tokens per split are a multiple of this
+};
+
+Splits plan_splits(const SplitRule& r, int64_t n) {
+  int64_t S = (r.target_wgs + r.wgs_per_split - 1) / r.wgs_per_split;
+  const int64_t by_size = (n + r.min_tokens - 1) / r.min_tokens;
   if (S > by_size) S = by_size;
-  if (S > kMaxSplits) S = kMaxSplits;
+  if (S > 4096) S = 4096;
   if (S < 1) S = 1;
   int64_t tps = (n + S - 1) / S;
-  tps = (tps + kTokAlign - 1) / kTokAlign * kTokAlign;
+  tps = (tps + r.align - 1) / r.align * r.align;
   S = (n + tps - 1) / tps;
   return {static_cast<int>(S), tps};
+}
+
+// Generic kernel: one workgroup per (split, 32 hidden units, pair).
+SplitRule generic_rule(const Plan& p) {
+  return {static_cast<int64_t>(p.P) * (p.h / 32), 1024, 256, 128};
+}
+
+// MFMA kernel: one workgroup per (split, 128 hidden units, pair); about
+// one workgroup per CU on 256 CUs (the kernel keeps one wavefront per SIMD).
+SplitRule mfma_rule(const Plan& p) {
+  const int64_t stage = lact::grad_mfma_stage_tokens(p.d);
+  return {static_cast<int64_t>(p.P) * (p.h / 128), 256, 4 * stage, stage};
 }
 
 bool finite(float x) { return std::isfinite(x); }
@@ -166,10 +179,15 @@ struct WsLayout {
 WsLayout ws_layout(const Plan& p, int64_t max_chunk_kv) {
   WsLayout w;
   const size_t per = static_cast<size_t>(3) * p.h * p.d;
-  const Splits sp = plan_splits(p, max_chunk_kv < 1 ? 1 : max_chunk_kv);
+  const int64_t n = max_chunk_kv < 1 ? 1 : max_chunk_kv;
+  int64_t S = plan_splits(generic_rule(p), n).S;
+  if (p.mfma) {
+    const int64_t sm = plan_splits(mfma_rule(p), n).S;
+    if (sm > S) S = sm;
+  }
   size_t off = 0;
   w.partials = off;
-  off += align_up(sizeof(float) * per * p.P * static_cast<size_t>(sp.S));
+  off += align_up(sizeof(float) * per * p.P * static_cast<size_t>(S));
   w.dir = off;
   off += align_up(sizeof(float) * per * p.P);
   w.ns = off;
@@ -195,7 +213,10 @@ size_t io_bytes(const Plan& p) { return p.bf16 ? 2 : 4; }
 int run_update(const lact_config* c, const Plan& p, const lact_state* st, const void* K,
                const void* V, const float* eta, int64_t n, int64_t kv_stride,
                int64_t eta_stride, char* ws, const WsLayout& L, hipStream_t s) {
-  const Splits sp = plan_splits(p, n);
+  // the MFMA kernel reads 16-byte rows: it needs aligned K, V and strides
+  const bool use_mfma = p.mfma && (reinterpret_cast<uintptr_t>(K) % 16 == 0) &&
+                        (reinterpret_cast<uintptr_t>(V) % 16 == 0) && (kv_stride % 8 == 0);
+  const Splits sp = plan_splits(use_mfma ? mfma_rule(p) : generic_rule(p), n);
   float* partials = reinterpret_cast<float*>(ws + L.partials);
   float* dir = reinterpret_cast<float*>(ws + L.dir);
   hipError_t e;
@@ -218,7 +239,7 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
     g.S = sp.S;
     g.tps = sp.tps;
     g.bf16 = p.bf16;
-    e = lact::launch_grad_simple(g, s);
+    e = use_mfma ? lact::launch_grad_mfma(g, s) : lact::launch_grad_simple(g, s);
     if (e != hipSuccess) return hip_fail(e, "gradient kernel");
   }
   {
@@ -313,9 +334,8 @@ void lact_config_default(lact_config* c) {
 }
 
 int lact_mfma_path(int32_t d, int32_t h, int32_t io_dtype) {
-  (void)io_dtype;
   if (!lact::simple_shape_ok(d, h)) return -1;
-  return 0;
+  return (io_dtype == LACT_BF16 && lact::grad_mfma_shape_ok(d, h)) ? 1 : 0;
 }
 
 size_t lact_workspace_bytes(const lact_config* cfg, int64_t max_chunk_kv, int64_t max_chunk_q) {

@@ -70,6 +70,11 @@ hipError_t launch_ns_simple(const NSArgs& a, hipStream_t s);
 hipError_t launch_step_norm(const StepArgs& a, hipStream_t s);
 hipError_t launch_apply_simple(const ApplyArgs& a, hipStream_t s);
 bool simple_shape_ok(int d, int h);
+
+// ---- bf16 MFMA kernels (gfx950) ----
+bool grad_mfma_shape_ok(int d, int h);
+int grad_mfma_stage_tokens(int d);  // token splits must be multiples of this
+hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s);
 size_t ns_simple_scratch_floats(int P, int d, int h);
 
 }  // namespace lact

@@ -18,8 +18,9 @@ pytestmark = pytest.mark.gpu
 TINY = S.WORKLOADS["tiny"]
 
 
-def small(name, **kw):
-    return S.WORKLOADS[name].replace(name=f"{name}-small", **kw)
+def small(base, **kw):
+    kw.setdefault("name", f"{base}-small")
+    return S.WORKLOADS[base].replace(**kw)
 
 
 SMALL_CASES = [
@@ -37,6 +38,10 @@ SMALL_CASES = [
     small("posed", H=2, T_kv=16384, T_q=512, chunk_kv=16384, chunk_q=512),
     small("video", H=2, T_kv=3 * 4096, T_q=3 * 4096),
     small("million", H=2, T_kv=40000, T_q=1000, chunk_kv=40000, chunk_q=1000),
+    # bf16, chunks shorter than one LDS stage of the MFMA kernel, ragged
+    small("posed", name="posed-tiny-chunks", H=3, T_kv=1000, T_q=70, chunk_kv=100, chunk_q=7),
+    # bf16, two 128-unit hidden slices at d = 64
+    small("posed", name="posed-h256", H=2, h=256, T_kv=5000, T_q=64, chunk_kv=5000, chunk_q=64),
 ]
 
 
