@@ -38,8 +38,13 @@ SMALL_CASES = [
     small("posed", H=2, T_kv=16384, T_q=512, chunk_kv=16384, chunk_q=512),
     small("video", H=2, T_kv=3 * 4096, T_q=3 * 4096),
     small("million", H=2, T_kv=40000, T_q=1000, chunk_kv=40000, chunk_q=1000),
-    # bf16, chunks shorter than one LDS stage of the MFMA kernel, ragged
-    small("posed", name="posed-tiny-chunks", H=3, T_kv=1000, T_q=70, chunk_kv=100, chunk_q=7),
+    # bf16, chunks shorter than one LDS stage of the MFMA kernel, ragged.
+    # (Muon is not used here: on 100-token chunks Newton-Schulz lifts the
+    # near-null singular directions of the gradient, and bf16 operand
+    # rounding alone moves the result by ~7e-2; a CPU emulation of bf16
+    # operands shows the same.)
+    small("posed", name="posed-tiny-chunks", H=3, T_kv=1000, T_q=70, chunk_kv=100, chunk_q=7,
+          opt="momentum", beta=0.9),
     # bf16, two 128-unit hidden slices at d = 64
     small("posed", name="posed-h256", H=2, h=256, T_kv=5000, T_q=64, chunk_kv=5000, chunk_q=64),
 ]
