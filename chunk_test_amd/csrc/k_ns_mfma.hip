@@ -1,0 +1,330 @@
+// Newton-Schulz orthogonalisation of the matrix gradients (Muon's transform,
+// "LaCT: Large Chunk Test-Time Training" review, section "Local attention
+// and nonlinear memory work together"; coefficients as given in the layer
+// configuration), one workgroup per matrix, on bf16 MFMA with split operands.
+//
+// X is the s x l orientation of the gradient (s = min(d, h), l = max(d, h)),
+// X0 = G / (||G||_F + eps), then `iters` times
+//     A = X X^T,  B = b A + c A A,  X <- a X + B X.
+// Every product uses the three-term split x = x_hi + x_lo (both bf16):
+//     P Q ~ P_hi Q_hi + P_hi Q_lo + P_lo Q_hi   (fp32 accumulation),
+// which keeps ~16 significant bits per operand.  Plain bf16 operands move
+// the orthogonalised result by ~3e-2 (relative) and the updated weights by
+// ~2e-2, which the split avoids.
+//
+// Work split: wave w owns CT tiles of 32 columns of X and keeps them as fp32
+// in registers, in the MFMA output layout.  That layout is directly the
+// B operand of B X (16 rows of X per k-step), so only two LDS layouts are
+// needed: X row-major (for X X^T, written once per iteration) and the
+// symmetric s x s matrices A and then B (written as the transpose of their
+// own output tiles, which for a symmetric matrix is the matrix itself).
+#include "lact_device.h"
+#include "lact_internal.h"
+
+namespace lact {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void split(float x, __bf16& hi, __bf16& lo) {
+  hi = static_cast<__bf16>(x);
+  lo = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+
+template <int S, int L>
+struct NSGeo {
+  static constexpr int NW = L / 32;          // waves
+  static constexpr int CT = L / (32 * NW);   // 32-column tiles of X per wave (1)
+  static constexpr int MT = S / 32;          // 32-row tiles of X (and of A)
+  static constexpr int XRS = 2 * L + 16;     // bytes per row of X (bf16, padded)
+  static constexpr int X_HALF = S * XRS;     // hi block, then lo block
+  static constexpr int ARS = 2 * S + 16;     // bytes per row of A / B
+  static constexpr int A_HALF = S * ARS;
+  static constexpr int REGION = (2 * X_HALF > 2 * A_HALF) ? 2 * X_HALF : 2 * A_HALF;
+  static constexpr int ATILES = MT * MT;
+  static constexpr int ATW = (ATILES + NW - 1) / NW;  // A tiles per wave
+};
+
+template <int S, int L>
+__global__ __launch_bounds__(2 * L) void k_ns_mfma(NSArgs a) {
+  using G = NSGeo<S, L>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[G::REGION];
+  __shared__ float red[G::NW];
+
+  const int mat = blockIdx.x;
+  const int pair = mat / 3, which = mat % 3;  // 0: W1 (h x d), 1: W2 (d x h), 2: W3 (h x d)
+  const int64_t hd = static_cast<int64_t>(a.h) * a.d;
+  float* Gm = a.dir + pair * 3 * hd + which * hd;
+  const int cols = (which == 1) ? a.h : a.d;
+  const bool tr = ((which == 1) ? a.d : a.h) > cols;  // X = G^T when G is tall
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, ln = lane & 31;
+  // column tile ct of this wave holds columns 32 (NW ct + w) .. +31
+  auto colof = [&](int ct) { return 32 * (G::NW * ct + w) + ln; };
+
+  // ---- X0 = G / (||G||_F + eps), fp32 in registers, MFMA output layout:
+  // x[ct][mt][r] = X[32 mt + 8 (r/4) + 4 g + r%4][colof(ct)].
+  // G is staged through LDS (fp32, row stride XFS) so that the global reads
+  // stay coalesced and the register reads use immediate offsets.
+  constexpr int XFS = 4 * L + 16;
+  float* xf = reinterpret_cast<float*>(lds);
+  float ss = 0.f;
+  for (int e = tid; e < S * L; e += 2 * L) {
+    const float v = Gm[e];
+    ss += v * v;
+    const int i = tr ? (e % S) : (e / L);  // row of X
+    const int j = tr ? (e / S) : (e % L);  // column of X
+    *reinterpret_cast<float*>(lds + i * XFS + 4 * j) = v;
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) red[w] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < G::NW; ++i) tot += red[i];
+  const float inv_denom = 1.f / (sqrtf(tot) + a.eps);
+  (void)xf;
+  f32x16_t x[G::CT][G::MT];
+#pragma unroll
+  for (int ct = 0; ct < G::CT; ++ct) {
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt) {
+      const unsigned char* xb = lds + (32 * mt + 4 * g) * XFS + 4 * colof(ct);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        x[ct][mt][r] = *reinterpret_cast<const float*>(xb + (8 * (r >> 2) + (r & 3)) * XFS) * inv_denom;
+      }
+    }
+  }
+
+  unsigned char* xhi = lds;
+  unsigned char* xlo = lds + G::X_HALF;
+  unsigned char* ahi = lds;
+  unsigned char* alo = lds + G::A_HALF;
+
+  for (int it = 0; it < a.iters; ++it) {
+    // ---- X row-major (hi, lo) into LDS
+    __syncthreads();
+#pragma unroll
+    for (int ct = 0; ct < G::CT; ++ct) {
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt) {
+        // one base per 32-row tile keeps every store offset an immediate
+        unsigned char* xb = xhi + (32 * mt + 4 * g) * G::XRS + 2 * colof(ct);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          __bf16 hi, lo;
+          split(x[ct][mt][r], hi, lo);
+          const int ro = (8 * (r >> 2) + (r & 3)) * G::XRS;
+          *reinterpret_cast<__bf16*>(xb + ro) = hi;
+          *reinterpret_cast<__bf16*>(xb + G::X_HALF + ro) = lo;
+        }
+        // keep the scheduler from computing every split value up front
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __syncthreads();
+
+    // ---- A = X X^T: this wave's tiles (ti, tj); K = l
+    f32x16_t at[G::ATW];
+#pragma unroll
+    for (int q = 0; q < G::ATW; ++q) {
+      const int t = w + G::NW * q;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) at[q][r] = 0.f;
+      if (t < G::ATILES) {
+        const int ti = t / G::MT, tj = t % G::MT;
+        const unsigned char* ra = xhi + (32 * ti + ln) * G::XRS + 16 * g;
+        const unsigned char* rb = xhi + (32 * tj + ln) * G::XRS + 16 * g;
+#pragma unroll 2
+        for (int ks = 0; ks < L / 16; ++ks) {
+          const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(ra + 32 * ks);
+          const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(ra + G::X_HALF + 32 * ks);
+          const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(rb + 32 * ks);
+          const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(rb + G::X_HALF + 32 * ks);
+          at[q] = mfma(ah, bh, at[q]);
+          at[q] = mfma(ah, bl, at[q]);
+          at[q] = mfma(al, bh, at[q]);
+        }
+      }
+    }
+    __syncthreads();  // X row-major no longer needed: the region becomes A
+
+    // A is symmetric: tile (ti, tj) transposed lands at rows 32 tj + ln,
+    // columns 32 ti + 8 (r/4) + 4 g .. +3 (four consecutive bf16 per store)
+#pragma unroll
+    for (int q = 0; q < G::ATW; ++q) {
+      const int t = w + G::NW * q;
+      if (t < G::ATILES) {
+        const int ti = t / G::MT, tj = t % G::MT;
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          bf16x4_t h4, l4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            __bf16 hi, lo;
+            split(at[q][4 * rg + i], hi, lo);
+            h4[i] = hi;
+            l4[i] = lo;
+          }
+          const int off = (32 * tj + ln) * G::ARS + 2 * (32 * ti + 8 * rg + 4 * g);
+          *reinterpret_cast<bf16x4_t*>(ahi + off) = h4;
+          *reinterpret_cast<bf16x4_t*>(alo + off) = l4;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- B = b A + c A A on the same tiles (A symmetric: both operands are rows of A)
+#pragma unroll
+    for (int q = 0; q < G::ATW; ++q) {
+      const int t = w + G::NW * q;
+      f32x16_t acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      if (t < G::ATILES) {
+        const int ti = t / G::MT, tj = t % G::MT;
+        const unsigned char* ra = ahi + (32 * ti + ln) * G::ARS + 16 * g;
+        const unsigned char* rb = ahi + (32 * tj + ln) * G::ARS + 16 * g;
+#pragma unroll 2
+        for (int ks = 0; ks < S / 16; ++ks) {
+          const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(ra + 32 * ks);
+          const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(ra + G::A_HALF + 32 * ks);
+          const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(rb + 32 * ks);
+          const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(rb + G::A_HALF + 32 * ks);
+          acc = mfma(ah, bh, acc);
+          acc = mfma(ah, bl, acc);
+          acc = mfma(al, bh, acc);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) at[q][r] = a.b * at[q][r] + a.c * acc[r];  // now B
+    }
+    __syncthreads();  // all reads of A done: the region becomes B
+    // B is symmetric too: same store
+#pragma unroll
+    for (int q = 0; q < G::ATW; ++q) {
+      const int t = w + G::NW * q;
+      if (t < G::ATILES) {
+        const int ti = t / G::MT, tj = t % G::MT;
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          bf16x4_t h4, l4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            __bf16 hi, lo;
+            split(at[q][4 * rg + i], hi, lo);
+            h4[i] = hi;
+            l4[i] = lo;
+          }
+          const int off = (32 * tj + ln) * G::ARS + 2 * (32 * ti + 8 * rg + 4 * g);
+          *reinterpret_cast<bf16x4_t*>(ahi + off) = h4;
+          *reinterpret_cast<bf16x4_t*>(alo + off) = l4;
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- X <- a X + B X for this wave's 32 columns.  The B operand (X,
+    // 16 rows per k-step) comes from this lane's own registers; the A
+    // operand (rows of B) uses the matching row order:
+    // slot 8g + i of k-step s <-> row 16 s + 8 (i/4) + 4 g + i%4.
+    // (one output tile at a time keeps few registers live; the split of X
+    // into hi/lo operands is redone per tile, which is cheap VALU work)
+#pragma unroll
+    for (int ct = 0; ct < G::CT; ++ct) {
+      f32x16_t accs[G::MT];
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt) {
+        f32x16_t acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        const unsigned char* rb = ahi + (32 * mt + ln) * G::ARS + 8 * g;
+#pragma unroll
+        for (int s = 0; s < S / 16; ++s) {
+          bf16x8_t xh, xl;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            __bf16 hi, lo;
+            split(x[ct][s >> 1][8 * (s & 1) + i], hi, lo);
+            xh[i] = hi;
+            xl[i] = lo;
+          }
+          const bf16x4_t h0 = *reinterpret_cast<const bf16x4_t*>(rb + 32 * s);
+          const bf16x4_t h1 = *reinterpret_cast<const bf16x4_t*>(rb + 32 * s + 16);
+          const bf16x4_t l0 = *reinterpret_cast<const bf16x4_t*>(rb + G::A_HALF + 32 * s);
+          const bf16x4_t l1 = *reinterpret_cast<const bf16x4_t*>(rb + G::A_HALF + 32 * s + 16);
+          bf16x8_t bh, bl;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            bh[i] = h0[i];
+            bh[4 + i] = h1[i];
+            bl[i] = l0[i];
+            bl[4 + i] = l1[i];
+          }
+          acc = mfma(bh, xh, acc);
+          acc = mfma(bh, xl, acc);
+          acc = mfma(bl, xh, acc);
+        }
+        accs[mt] = acc;
+      }
+      // this column tile is not read again in this iteration: update in place
+#pragma unroll
+      for (int mt = 0; mt < G::MT; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[ct][mt][r] = a.a * x[ct][mt][r] + accs[mt][r];
+      }
+    }
+  }
+
+  // ---- result back into the direction buffer, in G's orientation (via LDS)
+  __syncthreads();
+#pragma unroll
+  for (int ct = 0; ct < G::CT; ++ct) {
+#pragma unroll
+    for (int mt = 0; mt < G::MT; ++mt) {
+      unsigned char* xb = lds + (32 * mt + 4 * g) * XFS + 4 * colof(ct);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        *reinterpret_cast<float*>(xb + (8 * (r >> 2) + (r & 3)) * XFS) = x[ct][mt][r];
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < S * L; e += 2 * L) {
+    const int i = tr ? (e % S) : (e / L);
+    const int j = tr ? (e / S) : (e % L);
+    Gm[e] = *reinterpret_cast<const float*>(lds + i * XFS + 4 * j);
+  }
+}
+
+}  // namespace
+
+bool ns_mfma_shape_ok(int d, int h) {
+  const int s = d < h ? d : h, l = d < h ? h : d;
+  return (s == 64 && l == 128) || (s == 128 && l == 256) || (s == 64 && l == 256);
+}
+
+hipError_t launch_ns_mfma(const NSArgs& a, hipStream_t st) {
+  const int s = a.d < a.h ? a.d : a.h, l = a.d < a.h ? a.h : a.d;
+  const dim3 grid(3 * a.P);
+  if (s == 64 && l == 128) {
+    hipLaunchKernelGGL((k_ns_mfma<64, 128>), grid, dim3(2 * 128), 0, st, a);
+  } else if (s == 128 && l == 256) {
+    hipLaunchKernelGGL((k_ns_mfma<128, 256>), grid, dim3(2 * 256), 0, st, a);
+  } else if (s == 64 && l == 256) {
+    hipLaunchKernelGGL((k_ns_mfma<64, 256>), grid, dim3(2 * 256), 0, st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lact

@@ -273,7 +273,9 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
     a.b = c->ns_b;
     a.c = c->ns_c;
     a.eps = c->ns_eps;
-    e = lact::launch_ns_simple(a, s);
+    // bf16 mode: split-bf16 MFMA Newton-Schulz; fp32 mode keeps fp32 arithmetic
+    e = (p.bf16 && lact::ns_mfma_shape_ok(p.d, p.h)) ? lact::launch_ns_mfma(a, s)
+                                                      : lact::launch_ns_simple(a, s);
     if (e != hipSuccess) return hip_fail(e, "Newton-Schulz kernel");
   }
   {

@@ -75,6 +75,8 @@ bool simple_shape_ok(int d, int h);
 bool grad_mfma_shape_ok(int d, int h);
 int grad_mfma_stage_tokens(int d);  // token splits must be multiples of this
 hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s);
+bool ns_mfma_shape_ok(int d, int h);
+hipError_t launch_ns_mfma(const NSArgs& a, hipStream_t s);
 size_t ns_simple_scratch_floats(int P, int d, int h);
 
 }  // namespace lact
