@@ -33,6 +33,12 @@ typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 
 constexpr int kThreads = 256;
 constexpr int kHidPerWave = 32;
+// The key projection through W1 is computed pre-scaled by -log2(e), so the
+// sigmoid needs no extra multiply: sigmoid(h1) = 1 / (1 + 2^(-log2(e) h1)).
+// G and dH3 then carry the same factor, removed once from dW2 and dW3 at
+// the end (times -ln 2).
+constexpr float kNegLog2e = -1.4426950408889634f;
+constexpr float kNegLn2 = -0.6931471805599453f;
 constexpr int kHidPerWG = 128;
 
 template <int D>
@@ -51,6 +57,12 @@ struct Geo {
   static constexpr int OFF_KT = 2 * NAT_BYTES;
   static constexpr int OFF_UT = 2 * NAT_BYTES + TR_BYTES;
   static constexpr int LDS = 2 * NAT_BYTES + 2 * TR_BYTES;
+  // d = 64: two workgroups per CU (two wavefronts per SIMD, at most 256
+  // registers each, so the MFMAs write VGPRs and one wave's SwiGLU math
+  // overlaps the other's MFMAs).  d = 128 needs more accumulator registers:
+  // one wavefront per SIMD, with the next stage prefetched into registers.
+  static constexpr int WAVES_PER_SIMD = (D == 64) ? 2 : 1;
+  static constexpr bool PREFETCH = (D != 64);
 };
 
 // Byte offset of the 16-byte half `half` of row (s16, d) in a transposed
@@ -75,7 +87,9 @@ __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_grad_mfma(GradArgs a, int hsl, int nbase) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(Geo<D>::WAVES_PER_SIMD, Geo<D>::WAVES_PER_SIMD)))
+void k_grad_mfma(GradArgs a, int hsl, int nbase) {
   using G = Geo<D>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[G::LDS];
 
@@ -110,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void k_grad_mfma(GradArgs a, int hsl, int
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int dd = 16 * ks + 8 * g + i;
-        w1b[ks][i] = static_cast<__bf16>(W1[dd]);
+        w1b[ks][i] = static_cast<__bf16>(kNegLog2e * W1[dd]);
         w3b[ks][i] = static_cast<__bf16>(W3[dd]);
         w2b[ks][i] = static_cast<__bf16>(W2[static_cast<int64_t>(dd) * h]);
       }
@@ -205,14 +219,13 @@ __global__ __launch_bounds__(kThreads) void k_grad_mfma(GradArgs a, int hsl, int
     }
   };
 
-  constexpr float kLog2e = 1.4426950408889634f;
-
-  if (t_begin < t_end) load_stage(t_begin);
+  if (G::PREFETCH && t_begin < t_end) load_stage(t_begin);
   for (int64_t t0 = t_begin; t0 < t_end; t0 += G::TT) {
+    if (!G::PREFETCH) load_stage(t0);
     __syncthreads();
     store_stage();
     __syncthreads();
-    if (t0 + G::TT < t_end) load_stage(t0 + G::TT);
+    if (G::PREFETCH && t0 + G::TT < t_end) load_stage(t0 + G::TT);
 
 #pragma unroll 1
     for (int st = 0; st < G::SUB; ++st) {
@@ -234,24 +247,25 @@ __global__ __launch_bounds__(kThreads) void k_grad_mfma(GradArgs a, int hsl, int
         c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, w3b[ks], c3, 0, 0, 0);
         cg = __builtin_amdgcn_mfma_f32_32x32x16_bf16(au, w2b[ks], cg, 0, 0, 0);
       }
-      // SwiGLU forward and backward on the 16 (token, hidden) values of this lane
-      bf16x8_t pg[2], pd1[2], pd3[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float h1 = c1[r], h3 = c3[r], dg = cg[r];
-        const float e = __builtin_amdgcn_exp2f(-kLog2e * h1);
-        const float s = __builtin_amdgcn_rcpf(1.f + e);
-        const float act = h1 * s;
-        const float gv = act * h3;
-        const float dh3 = dg * act;
-        const float dh1 = dg * h3 * fmaf(act, 1.f - s, s);
-        pg[r >> 3][r & 7] = static_cast<__bf16>(gv);
-        pd1[r >> 3][r & 7] = static_cast<__bf16>(dh1);
-        pd3[r >> 3][r & 7] = static_cast<__bf16>(dh3);
-      }
-      // token contractions: K = 16 tokens per MFMA, two k-steps per sub-tile
+      // SwiGLU forward and backward, then the token contractions, one k-step
+      // (16 tokens) at a time.  With z = -log2(e) h1 (from the scaled W1):
+      //   s = 1 / (1 + 2^z),  a' = z s = -log2(e) silu(h1),
+      //   g' = a' h3,  dh3' = dg a',  silu'(h1) = s + a (1 - s) = s - ln2 a' (1 - s),
+      //   dh1 = dg h3 silu'(h1).
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
+        bf16x8_t pg, pd1, pd3;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = 8 * s + i;
+          const float z = c1[r], h3 = c3[r], dg = cg[r];
+          const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(z));
+          const float act = z * sg;
+          pg[i] = static_cast<__bf16>(act * h3);
+          pd3[i] = static_cast<__bf16>(dg * act);
+          const float u = fmaf(-act, sg, act);
+          pd1[i] = static_cast<__bf16>((dg * h3) * fmaf(kNegLn2, u, sg));
+        }
         const int grp = 2 * st + s;
 #pragma unroll
         for (int nt = 0; nt < G::NT; ++nt) {
@@ -259,9 +273,9 @@ __global__ __launch_bounds__(kThreads) void k_grad_mfma(GradArgs a, int hsl, int
           const int off = tr_off<D>(grp, dd, g);
           const bf16x8_t bk = *reinterpret_cast<const bf16x8_t*>(lds + G::OFF_KT + off);
           const bf16x8_t bu = *reinterpret_cast<const bf16x8_t*>(lds + G::OFF_UT + off);
-          aW1[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pd1[s], bk, aW1[nt], 0, 0, 0);
-          aW3[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pd3[s], bk, aW3[nt], 0, 0, 0);
-          aW2[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bu, pg[s], aW2[nt], 0, 0, 0);
+          aW1[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pd1, bk, aW1[nt], 0, 0, 0);
+          aW3[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pd3, bk, aW3[nt], 0, 0, 0);
+          aW2[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bu, pg, aW2[nt], 0, 0, 0);
         }
       }
     }
@@ -275,8 +289,8 @@ __global__ __launch_bounds__(kThreads) void k_grad_mfma(GradArgs a, int hsl, int
     for (int r = 0; r < 16; ++r) {
       const int row = 8 * (r >> 2) + 4 * g + (r & 3);
       out[static_cast<int64_t>(n0 + row) * D + 32 * nt + ln] = aW1[nt][r];
-      out[2 * hd + static_cast<int64_t>(n0 + row) * D + 32 * nt + ln] = aW3[nt][r];
-      out[hd + static_cast<int64_t>(32 * nt + row) * h + n0 + ln] = aW2[nt][r];
+      out[2 * hd + static_cast<int64_t>(n0 + row) * D + 32 * nt + ln] = kNegLn2 * aW3[nt][r];
+      out[hd + static_cast<int64_t>(32 * nt + row) * h + n0 + ln] = kNegLn2 * aW2[nt][r];
     }
   }
 }
@@ -297,6 +311,8 @@ bool grad_mfma_shape_ok(int d, int h) {
 }
 
 int grad_mfma_stage_tokens(int d) { return 8192 / d; }
+
+int grad_mfma_wgs_per_cu(int d) { return d == 64 ? Geo<64>::WAVES_PER_SIMD : Geo<128>::WAVES_PER_SIMD; }
 
 hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s) {
   switch (a.d) {

@@ -118,11 +118,16 @@ SplitRule generic_rule(const Plan& p) {
   return {static_cast<int64_t>(p.P) * (p.h / 32), 1024, 256, 128};
 }
 
-// MFMA kernel: one workgroup per (split, 128 hidden units, pair); about
-// one workgroup per CU on 256 CUs (the kernel keeps one wavefront per SIMD).
+// MFMA kernel: one workgroup per (split, 128 hidden units, pair), sized to
+// one round of resident workgroups on 256 CUs (two per CU at d = 64, one at
+// d = 128), rounding the split count down so no second round is started.
 SplitRule mfma_rule(const Plan& p) {
   const int64_t stage = lact::grad_mfma_stage_tokens(p.d);
-  return {static_cast<int64_t>(p.P) * (p.h / 128), 256, 4 * stage, stage};
+  const int64_t per_split = static_cast<int64_t>(p.P) * (p.h / 128);
+  const int64_t resident = 256 * lact::grad_mfma_wgs_per_cu(p.d);
+  int64_t target = (resident / per_split) * per_split;
+  if (target < per_split) target = per_split;
+  return {per_split, target, 4 * stage, stage};
 }
 
 bool finite(float x) { return std::isfinite(x); }
@@ -311,7 +316,10 @@ int run_apply(const Plan& p, const lact_state* st, const void* Q, void* O, int64
   a.d = p.d;
   a.h = p.h;
   a.bf16 = p.bf16;
-  hipError_t e = lact::launch_apply_simple(a, s);
+  const bool use_mfma = p.bf16 && lact::apply_mfma_shape_ok(p.d, p.h) &&
+                        reinterpret_cast<uintptr_t>(Q) % 16 == 0 &&
+                        reinterpret_cast<uintptr_t>(O) % 16 == 0 && q_stride % 8 == 0;
+  hipError_t e = use_mfma ? lact::launch_apply_mfma(a, s) : lact::launch_apply_simple(a, s);
   if (e != hipSuccess) return hip_fail(e, "query-read kernel");
   return LACT_OK;
 }

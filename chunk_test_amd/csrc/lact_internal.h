@@ -74,8 +74,11 @@ bool simple_shape_ok(int d, int h);
 // ---- bf16 MFMA kernels (gfx950) ----
 bool grad_mfma_shape_ok(int d, int h);
 int grad_mfma_stage_tokens(int d);  // token splits must be multiples of this
+int grad_mfma_wgs_per_cu(int d);    // resident workgroups per CU
 hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s);
 bool ns_mfma_shape_ok(int d, int h);
+bool apply_mfma_shape_ok(int d, int h);
+hipError_t launch_apply_mfma(const ApplyArgs& a, hipStream_t s);
 hipError_t launch_ns_mfma(const NSArgs& a, hipStream_t s);
 size_t ns_simple_scratch_floats(int P, int d, int h);
 
