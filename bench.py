@@ -80,6 +80,9 @@ def main():
     ap.add_argument("--workload", default="posed", choices=sorted(S.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a reference for "
+                         "hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -96,7 +99,7 @@ def main():
     x = S.gen_inputs(w)
     io = torch.bfloat16 if w.io_dtype == "bf16" else torch.float32
     cfg = L.Config(B=w.B, H=w.H, d=w.d, h=w.h, io_dtype=w.io_dtype, opt=w.opt, beta=w.beta,
-                   ns_iters=w.ns_iters)
+                   ns_iters=w.ns_iters, products=w.products)
     dev = {n: torch.from_numpy(st[n]).cuda() for n in ("W1", "W2", "W3")}
     if cfg.uses_momentum():
         for n in ("M1", "M2", "M3"):
@@ -109,6 +112,13 @@ def main():
 
     def step():
         L.lact_chunked_forward(cfg, dev, Q, K, V, eta, O, w.chunk_kv, w.chunk_q, w.order, ws)
+
+    if args.copy_probe_mib:
+        src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -167,6 +177,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "h": w.h,
                    "T_kv": w.T_kv, "T_q": w.T_q, "chunk_kv": w.chunk_kv, "chunk_q": w.chunk_q,
                    "order": w.order, "opt": w.opt, "beta": w.beta, "ns_iters": w.ns_iters,
+                   "products": w.products,
                    "mfma_path": L.mfma_path(w.d, w.h, w.io_dtype)},
         "tokens_per_s": round(w.B * w.T_kv / (ms * 1e-3), 1),
         "query_tokens_per_s": round(w.B * w.T_q / (ms * 1e-3), 1),

@@ -85,6 +85,7 @@ struct Plan {
   bool mfma = false;
   bool momentum = false;
   bool muon = false;
+  bool split = false;  // bf16 inputs, ~fp32 derived operands
 };
 
 // Token splits of one chunk's gradient.  Derived from the shapes only (not
@@ -151,6 +152,8 @@ int check_config(const lact_config* c, Plan* p) {
       return fail(LACT_ERR_INVALID_ARG, "Newton-Schulz coefficients must be finite, eps >= 0");
   }
   if (!finite(c->step)) return fail(LACT_ERR_INVALID_ARG, "step must be finite");
+  if (c->products != LACT_PRODUCTS_BF16 && c->products != LACT_PRODUCTS_SPLIT)
+    return fail(LACT_ERR_INVALID_ARG, "products %d unknown", c->products);
   if (!finite(c->norm_eps) || c->norm_eps <= 0.f)
     return fail(LACT_ERR_INVALID_ARG, "norm_eps %g must be finite and > 0", c->norm_eps);
   const int mf = lact_mfma_path(c->d, c->h, c->io_dtype);
@@ -165,6 +168,7 @@ int check_config(const lact_config* c, Plan* p) {
   p->mfma = mf == 1;
   p->momentum = c->opt == LACT_OPT_MOMENTUM || (c->opt == LACT_OPT_MUON && c->beta > 0.f);
   p->muon = c->opt == LACT_OPT_MUON;
+  p->split = p->bf16 && c->products == LACT_PRODUCTS_SPLIT;
   return LACT_OK;
 }
 
@@ -219,7 +223,8 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
                const void* V, const float* eta, int64_t n, int64_t kv_stride,
                int64_t eta_stride, char* ws, const WsLayout& L, hipStream_t s) {
   // the MFMA kernel reads 16-byte rows: it needs aligned K, V and strides
-  const bool use_mfma = p.mfma && (reinterpret_cast<uintptr_t>(K) % 16 == 0) &&
+  // (split products: the fp32-arithmetic kernel)
+  const bool use_mfma = p.mfma && !p.split && (reinterpret_cast<uintptr_t>(K) % 16 == 0) &&
                         (reinterpret_cast<uintptr_t>(V) % 16 == 0) && (kv_stride % 8 == 0);
   const Splits sp = plan_splits(use_mfma ? mfma_rule(p) : generic_rule(p), n);
   float* partials = reinterpret_cast<float*>(ws + L.partials);
@@ -341,6 +346,7 @@ void lact_config_default(lact_config* c) {
   c->ns_eps = 1e-7f;
   c->step = 1.f;
   c->norm_eps = 1e-12f;
+  c->products = LACT_PRODUCTS_BF16;
 }
 
 int lact_mfma_path(int32_t d, int32_t h, int32_t io_dtype) {

@@ -28,6 +28,7 @@ PROFILE_PHASES = ("gradient", "reduce", "newton_schulz", "step_norm", "apply")
 ORDER_CODES = {"apply_then_update": LACT_APPLY_THEN_UPDATE, "update_then_apply": LACT_UPDATE_THEN_APPLY}
 OPT_CODES = {"gd": LACT_OPT_GD, "momentum": LACT_OPT_MOMENTUM, "muon": LACT_OPT_MUON}
 DTYPE_CODES = {"fp32": LACT_F32, "bf16": LACT_BF16}
+PRODUCT_CODES = {"bf16": 0, "split": 1}
 
 EXPORTED = (
     "lact_config_default", "lact_workspace_bytes", "lact_update", "lact_apply",
@@ -41,7 +42,7 @@ class LactConfig(ctypes.Structure):
         ("B", c_int32), ("H", c_int32), ("d", c_int32), ("h", c_int32),
         ("io_dtype", c_int32), ("opt", c_int32), ("beta", c_float),
         ("ns_iters", c_int32), ("ns_a", c_float), ("ns_b", c_float), ("ns_c", c_float),
-        ("ns_eps", c_float), ("step", c_float), ("norm_eps", c_float),
+        ("ns_eps", c_float), ("step", c_float), ("norm_eps", c_float), ("products", c_int32),
     ]
 
 
@@ -121,11 +122,13 @@ class Config:
     ns_eps: float = 1e-7
     step: float = 1.0
     norm_eps: float = 1e-12
+    products: str = "bf16"
 
     def to_c(self) -> LactConfig:
         return LactConfig(self.B, self.H, self.d, self.h, DTYPE_CODES[self.io_dtype],
                           OPT_CODES[self.opt], self.beta, self.ns_iters, self.ns_a, self.ns_b,
-                          self.ns_c, self.ns_eps, self.step, self.norm_eps)
+                          self.ns_c, self.ns_eps, self.step, self.norm_eps,
+                          PRODUCT_CODES[self.products])
 
     def uses_momentum(self) -> bool:
         return self.opt == "momentum" or (self.opt == "muon" and self.beta > 0)

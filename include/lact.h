@@ -74,6 +74,15 @@ typedef enum { LACT_APPLY_THEN_UPDATE = 0, LACT_UPDATE_THEN_APPLY = 1 } lact_ord
 /* Update rule ("Local attention and nonlinear memory work together"). */
 typedef enum { LACT_OPT_GD = 0, LACT_OPT_MOMENTUM = 1, LACT_OPT_MUON = 2 } lact_opt;
 
+/* bf16 I/O mode only.  LACT_PRODUCTS_BF16: every product operand is rounded
+ * to bf16 (the inputs already are; W, u = -eta v, and the SwiGLU values are
+ * rounded), fp32 accumulation.  LACT_PRODUCTS_SPLIT: only the inputs Q, K,
+ * V are bf16; every derived operand keeps ~16 significant bits (computed in
+ * fp32, or as a hi + lo pair of bf16 values on the matrix cores).  Muon over
+ * many chunks amplifies operand rounding from chunk to chunk, which the
+ * split mode avoids at a higher cost.  Ignored in fp32 I/O mode. */
+typedef enum { LACT_PRODUCTS_BF16 = 0, LACT_PRODUCTS_SPLIT = 1 } lact_products;
+
 typedef struct {
   int32_t B, H;      /* batch and heads: P = B*H independent pairs                        */
   int32_t d, h;      /* head dim and SwiGLU hidden dim                                    */
@@ -85,6 +94,7 @@ typedef struct {
   float ns_eps;      /* X0 = G / (||G||_F + ns_eps)                                       */
   float step;        /* W <- W - step * direction                                         */
   float norm_eps;    /* row r <- r / max(||r||_2, norm_eps)                               */
+  int32_t products;  /* lact_products: how bf16-mode products treat derived operands      */
 } lact_config;
 
 typedef struct {
@@ -94,7 +104,8 @@ typedef struct {
 
 /* Defaults: opt GD, beta 0, ns_iters 5, (a,b,c) = (3.4445, -4.7750, 2.0315)
  * (the quintic published with the Muon optimizer; the pages only name
- * Newton-Schulz), ns_eps 1e-7, step 1, norm_eps 1e-12, io_dtype LACT_BF16.
+ * Newton-Schulz), ns_eps 1e-7, step 1, norm_eps 1e-12, io_dtype LACT_BF16,
+ * products LACT_PRODUCTS_BF16.
  * B, H, d, h are set to 0 and must be filled in. */
 void lact_config_default(lact_config* cfg);
 

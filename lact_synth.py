@@ -72,6 +72,7 @@ class Workload:
     ns_iters: int = 5
     io_dtype: str = "bf16"  # "fp32" | "bf16"
     seed: int = 0
+    products: str = "bf16"  # "bf16" | "split": precision of derived product operands
 
     @property
     def n_chunks(self) -> int:
@@ -118,9 +119,11 @@ WORKLOADS = {
                       opt="muon"),
     # AR video: 14 chunks of 4096 tokens, 40 heads d=128, h=256,
     # apply-then-update, Muon 5.
+    # (Muon over 14 chunks amplifies bf16 rounding of the gradient's operands
+    # from chunk to chunk, so this workload keeps derived operands split)
     "video": Workload("video", B=1, H=40, d=128, h=256, T_kv=57344, T_q=57344,
                       chunk_kv=4096, chunk_q=4096, order="apply_then_update",
-                      opt="muon"),
+                      opt="muon", products="split"),
     # million-token set: 1,029,120 tokens as one chunk, 12 heads d=64, h=128,
     # update-then-apply on 8040 query tokens, Muon 5.
     "million": Workload("million", B=1, H=12, d=64, h=128, T_kv=1029120, T_q=8040,

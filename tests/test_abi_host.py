@@ -128,3 +128,15 @@ def test_apply_validation():
     assert lib.lact_apply(ctypes.byref(c), ctypes.byref(s), 256, None, 4, 256, None, 0, None) == B.LACT_ERR_INVALID_ARG
     assert lib.lact_apply(ctypes.byref(c), ctypes.byref(s), 256, 256, 0, 256, None, 0, None) == B.LACT_ERR_INVALID_ARG
     assert lib.lact_apply(ctypes.byref(c), ctypes.byref(s), 256, 256, 8, 100, None, 0, None) == B.LACT_ERR_INVALID_ARG
+
+
+def test_products_mode_validation():
+    lib = L.load_library()
+    c = L.Config(1, 1, 64, 128).to_c()
+    c.products = 7
+    assert lib.lact_workspace_bytes(ctypes.byref(c), 128, 128) == 0
+    s = B.LactState(256, 256, 256, None, None, None)
+    assert lib.lact_update(ctypes.byref(c), ctypes.byref(s), 256, 256, 256, 16, 16 * 64, 16, 256,
+                           1 << 30, None) == B.LACT_ERR_INVALID_ARG
+    assert "products" in lib.lact_last_error().decode()
+    assert L.workspace_bytes(L.Config(1, 1, 64, 128, products="split"), 128, 128) > 0
