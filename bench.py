@@ -41,6 +41,22 @@ def gradient_flops(w: S.Workload) -> float:
     return 12.0 * w.chunk_kv * w.d * w.h * w.pairs
 
 
+def counted_traffic(w: S.Workload):
+    """HBM bytes per gradient launch from the committed rocprofv3 counter
+    summary, if it was taken on this workload from the current kernel source
+    (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "grad_posed_hbm_counters.json")
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if rec.get("workload") != w.name or hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec["bytes_per_dispatch"]
+
+
 def cpu_baseline(w: S.Workload, x, st, budget_s: float = 15.0):
     """The float32 oracle on a bounded sample: whole pairs of the workload,
     as many as fit the time budget (at least one)."""
@@ -158,7 +174,7 @@ def main():
         "bound": "mfma", "achieved": round(grad_tflops, 3) if grad_tflops else None,
         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(grad_tflops / PEAK_BF16_TFLOPS, 4) if grad_tflops else None,
-        "traffic": None, "avg_launch_ms": round(grad_avg, 5),
+        "traffic": counted_traffic(w), "avg_launch_ms": round(grad_avg, 5),
         "flop_per_launch": gradient_flops(w),
     }
     line = {
