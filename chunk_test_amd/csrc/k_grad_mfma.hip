@@ -312,7 +312,8 @@ bool grad_mfma_shape_ok(int d, int h) {
 
 int grad_mfma_stage_tokens(int d) { return 8192 / d; }
 
-int grad_mfma_wgs_per_cu(int d) { return d == 64 ? Geo<64>::WAVES_PER_SIMD : Geo<128>::WAVES_PER_SIMD; }
+// d = 64 runs the two-group variant (k_grad_pp.hip): one 8-wave workgroup per CU
+int grad_mfma_wgs_per_cu(int d) { return d == 64 ? 1 : Geo<128>::WAVES_PER_SIMD; }
 
 hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s) {
   switch (a.d) {

@@ -249,7 +249,13 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
     g.S = sp.S;
     g.tps = sp.tps;
     g.bf16 = p.bf16;
-    e = use_mfma ? lact::launch_grad_mfma(g, s) : lact::launch_grad_simple(g, s);
+    if (!use_mfma) {
+      e = lact::launch_grad_simple(g, s);
+    } else if (p.d == 64) {
+      e = lact::launch_grad_pp(g, s);
+    } else {
+      e = lact::launch_grad_mfma(g, s);
+    }
     if (e != hipSuccess) return hip_fail(e, "gradient kernel");
   }
   {
