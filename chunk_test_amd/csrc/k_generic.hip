@@ -299,6 +299,74 @@ __global__ __launch_bounds__(kThreads) void k_step_norm(StepArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// GD / momentum update tail, one wavefront per stored row: fixed-order sum of
+// the split partials, M <- beta M + g (when kept), W <- W - step g, unit row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_reduce_step(TailArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  const int R = 2 * a.h + a.d;
+  const int64_t pair = row / R;
+  if (pair >= a.P) return;
+  const int r = static_cast<int>(row % R);
+  const int64_t hd = static_cast<int64_t>(a.h) * a.d;
+  float* W;
+  float* M;
+  int64_t po;
+  int len;
+  if (r < a.h) {
+    W = a.W1;
+    M = a.M1;
+    po = static_cast<int64_t>(r) * a.d;
+    len = a.d;
+  } else if (r < 2 * a.h) {
+    W = a.W3;
+    M = a.M3;
+    po = 2 * hd + static_cast<int64_t>(r - a.h) * a.d;
+    len = a.d;
+  } else {
+    W = a.W2;
+    M = a.M2;
+    po = hd + static_cast<int64_t>(r - 2 * a.h) * a.h;
+    len = a.h;
+  }
+  const int64_t wo = pair * hd + (po % hd);  // offset of this row inside its matrix
+  const float* part = a.partials + pair * a.splits * 3 * hd + po;
+  float v[kMaxRowPerLane];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxRowPerLane; ++k) {
+    const int e = lane + 64 * k;
+    v[k] = 0.f;
+    if (e < len) {
+      float g = 0.f;
+      int sp = 0;
+      for (; sp + 8 <= a.splits; sp += 8) {  // eight loads in flight, summed in split order
+        float t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[u] = part[static_cast<int64_t>(sp + u) * 3 * hd + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) g += t[u];
+      }
+      for (; sp < a.splits; ++sp) g += part[static_cast<int64_t>(sp) * 3 * hd + e];
+      if (M != nullptr) {
+        g = a.beta * M[wo + e] + g;
+        M[wo + e] = g;
+      }
+      v[k] = W[wo + e] - a.step * g;
+      ss += v[k] * v[k];
+    }
+  }
+  ss = wave_sum(ss);
+  const float den = fmaxf(sqrtf(ss), a.norm_eps);
+#pragma unroll
+  for (int k = 0; k < kMaxRowPerLane; ++k) {
+    const int e = lane + 64 * k;
+    if (e < len) W[wo + e] = v[k] / den;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Query read O = W2 (silu(W1 q) * (W3 q)).  Grid (ceil(m/32), P); hidden
 // units in slices of 256 staged through LDS.
 // ---------------------------------------------------------------------------
@@ -421,6 +489,13 @@ hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s) {
 
 hipError_t launch_ns_simple(const NSArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(k_ns_generic, dim3(3 * a.P), dim3(kNSThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_step(const TailArgs& a, hipStream_t s) {
+  const int64_t rows = static_cast<int64_t>(a.P) * (2 * a.h + a.d);
+  const unsigned blocks = static_cast<unsigned>((rows + 3) / 4);
+  hipLaunchKernelGGL(k_reduce_step, dim3(blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

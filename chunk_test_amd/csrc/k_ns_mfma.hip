@@ -1,7 +1,10 @@
-// Newton-Schulz orthogonalisation of the matrix gradients (Muon's transform,
-// "LaCT: Large Chunk Test-Time Training" review, section "Local attention
-// and nonlinear memory work together"; coefficients as given in the layer
-// configuration), one workgroup per matrix, on bf16 MFMA with split operands.
+// The update tail of a Muon step, one workgroup per fast-weight matrix
+// (W1, W2 or W3 of one pair): fixed-order sum of the token-split partial
+// gradients, the momentum update when one is kept, Newton-Schulz
+// orthogonalisation (Muon's transform, "LaCT: Large Chunk Test-Time
+// Training" review, section "Local attention and nonlinear memory work
+// together"; coefficients as given in the layer configuration) on bf16 MFMA
+// with split operands, then W <- W - step X and unit L2 rows.
 //
 // X is the s x l orientation of the gradient (s = min(d, h), l = max(d, h)),
 // X0 = G / (||G||_F + eps), then `iters` times
@@ -52,7 +55,7 @@ struct NSGeo {
 };
 
 template <int S, int L>
-__global__ __launch_bounds__(2 * L) void k_ns_mfma(NSArgs a) {
+__global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
   using G = NSGeo<S, L>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[G::REGION];
   __shared__ float red[G::NW];
@@ -60,28 +63,65 @@ __global__ __launch_bounds__(2 * L) void k_ns_mfma(NSArgs a) {
   const int mat = blockIdx.x;
   const int pair = mat / 3, which = mat % 3;  // 0: W1 (h x d), 1: W2 (d x h), 2: W3 (h x d)
   const int64_t hd = static_cast<int64_t>(a.h) * a.d;
-  float* Gm = a.dir + pair * 3 * hd + which * hd;
   const int cols = (which == 1) ? a.h : a.d;
   const bool tr = ((which == 1) ? a.d : a.h) > cols;  // X = G^T when G is tall
+  float* Wm = (which == 0 ? a.W1 : which == 1 ? a.W2 : a.W3) + pair * hd;
+  float* Mm = (a.M1 == nullptr) ? nullptr : (which == 0 ? a.M1 : which == 1 ? a.M2 : a.M3) + pair * hd;
+  const float* part = a.partials + static_cast<int64_t>(pair) * a.splits * 3 * hd + which * hd;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, ln = lane & 31;
   // column tile ct of this wave holds columns 32 (NW ct + w) .. +31
   auto colof = [&](int ct) { return 32 * (G::NW * ct + w) + ln; };
 
-  // ---- X0 = G / (||G||_F + eps), fp32 in registers, MFMA output layout:
-  // x[ct][mt][r] = X[32 mt + 8 (r/4) + 4 g + r%4][colof(ct)].
-  // G is staged through LDS (fp32, row stride XFS) so that the global reads
-  // stay coalesced and the register reads use immediate offsets.
+  // ---- G = sum of the split partials in fixed order (then the momentum
+  // update M <- beta M + G, G <- M), staged through LDS as fp32 X (row stride
+  // XFS) so the global reads stay coalesced and the register reads below use
+  // immediate offsets.  X0 = G / (||G||_F + eps) in registers, MFMA output
+  // layout: x[ct][mt][r] = X[32 mt + 8 (r/4) + 4 g + r%4][colof(ct)].
   constexpr int XFS = 4 * L + 16;
-  float* xf = reinterpret_cast<float*>(lds);
+  constexpr int NV = S * L / 4;  // float4 groups per matrix
+  const float4* part4 = reinterpret_cast<const float4*>(part);
+  const int64_t sstride4 = 3 * hd / 4;
   float ss = 0.f;
-  for (int e = tid; e < S * L; e += 2 * L) {
-    const float v = Gm[e];
-    ss += v * v;
-    const int i = tr ? (e % S) : (e / L);  // row of X
-    const int j = tr ? (e / S) : (e % L);  // column of X
-    *reinterpret_cast<float*>(lds + i * XFS + 4 * j) = v;
+  // eight split loads in flight per group, summed in split order
+#pragma unroll 2
+  for (int c = tid; c < NV; c += 2 * L) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int sp = 0;
+    for (; sp + 8 <= a.splits; sp += 8) {
+      float4 t[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) t[u] = part4[(sp + u) * sstride4 + c];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        acc.x += t[u].x;
+        acc.y += t[u].y;
+        acc.z += t[u].z;
+        acc.w += t[u].w;
+      }
+    }
+    for (; sp < a.splits; ++sp) {
+      const float4 t = part4[sp * sstride4 + c];
+      acc.x += t.x;
+      acc.y += t.y;
+      acc.z += t.z;
+      acc.w += t.w;
+    }
+    const float g4[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * c + q;
+      float v = g4[q];
+      if (Mm != nullptr) {
+        v = a.beta * Mm[e] + v;
+        Mm[e] = v;
+      }
+      ss += v * v;
+      const int i = tr ? (e % S) : (e / L);  // row of X
+      const int j = tr ? (e / S) : (e % L);  // column of X
+      *reinterpret_cast<float*>(lds + i * XFS + 4 * j) = v;
+    }
   }
   ss = wave_sum(ss);
   if (lane == 0) red[w] = ss;
@@ -90,7 +130,6 @@ __global__ __launch_bounds__(2 * L) void k_ns_mfma(NSArgs a) {
 #pragma unroll
   for (int i = 0; i < G::NW; ++i) tot += red[i];
   const float inv_denom = 1.f / (sqrtf(tot) + a.eps);
-  (void)xf;
   f32x16_t x[G::CT][G::MT];
 #pragma unroll
   for (int ct = 0; ct < G::CT; ++ct) {
@@ -105,7 +144,6 @@ __global__ __launch_bounds__(2 * L) void k_ns_mfma(NSArgs a) {
   }
 
   unsigned char* xhi = lds;
-  unsigned char* xlo = lds + G::X_HALF;
   unsigned char* ahi = lds;
   unsigned char* alo = lds + G::A_HALF;
 
@@ -137,8 +175,12 @@ __global__ __launch_bounds__(2 * L) void k_ns_mfma(NSArgs a) {
 #pragma unroll
     for (int q = 0; q < G::ATW; ++q) {
       const int t = w + G::NW * q;
+      f32x16_t a2;  // second accumulator chain (cross terms)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) at[q][r] = 0.f;
+      for (int r = 0; r < 16; ++r) {
+        at[q][r] = 0.f;
+        a2[r] = 0.f;
+      }
       if (t < G::ATILES) {
         const int ti = t / G::MT, tj = t % G::MT;
         const unsigned char* ra = xhi + (32 * ti + ln) * G::XRS + 16 * g;
@@ -150,10 +192,12 @@ __global__ __launch_bounds__(2 * L) void k_ns_mfma(NSArgs a) {
           const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(rb + 32 * ks);
           const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(rb + G::X_HALF + 32 * ks);
           at[q] = mfma(ah, bh, at[q]);
-          at[q] = mfma(ah, bl, at[q]);
-          at[q] = mfma(al, bh, at[q]);
+          a2 = mfma(ah, bl, a2);
+          a2 = mfma(al, bh, a2);
         }
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) at[q][r] += a2[r];
     }
     __syncthreads();  // X row-major no longer needed: the region becomes A
 
@@ -186,9 +230,12 @@ __global__ __launch_bounds__(2 * L) void k_ns_mfma(NSArgs a) {
 #pragma unroll
     for (int q = 0; q < G::ATW; ++q) {
       const int t = w + G::NW * q;
-      f32x16_t acc;
+      f32x16_t acc, a2;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+      for (int r = 0; r < 16; ++r) {
+        acc[r] = 0.f;
+        a2[r] = 0.f;
+      }
       if (t < G::ATILES) {
         const int ti = t / G::MT, tj = t % G::MT;
         const unsigned char* ra = ahi + (32 * ti + ln) * G::ARS + 16 * g;
@@ -200,12 +247,12 @@ __global__ __launch_bounds__(2 * L) void k_ns_mfma(NSArgs a) {
           const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(rb + 32 * ks);
           const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(rb + G::A_HALF + 32 * ks);
           acc = mfma(ah, bh, acc);
-          acc = mfma(ah, bl, acc);
-          acc = mfma(al, bh, acc);
+          a2 = mfma(ah, bl, a2);
+          a2 = mfma(al, bh, a2);
         }
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) at[q][r] = a.b * at[q][r] + a.c * acc[r];  // now B
+      for (int r = 0; r < 16; ++r) at[q][r] = a.b * at[q][r] + a.c * (acc[r] + a2[r]);  // now B
     }
     __syncthreads();  // all reads of A done: the region becomes B
     // B is symmetric too: same store
@@ -243,9 +290,12 @@ __global__ __launch_bounds__(2 * L) void k_ns_mfma(NSArgs a) {
       f32x16_t accs[G::MT];
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt) {
-        f32x16_t acc;
+        f32x16_t acc, a2;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        for (int r = 0; r < 16; ++r) {
+          acc[r] = 0.f;
+          a2[r] = 0.f;
+        }
         const unsigned char* rb = ahi + (32 * mt + ln) * G::ARS + 8 * g;
 #pragma unroll
         for (int s = 0; s < S / 16; ++s) {
@@ -270,10 +320,11 @@ __global__ __launch_bounds__(2 * L) void k_ns_mfma(NSArgs a) {
             bl[4 + i] = l1[i];
           }
           acc = mfma(bh, xh, acc);
-          acc = mfma(bh, xl, acc);
-          acc = mfma(bl, xh, acc);
+          a2 = mfma(bh, xl, a2);
+          a2 = mfma(bl, xh, a2);
         }
-        accs[mt] = acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) accs[mt][r] = acc[r] + a2[r];
       }
       // this column tile is not read again in this iteration: update in place
 #pragma unroll
@@ -284,7 +335,7 @@ __global__ __launch_bounds__(2 * L) void k_ns_mfma(NSArgs a) {
     }
   }
 
-  // ---- result back into the direction buffer, in G's orientation (via LDS)
+  // ---- the result X into LDS (fp32) for the row-wise step
   __syncthreads();
 #pragma unroll
   for (int ct = 0; ct < G::CT; ++ct) {
@@ -298,10 +349,30 @@ __global__ __launch_bounds__(2 * L) void k_ns_mfma(NSArgs a) {
     }
   }
   __syncthreads();
-  for (int e = tid; e < S * L; e += 2 * L) {
-    const int i = tr ? (e % S) : (e / L);
-    const int j = tr ? (e / S) : (e % L);
-    Gm[e] = *reinterpret_cast<const float*>(lds + i * XFS + 4 * j);
+  // ---- W <- W - step X, then unit L2 rows; one wavefront per stored row
+  // (W1, W3 rows are columns of X, W2 rows are rows of X)
+  const int nrows = tr ? L : S;
+  const int rowlen = tr ? S : L;
+  for (int r = w; r < nrows; r += G::NW) {
+    float v[L / 64];
+    float sq = 0.f;
+#pragma unroll
+    for (int k = 0; k < L / 64; ++k) {
+      const int cidx = lane + 64 * k;
+      v[k] = 0.f;
+      if (cidx < rowlen) {
+        const int i = tr ? cidx : r, j = tr ? r : cidx;
+        v[k] = Wm[static_cast<int64_t>(r) * rowlen + cidx] - a.step * *reinterpret_cast<const float*>(lds + i * XFS + 4 * j);
+        sq += v[k] * v[k];
+      }
+    }
+    sq = wave_sum(sq);
+    const float den = fmaxf(sqrtf(sq), a.norm_eps);
+#pragma unroll
+    for (int k = 0; k < L / 64; ++k) {
+      const int cidx = lane + 64 * k;
+      if (cidx < rowlen) Wm[static_cast<int64_t>(r) * rowlen + cidx] = v[k] / den;
+    }
   }
 }
 
@@ -312,15 +383,15 @@ bool ns_mfma_shape_ok(int d, int h) {
   return (s == 64 && l == 128) || (s == 128 && l == 256) || (s == 64 && l == 256);
 }
 
-hipError_t launch_ns_mfma(const NSArgs& a, hipStream_t st) {
+hipError_t launch_muon_tail(const TailArgs& a, hipStream_t st) {
   const int s = a.d < a.h ? a.d : a.h, l = a.d < a.h ? a.h : a.d;
   const dim3 grid(3 * a.P);
   if (s == 64 && l == 128) {
-    hipLaunchKernelGGL((k_ns_mfma<64, 128>), grid, dim3(2 * 128), 0, st, a);
+    hipLaunchKernelGGL((k_muon_tail<64, 128>), grid, dim3(2 * 128), 0, st, a);
   } else if (s == 128 && l == 256) {
-    hipLaunchKernelGGL((k_ns_mfma<128, 256>), grid, dim3(2 * 256), 0, st, a);
+    hipLaunchKernelGGL((k_muon_tail<128, 256>), grid, dim3(2 * 256), 0, st, a);
   } else if (s == 64 && l == 256) {
-    hipLaunchKernelGGL((k_ns_mfma<64, 256>), grid, dim3(2 * 256), 0, st, a);
+    hipLaunchKernelGGL((k_muon_tail<64, 256>), grid, dim3(2 * 256), 0, st, a);
   } else {
     return hipErrorInvalidValue;
   }

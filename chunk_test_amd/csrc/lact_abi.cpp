@@ -258,6 +258,44 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
     }
     if (e != hipSuccess) return hip_fail(e, "gradient kernel");
   }
+  lact::TailArgs ta{};
+  ta.partials = partials;
+  ta.splits = sp.S;
+  if (p.momentum) {
+    ta.M1 = st->M1;
+    ta.M2 = st->M2;
+    ta.M3 = st->M3;
+  }
+  ta.beta = c->beta;
+  ta.W1 = st->W1;
+  ta.W2 = st->W2;
+  ta.W3 = st->W3;
+  ta.step = c->step;
+  ta.norm_eps = c->norm_eps;
+  ta.P = p.P;
+  ta.d = p.d;
+  ta.h = p.h;
+  ta.iters = c->ns_iters;
+  ta.a = c->ns_a;
+  ta.b = c->ns_b;
+  ta.c = c->ns_c;
+  ta.eps = c->ns_eps;
+  if (!p.muon) {
+    // GD / momentum: one row-wise kernel for reduction, momentum, step, unit rows
+    PhaseTimer t(1, s);
+    e = lact::launch_reduce_step(ta, s);
+    if (e != hipSuccess) return hip_fail(e, "update-tail kernel");
+    return LACT_OK;
+  }
+  if (p.bf16 && lact::ns_mfma_shape_ok(p.d, p.h)) {
+    // bf16 mode Muon: one kernel per matrix for reduction, momentum,
+    // split-bf16 MFMA Newton-Schulz, step and unit rows
+    PhaseTimer t(1, s);
+    e = lact::launch_muon_tail(ta, s);
+    if (e != hipSuccess) return hip_fail(e, "Muon update-tail kernel");
+    return LACT_OK;
+  }
+  // fp32 arithmetic Muon: reduction (+momentum), Newton-Schulz, step + unit rows
   {
     PhaseTimer t(1, s);
     lact::ReduceArgs r{};
@@ -276,7 +314,7 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
     e = lact::launch_reduce(r, s);
     if (e != hipSuccess) return hip_fail(e, "reduction kernel");
   }
-  if (p.muon) {
+  {
     PhaseTimer t(2, s);
     lact::NSArgs a{};
     a.dir = dir;
@@ -289,9 +327,7 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
     a.b = c->ns_b;
     a.c = c->ns_c;
     a.eps = c->ns_eps;
-    // bf16 mode: split-bf16 MFMA Newton-Schulz; fp32 mode keeps fp32 arithmetic
-    e = (p.bf16 && lact::ns_mfma_shape_ok(p.d, p.h)) ? lact::launch_ns_mfma(a, s)
-                                                      : lact::launch_ns_simple(a, s);
+    e = lact::launch_ns_simple(a, s);
     if (e != hipSuccess) return hip_fail(e, "Newton-Schulz kernel");
   }
   {

@@ -44,6 +44,20 @@ struct NSArgs {
   float a, b, c, eps;
 };
 
+// Update tails that read the split partials directly (fixed-order sum):
+//   Muon: momentum (optional), Newton-Schulz, step, unit rows (per matrix);
+//   GD / momentum: momentum (optional), step, unit rows (per row).
+struct TailArgs {
+  const float* partials;  // [P, splits, 3hd]
+  int splits;
+  float *M1, *M2, *M3;    // momentum buffers or NULL
+  float beta;
+  float *W1, *W2, *W3;
+  float step, norm_eps;
+  int P, d, h, iters;
+  float a, b, c, eps;     // Newton-Schulz (Muon only)
+};
+
 // W <- W - step * dir, then unit L2 rows.
 struct StepArgs {
   float *W1, *W2, *W3;
@@ -68,6 +82,7 @@ hipError_t launch_grad_simple(const GradArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_ns_simple(const NSArgs& a, hipStream_t s);
 hipError_t launch_step_norm(const StepArgs& a, hipStream_t s);
+hipError_t launch_reduce_step(const TailArgs& a, hipStream_t s);  // GD / momentum tail
 hipError_t launch_apply_simple(const ApplyArgs& a, hipStream_t s);
 bool simple_shape_ok(int d, int h);
 
@@ -80,7 +95,7 @@ hipError_t launch_grad_pp(const GradArgs& a, hipStream_t s);  // d = 64, one 8-w
 bool ns_mfma_shape_ok(int d, int h);
 bool apply_mfma_shape_ok(int d, int h);
 hipError_t launch_apply_mfma(const ApplyArgs& a, hipStream_t s);
-hipError_t launch_ns_mfma(const NSArgs& a, hipStream_t s);
+hipError_t launch_muon_tail(const TailArgs& a, hipStream_t s);  // bf16-mode Muon tail
 size_t ns_simple_scratch_floats(int P, int d, int h);
 
 }  // namespace lact

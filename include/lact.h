@@ -157,8 +157,11 @@ int lact_mfma_path(int32_t d, int32_t h, int32_t io_dtype);
  * While enabled, every entry point records HIP events on its stream around
  * each phase; lact_profile_read() waits for the recorded events, adds their
  * durations into ms[phase] / launches[phase] (arrays of LACT_PROFILE_PHASES)
- * and clears the record.  Phases: 0 gradient, 1 split reduction (+momentum),
- * 2 Newton-Schulz, 3 step + row normalisation, 4 query read. */
+ * and clears the record.  Phases: 0 chunk gradient; 1 update tail (split
+ * reduction and momentum, fused with the step and row normalisation, and
+ * for bf16-mode Muon with Newton-Schulz too); 2 Newton-Schulz and 3 step +
+ * row normalisation when they run as kernels of their own (fp32-arithmetic
+ * Muon); 4 query read. */
 #define LACT_PROFILE_PHASES 5
 int lact_profile_enable(int on);
 int lact_profile_read(double* ms, int64_t* launches);
