@@ -35,8 +35,8 @@ constexpr int kThreads = 256;
 constexpr int kHidPerWave = 32;
 // The key projection through W1 is computed pre-scaled by -log2(e), so the
 // sigmoid needs no extra multiply: sigmoid(h1) = 1 / (1 + 2^(-log2(e) h1)).
-// G and dH3 then carry the same factor, removed once from dW2 and dW3 at
-// the end (times -ln 2).
+// G, dH3 and dH1 then carry the same factor, removed once from the three
+// sums at the end (times -ln 2).
 constexpr float kNegLog2e = -1.4426950408889634f;
 constexpr float kNegLn2 = -0.6931471805599453f;
 constexpr int kHidPerWG = 128;
@@ -167,19 +167,18 @@ void k_grad_mfma(GradArgs a, int hsl, int nbase) {
 
   u32x4_t kr[4], vr[4];
   float er[4];
+  // Tokens past the end of the split re-read the split's last token with
+  // eta = 0: u = 0 and dg = 0 then, so they add nothing to any of the three
+  // sums (finite inputs), and the loads need no branches.
   auto load_stage = [&](int64_t t0) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int64_t tok = t0 + t_first + k;
-      if (tok < t_end) {
-        kr[k] = *reinterpret_cast<const u32x4_t*>(Kg + tok * D + 8 * c);
-        vr[k] = *reinterpret_cast<const u32x4_t*>(Vg + tok * D + 8 * c);
-        er[k] = etag[tok];
-      } else {
-        kr[k] = u32x4_t{0u, 0u, 0u, 0u};
-        vr[k] = u32x4_t{0u, 0u, 0u, 0u};
-        er[k] = 0.f;
-      }
+      const int64_t tc = tok < t_end ? tok : t_end - 1;
+      kr[k] = *reinterpret_cast<const u32x4_t*>(Kg + tc * D + 8 * c);
+      vr[k] = *reinterpret_cast<const u32x4_t*>(Vg + tc * D + 8 * c);
+      const float ev = etag[tc];
+      er[k] = tok < t_end ? ev : 0.f;
     }
   };
 
@@ -201,18 +200,13 @@ void k_grad_mfma(GradArgs a, int hsl, int nbase) {
     for (int j = 0; j < 8; ++j) {
       const int dd = 8 * c + j;
       const int w = j >> 1;
+      // (low halves of tokens 0,1 | high halves) -> one byte permute each
+      const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
       u32x2_t pk, pu;
-      if (j & 1) {
-        pk[0] = (kr[0][w] >> 16) | (kr[1][w] & 0xffff0000u);
-        pk[1] = (kr[2][w] >> 16) | (kr[3][w] & 0xffff0000u);
-        pu[0] = (ur[0][w] >> 16) | (ur[1][w] & 0xffff0000u);
-        pu[1] = (ur[2][w] >> 16) | (ur[3][w] & 0xffff0000u);
-      } else {
-        pk[0] = (kr[0][w] & 0xffffu) | (kr[1][w] << 16);
-        pk[1] = (kr[2][w] & 0xffffu) | (kr[3][w] << 16);
-        pu[0] = (ur[0][w] & 0xffffu) | (ur[1][w] << 16);
-        pu[1] = (ur[2][w] & 0xffffu) | (ur[3][w] << 16);
-      }
+      pk[0] = __builtin_amdgcn_perm(kr[1][w], kr[0][w], sel);
+      pk[1] = __builtin_amdgcn_perm(kr[3][w], kr[2][w], sel);
+      pu[0] = __builtin_amdgcn_perm(ur[1][w], ur[0][w], sel);
+      pu[1] = __builtin_amdgcn_perm(ur[3][w], ur[2][w], sel);
       const int off = tr_off<D>(s16, dd, hf) + 8 * sub;
       *reinterpret_cast<u32x2_t*>(lds + G::OFF_KT + off) = pk;
       *reinterpret_cast<u32x2_t*>(lds + G::OFF_UT + off) = pu;
@@ -248,10 +242,12 @@ void k_grad_mfma(GradArgs a, int hsl, int nbase) {
         cg = __builtin_amdgcn_mfma_f32_32x32x16_bf16(au, w2b[ks], cg, 0, 0, 0);
       }
       // SwiGLU forward and backward, then the token contractions, one k-step
-      // (16 tokens) at a time.  With z = -log2(e) h1 (from the scaled W1):
-      //   s = 1 / (1 + 2^z),  a' = z s = -log2(e) silu(h1),
-      //   g' = a' h3,  dh3' = dg a',  silu'(h1) = s + a (1 - s) = s - ln2 a' (1 - s),
-      //   dh1 = dg h3 silu'(h1).
+      // (16 tokens) at a time.  With z = -log2(e) h1 (from the scaled W1),
+      // s = sigmoid(h1) = 1 / (1 + 2^z) and a = silu(h1), g = a h3:
+      //   a' = z s = -log2(e) a,   g' = a' h3 = -log2(e) g,   dh3' = dg a',
+      //   dh1 = dg h3 s (1 + h1 (1 - s)) = dg (g + s (h3 - g)),
+      //   dh1' = dg (g' + s t'),  t' = -log2(e) h3 - g'   (= -log2(e) dh1),
+      // so all three carry -log2(e), removed once at the end (times -ln 2).
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         bf16x8_t pg, pd1, pd3;
@@ -261,10 +257,11 @@ void k_grad_mfma(GradArgs a, int hsl, int nbase) {
           const float z = c1[r], h3 = c3[r], dg = cg[r];
           const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(z));
           const float act = z * sg;
-          pg[i] = static_cast<__bf16>(act * h3);
+          const float gs = act * h3;
+          pg[i] = static_cast<__bf16>(gs);
           pd3[i] = static_cast<__bf16>(dg * act);
-          const float u = fmaf(-act, sg, act);
-          pd1[i] = static_cast<__bf16>((dg * h3) * fmaf(kNegLn2, u, sg));
+          const float t = fmaf(h3, kNegLog2e, -gs);
+          pd1[i] = static_cast<__bf16>(dg * fmaf(sg, t, gs));
         }
         const int grp = 2 * st + s;
 #pragma unroll
@@ -288,7 +285,7 @@ void k_grad_mfma(GradArgs a, int hsl, int nbase) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 8 * (r >> 2) + 4 * g + (r & 3);
-      out[static_cast<int64_t>(n0 + row) * D + 32 * nt + ln] = aW1[nt][r];
+      out[static_cast<int64_t>(n0 + row) * D + 32 * nt + ln] = kNegLn2 * aW1[nt][r];
       out[2 * hd + static_cast<int64_t>(n0 + row) * D + 32 * nt + ln] = kNegLn2 * aW3[nt][r];
       out[hd + static_cast<int64_t>(32 * nt + row) * h + n0 + ln] = kNegLn2 * aW2[nt][r];
     }
@@ -312,8 +309,7 @@ bool grad_mfma_shape_ok(int d, int h) {
 
 int grad_mfma_stage_tokens(int d) { return 8192 / d; }
 
-// d = 64 runs the two-group variant (k_grad_pp.hip): one 8-wave workgroup per CU
-int grad_mfma_wgs_per_cu(int d) { return d == 64 ? 1 : Geo<128>::WAVES_PER_SIMD; }
+int grad_mfma_wgs_per_cu(int d) { return d == 64 ? Geo<64>::WAVES_PER_SIMD : Geo<128>::WAVES_PER_SIMD; }
 
 hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s) {
   switch (a.d) {

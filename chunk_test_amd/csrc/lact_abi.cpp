@@ -251,8 +251,6 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
     g.bf16 = p.bf16;
     if (!use_mfma) {
       e = lact::launch_grad_simple(g, s);
-    } else if (p.d == 64) {
-      e = lact::launch_grad_pp(g, s);
     } else {
       e = lact::launch_grad_mfma(g, s);
     }
