@@ -170,15 +170,19 @@ void k_grad_mfma(GradArgs a, int hsl, int nbase) {
   // Tokens past the end of the split re-read the split's last token with
   // eta = 0: u = 0 and dg = 0 then, so they add nothing to any of the three
   // sums (finite inputs), and the loads need no branches.
+  // (token offsets inside one pair's rows fit 32 bits: the host routes
+  // longer sequences elsewhere)
+  const int t_last = static_cast<int>(t_end - 1);
   auto load_stage = [&](int64_t t0) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int64_t tok = t0 + t_first + k;
-      const int64_t tc = tok < t_end ? tok : t_end - 1;
-      kr[k] = *reinterpret_cast<const u32x4_t*>(Kg + tc * D + 8 * c);
-      vr[k] = *reinterpret_cast<const u32x4_t*>(Vg + tc * D + 8 * c);
-      const float ev = etag[tc];
-      er[k] = tok < t_end ? ev : 0.f;
+      const int tok = static_cast<int>(t0) + t_first + k;
+      const int tc = tok < t_last ? tok : t_last;
+      const unsigned off = static_cast<unsigned>(tc) * D + 8 * c;
+      kr[k] = *reinterpret_cast<const u32x4_t*>(Kg + off);
+      vr[k] = *reinterpret_cast<const u32x4_t*>(Vg + off);
+      const float ev = etag[static_cast<unsigned>(tc)];
+      er[k] = tok <= t_last ? ev : 0.f;
     }
   };
 

@@ -222,10 +222,12 @@ size_t io_bytes(const Plan& p) { return p.bf16 ? 2 : 4; }
 int run_update(const lact_config* c, const Plan& p, const lact_state* st, const void* K,
                const void* V, const float* eta, int64_t n, int64_t kv_stride,
                int64_t eta_stride, char* ws, const WsLayout& L, hipStream_t s) {
-  // the MFMA kernel reads 16-byte rows: it needs aligned K, V and strides
-  // (split products: the fp32-arithmetic kernel)
+  // the MFMA kernel reads 16-byte rows with 32-bit offsets inside a pair's
+  // rows: it needs aligned K, V and strides and n d < 2^31 (split products:
+  // the fp32-arithmetic kernel)
   const bool use_mfma = p.mfma && !p.split && (reinterpret_cast<uintptr_t>(K) % 16 == 0) &&
-                        (reinterpret_cast<uintptr_t>(V) % 16 == 0) && (kv_stride % 8 == 0);
+                        (reinterpret_cast<uintptr_t>(V) % 16 == 0) && (kv_stride % 8 == 0) &&
+                        n * p.d < (static_cast<int64_t>(1) << 31);
   const Splits sp = plan_splits(use_mfma ? mfma_rule(p) : generic_rule(p), n);
   float* partials = reinterpret_cast<float*>(ws + L.partials);
   float* dir = reinterpret_cast<float*>(ws + L.dir);
@@ -251,6 +253,8 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
     g.bf16 = p.bf16;
     if (!use_mfma) {
       e = lact::launch_grad_simple(g, s);
+    } else if (lact::grad_d64_shape_ok(p.d, p.h)) {
+      e = lact::launch_grad_d64(g, s);
     } else {
       e = lact::launch_grad_mfma(g, s);
     }

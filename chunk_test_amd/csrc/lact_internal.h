@@ -91,7 +91,8 @@ bool grad_mfma_shape_ok(int d, int h);
 int grad_mfma_stage_tokens(int d);  // token splits must be multiples of this
 int grad_mfma_wgs_per_cu(int d);    // resident workgroups per CU
 hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s);
-hipError_t launch_grad_pp(const GradArgs& a, hipStream_t s);  // d = 64, one 8-wave workgroup per CU
+bool grad_d64_shape_ok(int d, int h);  // d = 64, LDS-DMA staging
+hipError_t launch_grad_d64(const GradArgs& a, hipStream_t s);
 bool ns_mfma_shape_ok(int d, int h);
 bool apply_mfma_shape_ok(int d, int h);
 hipError_t launch_apply_mfma(const ApplyArgs& a, hipStream_t s);
