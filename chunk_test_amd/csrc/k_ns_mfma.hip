@@ -83,32 +83,47 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
   constexpr int NV = S * L / 4;  // float4 groups per matrix
   const float4* part4 = reinterpret_cast<const float4*>(part);
   const int64_t sstride4 = 3 * hd / 4;
-  float ss = 0.f;
-  // eight split loads in flight per group, summed in split order
-#pragma unroll 2
-  for (int c = tid; c < NV; c += 2 * L) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int sp = 0;
-    for (; sp + 8 <= a.splits; sp += 8) {
-      float4 t[8];
+  // every thread sums CPT float4 groups (tid + 2 L k) over the splits, with
+  // UD splits x CPT groups of loads in flight, in split order
+  constexpr int CPT = NV / (2 * L);
+  constexpr int UD = CPT >= 32 ? 1 : 32 / CPT;
+  float4 acc[CPT];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) t[u] = part4[(sp + u) * sstride4 + c];
+  for (int k = 0; k < CPT; ++k) acc[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  int sp = 0;
+  for (; sp + UD <= a.splits; sp += UD) {
+    float4 t[UD][CPT];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        acc.x += t[u].x;
-        acc.y += t[u].y;
-        acc.z += t[u].z;
-        acc.w += t[u].w;
+    for (int u = 0; u < UD; ++u) {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) t[u][k] = part4[(sp + u) * sstride4 + tid + 2 * L * k];
+    }
+#pragma unroll
+    for (int u = 0; u < UD; ++u) {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        acc[k].x += t[u][k].x;
+        acc[k].y += t[u][k].y;
+        acc[k].z += t[u][k].z;
+        acc[k].w += t[u][k].w;
       }
     }
-    for (; sp < a.splits; ++sp) {
-      const float4 t = part4[sp * sstride4 + c];
-      acc.x += t.x;
-      acc.y += t.y;
-      acc.z += t.z;
-      acc.w += t.w;
+  }
+  for (; sp < a.splits; ++sp) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const float4 t = part4[sp * sstride4 + tid + 2 * L * k];
+      acc[k].x += t.x;
+      acc[k].y += t.y;
+      acc[k].z += t.z;
+      acc[k].w += t.w;
     }
-    const float g4[4] = {acc.x, acc.y, acc.z, acc.w};
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int c = tid + 2 * L * k;
+    const float g4[4] = {acc[k].x, acc[k].y, acc[k].z, acc[k].w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = 4 * c + q;
