@@ -102,12 +102,19 @@ struct SplitRule {
   int64_t align;          // tokens per split are a multiple of this
 };
 
-Splits plan_splits(const SplitRule& r, int64_t n) {
+// Upper bound of the split count for n tokens; non-decreasing in n, and
+// plan_splits never exceeds it (the workspace is sized with it).
+int64_t split_bound(const SplitRule& r, int64_t n) {
   int64_t S = (r.target_wgs + r.wgs_per_split - 1) / r.wgs_per_split;
   const int64_t by_size = (n + r.min_tokens - 1) / r.min_tokens;
   if (S > by_size) S = by_size;
   if (S > 4096) S = 4096;
   if (S < 1) S = 1;
+  return S;
+}
+
+Splits plan_splits(const SplitRule& r, int64_t n) {
+  int64_t S = split_bound(r, n);
   int64_t tps = (n + S - 1) / S;
   tps = (tps + r.align - 1) / r.align * r.align;
   S = (n + tps - 1) / tps;
@@ -119,16 +126,38 @@ SplitRule generic_rule(const Plan& p) {
   return {static_cast<int64_t>(p.P) * (p.h / 32), 1024, 256, 128};
 }
 
-// MFMA kernel: one workgroup per (split, 128 hidden units, pair), sized to
-// one round of resident workgroups on 256 CUs (two per CU at d = 64, one at
-// d = 128), rounding the split count down so no second round is started.
-SplitRule mfma_rule(const Plan& p) {
-  const int64_t stage = lact::grad_mfma_stage_tokens(p.d);
+// Which chunk-gradient kernel runs.  The MFMA kernels read 16-byte rows with
+// 32-bit offsets inside a pair's rows: they need aligned K, V and strides and
+// n d < 2^31.  Split products run on MFMA at d = 128 only.
+enum class GradKind { Generic, D64, D128, Mfma };
+
+struct GradChoice {
+  GradKind kind;
+  int stage;        // token splits are multiples of this
+  int wgs_per_cu;   // resident workgroups per CU
+};
+
+GradChoice grad_choice(const Plan& p, bool aligned, int64_t n) {
+  const bool fits = aligned && n * p.d < (static_cast<int64_t>(1) << 31);
+  if (p.mfma && fits) {
+    if (!p.split && lact::grad_d64_shape_ok(p.d, p.h)) return {GradKind::D64, 128, 2};
+    if (lact::grad_d128_shape_ok(p.d, p.h))
+      return {GradKind::D128, lact::grad_d128_stage_tokens(p.split), 1};
+    if (!p.split && lact::grad_mfma_shape_ok(p.d, p.h))
+      return {GradKind::Mfma, lact::grad_mfma_stage_tokens(p.d), lact::grad_mfma_wgs_per_cu(p.d)};
+  }
+  return {GradKind::Generic, 1, 0};
+}
+
+// MFMA kernels: one workgroup per (split, 128 hidden units, pair), sized to
+// one round of resident workgroups on 256 CUs, rounding the split count
+// down so no second round is started.
+SplitRule mfma_rule(const Plan& p, const GradChoice& k) {
   const int64_t per_split = static_cast<int64_t>(p.P) * (p.h / 128);
-  const int64_t resident = 256 * lact::grad_mfma_wgs_per_cu(p.d);
+  const int64_t resident = 256 * k.wgs_per_cu;
   int64_t target = (resident / per_split) * per_split;
   if (target < per_split) target = per_split;
-  return {per_split, target, 4 * stage, stage};
+  return {per_split, target, 4 * static_cast<int64_t>(k.stage), k.stage};
 }
 
 bool finite(float x) { return std::isfinite(x); }
@@ -189,9 +218,11 @@ WsLayout ws_layout(const Plan& p, int64_t max_chunk_kv) {
   WsLayout w;
   const size_t per = static_cast<size_t>(3) * p.h * p.d;
   const int64_t n = max_chunk_kv < 1 ? 1 : max_chunk_kv;
-  int64_t S = plan_splits(generic_rule(p), n).S;
-  if (p.mfma) {
-    const int64_t sm = plan_splits(mfma_rule(p), n).S;
+  // every kernel the update may pick for up to n tokens
+  int64_t S = split_bound(generic_rule(p), n);
+  const GradChoice k = grad_choice(p, true, 0);
+  if (k.kind != GradKind::Generic) {
+    const int64_t sm = split_bound(mfma_rule(p, k), n);
     if (sm > S) S = sm;
   }
   size_t off = 0;
@@ -222,13 +253,10 @@ size_t io_bytes(const Plan& p) { return p.bf16 ? 2 : 4; }
 int run_update(const lact_config* c, const Plan& p, const lact_state* st, const void* K,
                const void* V, const float* eta, int64_t n, int64_t kv_stride,
                int64_t eta_stride, char* ws, const WsLayout& L, hipStream_t s) {
-  // the MFMA kernel reads 16-byte rows with 32-bit offsets inside a pair's
-  // rows: it needs aligned K, V and strides and n d < 2^31 (split products:
-  // the fp32-arithmetic kernel)
-  const bool use_mfma = p.mfma && !p.split && (reinterpret_cast<uintptr_t>(K) % 16 == 0) &&
-                        (reinterpret_cast<uintptr_t>(V) % 16 == 0) && (kv_stride % 8 == 0) &&
-                        n * p.d < (static_cast<int64_t>(1) << 31);
-  const Splits sp = plan_splits(use_mfma ? mfma_rule(p) : generic_rule(p), n);
+  const bool aligned = (reinterpret_cast<uintptr_t>(K) % 16 == 0) &&
+                       (reinterpret_cast<uintptr_t>(V) % 16 == 0) && (kv_stride % 8 == 0);
+  const GradChoice gk = grad_choice(p, aligned, n);
+  const Splits sp = plan_splits(gk.kind == GradKind::Generic ? generic_rule(p) : mfma_rule(p, gk), n);
   float* partials = reinterpret_cast<float*>(ws + L.partials);
   float* dir = reinterpret_cast<float*>(ws + L.dir);
   hipError_t e;
@@ -251,12 +279,11 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
     g.S = sp.S;
     g.tps = sp.tps;
     g.bf16 = p.bf16;
-    if (!use_mfma) {
-      e = lact::launch_grad_simple(g, s);
-    } else if (lact::grad_d64_shape_ok(p.d, p.h)) {
-      e = lact::launch_grad_d64(g, s);
-    } else {
-      e = lact::launch_grad_mfma(g, s);
+    switch (gk.kind) {
+      case GradKind::D64: e = lact::launch_grad_d64(g, s); break;
+      case GradKind::D128: e = lact::launch_grad_d128(g, p.split, s); break;
+      case GradKind::Mfma: e = lact::launch_grad_mfma(g, s); break;
+      default: e = lact::launch_grad_simple(g, s); break;
     }
     if (e != hipSuccess) return hip_fail(e, "gradient kernel");
   }

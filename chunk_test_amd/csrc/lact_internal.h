@@ -93,6 +93,9 @@ int grad_mfma_wgs_per_cu(int d);    // resident workgroups per CU
 hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s);
 bool grad_d64_shape_ok(int d, int h);  // d = 64, LDS-DMA staging
 hipError_t launch_grad_d64(const GradArgs& a, hipStream_t s);
+bool grad_d128_shape_ok(int d, int h);  // d = 128, LDS-DMA staging, bf16 or split products
+int grad_d128_stage_tokens(bool split);
+hipError_t launch_grad_d128(const GradArgs& a, bool split, hipStream_t s);
 bool ns_mfma_shape_ok(int d, int h);
 bool apply_mfma_shape_ok(int d, int h);
 hipError_t launch_apply_mfma(const ApplyArgs& a, hipStream_t s);
