@@ -46,7 +46,7 @@ def counted_traffic(w: S.Workload):
     summary, if it was taken on this workload from the current kernel source
     (else None)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "grad_posed_hbm_counters.json")
+    path = os.path.join(ROOT, "profiles", f"grad_{w.name}_hbm_counters.json")
     try:
         rec = json.load(open(path))
         src = open(os.path.join(ROOT, rec["source"]), "rb").read()

@@ -129,7 +129,7 @@ SplitRule generic_rule(const Plan& p) {
 // Which chunk-gradient kernel runs.  The MFMA kernels read 16-byte rows with
 // 32-bit offsets inside a pair's rows: they need aligned K, V and strides and
 // n d < 2^31.  Split products run on MFMA at d = 128 only.
-enum class GradKind { Generic, D64, D128, Mfma };
+enum class GradKind { Generic, D64, D128 };
 
 struct GradChoice {
   GradKind kind;
@@ -143,8 +143,6 @@ GradChoice grad_choice(const Plan& p, bool aligned, int64_t n) {
     if (!p.split && lact::grad_d64_shape_ok(p.d, p.h)) return {GradKind::D64, 128, 2};
     if (lact::grad_d128_shape_ok(p.d, p.h))
       return {GradKind::D128, lact::grad_d128_stage_tokens(p.split), 1};
-    if (!p.split && lact::grad_mfma_shape_ok(p.d, p.h))
-      return {GradKind::Mfma, lact::grad_mfma_stage_tokens(p.d), lact::grad_mfma_wgs_per_cu(p.d)};
   }
   return {GradKind::Generic, 1, 0};
 }
@@ -282,7 +280,6 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
     switch (gk.kind) {
       case GradKind::D64: e = lact::launch_grad_d64(g, s); break;
       case GradKind::D128: e = lact::launch_grad_d128(g, p.split, s); break;
-      case GradKind::Mfma: e = lact::launch_grad_mfma(g, s); break;
       default: e = lact::launch_grad_simple(g, s); break;
     }
     if (e != hipSuccess) return hip_fail(e, "gradient kernel");
@@ -422,7 +419,7 @@ void lact_config_default(lact_config* c) {
 
 int lact_mfma_path(int32_t d, int32_t h, int32_t io_dtype) {
   if (!lact::simple_shape_ok(d, h)) return -1;
-  return (io_dtype == LACT_BF16 && lact::grad_mfma_shape_ok(d, h)) ? 1 : 0;
+  return (io_dtype == LACT_BF16 && (lact::grad_d64_shape_ok(d, h) || lact::grad_d128_shape_ok(d, h))) ? 1 : 0;
 }
 
 size_t lact_workspace_bytes(const lact_config* cfg, int64_t max_chunk_kv, int64_t max_chunk_q) {

@@ -87,10 +87,6 @@ hipError_t launch_apply_simple(const ApplyArgs& a, hipStream_t s);
 bool simple_shape_ok(int d, int h);
 
 // ---- bf16 MFMA kernels (gfx950) ----
-bool grad_mfma_shape_ok(int d, int h);
-int grad_mfma_stage_tokens(int d);  // token splits must be multiples of this
-int grad_mfma_wgs_per_cu(int d);    // resident workgroups per CU
-hipError_t launch_grad_mfma(const GradArgs& a, hipStream_t s);
 bool grad_d64_shape_ok(int d, int h);  // d = 64, LDS-DMA staging
 hipError_t launch_grad_d64(const GradArgs& a, hipStream_t s);
 bool grad_d128_shape_ok(int d, int h);  // d = 128, LDS-DMA staging, bf16 or split products
