@@ -150,7 +150,15 @@ __global__ __launch_bounds__(kThreads) void k_reduce(ReduceArgs a) {
   const int64_t pair = i / per, e = i % per;
   const float* src = a.partials + pair * a.S * per + e;
   float g = 0.f;
-  for (int s = 0; s < a.S; ++s) g += src[static_cast<int64_t>(s) * per];
+  int s = 0;
+  for (; s + 8 <= a.S; s += 8) {  // eight loads in flight, summed in split order
+    float t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = src[static_cast<int64_t>(s + u) * per];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) g += t[u];
+  }
+  for (; s < a.S; ++s) g += src[static_cast<int64_t>(s) * per];
   if (a.M1 != nullptr) {
     float* M;
     int64_t off;

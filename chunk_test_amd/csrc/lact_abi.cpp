@@ -131,6 +131,10 @@ SplitRule generic_rule(const Plan& p) {
 // n d < 2^31.  Split products run on MFMA at d = 128 only.
 enum class GradKind { Generic, D64, D128 };
 
+// Above this many token splits the Muon tail's partial sum runs as a
+// separate all-CU kernel.
+constexpr int kTailSplitsInline = 8;
+
 struct GradChoice {
   GradKind kind;
   int stage;        // token splits are multiples of this
@@ -315,8 +319,30 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
   }
   if (p.bf16 && lact::ns_mfma_shape_ok(p.d, p.h)) {
     // bf16 mode Muon: one kernel per matrix for reduction, momentum,
-    // split-bf16 MFMA Newton-Schulz, step and unit rows
+    // split-bf16 MFMA Newton-Schulz, step and unit rows.  With many splits
+    // the partial sum goes first to a kernel that spreads it over every CU
+    // (the tail then reads one reduced gradient per matrix).
     PhaseTimer t(1, s);
+    if (sp.S > kTailSplitsInline) {
+      lact::ReduceArgs r{};
+      r.partials = partials;
+      r.dir = dir;
+      if (p.momentum) {
+        r.M1 = st->M1;
+        r.M2 = st->M2;
+        r.M3 = st->M3;
+      }
+      r.beta = c->beta;
+      r.P = p.P;
+      r.d = p.d;
+      r.h = p.h;
+      r.S = sp.S;
+      e = lact::launch_reduce(r, s);
+      if (e != hipSuccess) return hip_fail(e, "reduction kernel");
+      ta.partials = dir;
+      ta.splits = 1;
+      ta.M1 = ta.M2 = ta.M3 = nullptr;
+    }
     e = lact::launch_muon_tail(ta, s);
     if (e != hipSuccess) return hip_fail(e, "Muon update-tail kernel");
     return LACT_OK;

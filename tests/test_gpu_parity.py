@@ -47,6 +47,16 @@ SMALL_CASES = [
           opt="momentum", beta=0.9),
     # bf16, two 128-unit hidden slices at d = 64
     small("posed", name="posed-h256", H=2, h=256, T_kv=5000, T_q=64, chunk_kv=5000, chunk_q=64),
+    # bf16 Muon with momentum at d = 64 (the Muon tail's momentum buffer)
+    small("posed", name="posed-muon-momentum", H=2, T_kv=9000, T_q=256, chunk_kv=9000, chunk_q=256,
+          beta=0.5),
+    # split products at d = 128, chunks of 1000 keys (ragged against the 64-token stage)
+    small("video", name="video-ragged", H=2, T_kv=3000, T_q=3000, chunk_kv=1000, chunk_q=1000),
+    # split products with momentum under Muon
+    small("video", name="video-muon-momentum", H=1, T_kv=2 * 4096, T_q=2 * 4096, beta=0.5),
+    # bf16 at d = 128 with four 128-unit hidden slices, ragged chunks
+    small("lm", name="lm-h512-ragged", B=1, H=2, h=512, T_kv=3000, T_q=600, chunk_kv=1500,
+          chunk_q=300),
 ]
 
 
