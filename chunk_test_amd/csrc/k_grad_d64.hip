@@ -50,10 +50,13 @@ constexpr int KS = D / 16;           // k-steps of the projections
 constexpr int NT = D / 32;           // 32-wide d tiles of the contractions
 constexpr int ROW = 2 * D;           // bytes per token row (eight 16-byte chunks)
 constexpr int TILE = TT * ROW;       // one stage of K (or V)
-constexpr int OFF_K = 0;             // K[2]
-constexpr int OFF_V = 2 * TILE;      // V[2]
-constexpr int OFF_E = 4 * TILE;      // eta[2]
-constexpr int LDS_BYTES = 4 * TILE + 2 * TT * 4;
+// one stage buffer: K tile, V tile, eta; two buffers as separate LDS arrays
+// (so the compiler sees that reads of one never alias the DMA into the other
+// and puts no wait for the in-flight loads before them)
+constexpr int OFF_K = 0;
+constexpr int OFF_V = TILE;
+constexpr int OFF_E = 2 * TILE;
+constexpr int BUF_BYTES = 2 * TILE + TT * 4;
 
 // W1 enters pre-scaled by -log2(e) (sigmoid(h1) = 1 / (1 + 2^z), z = -log2(e) h1);
 // G, dH3 and dH1 then carry that factor, removed at the end (times -ln 2).
@@ -81,7 +84,8 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_grad_d64(GradArgs a, int hsl, int nbase) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char buf0[BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char buf1[BUF_BYTES];
 
   // XCD-aware block order: the hidden slices of one (pair, split) land on
   // the same XCD (block ids congruent mod 8) so their key/value reads share L2.
@@ -150,7 +154,7 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
   // move 64 eta values each.  Rows past the end re-read the split's last
   // token (finite values); their eta is written as 0 instead of loaded, so
   // they add nothing to the sums.
-  auto dma_stage = [&](int64_t t0, int b) {
+  auto dma_stage = [&](int64_t t0, unsigned char* dst) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int piece = 4 * wv + k;
@@ -159,16 +163,16 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
       const int tok = static_cast<int>(t0) + r;
       const int tc = tok < t_last ? tok : t_last;
       const unsigned off = static_cast<unsigned>(tc) * D + 8 * cl;
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Kg + off), (lds_ptr_t)(lds + OFF_K + b * TILE + 1024 * piece), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Vg + off), (lds_ptr_t)(lds + OFF_V + b * TILE + 1024 * piece), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Kg + off), (lds_ptr_t)(dst + OFF_K + 1024 * piece), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Vg + off), (lds_ptr_t)(dst + OFF_V + 1024 * piece), 16, 0, 0);
     }
     if (wv < 2) {
       const int tok = static_cast<int>(t0) + 64 * wv + lane;
       if (tok <= t_last) {
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)(etag + static_cast<unsigned>(tok)),
-                                         (lds_ptr_t)(lds + OFF_E + b * TT * 4 + 256 * wv), 4, 0, 0);
+                                         (lds_ptr_t)(dst + OFF_E + 256 * wv), 4, 0, 0);
       } else {
-        *reinterpret_cast<float*>(lds + OFF_E + b * TT * 4 + 256 * wv + 4 * lane) = 0.f;
+        *reinterpret_cast<float*>(dst + OFF_E + 256 * wv + 4 * lane) = 0.f;
       }
     }
   };
@@ -179,19 +183,18 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
   // holds feature 32 nt + 16 (Q & 1) + 4 a + b' of those four tokens.
   const int tq = lane >> 4, tk = (lane >> 2) & 3, ta = lane & 3;
 
-  if (t_begin < t_end) dma_stage(t_begin, 0);
-  int b = 0;
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += TT, b ^= 1) {
+  // one stage: compute on buffer cur while the next stage loads into nxt
+  auto stage = [&](int64_t t0, const unsigned char* cur, unsigned char* nxt) {
     // this stage has landed (each wave waits for its own loads, the barrier
     // for everyone's, and makes the eta zeros visible); every wave is past
     // the previous stage, so its buffer can take the next one
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (t0 + TT < t_end) dma_stage(t0 + TT, b ^ 1);
+    if (t0 + TT < t_end) dma_stage(t0 + TT, nxt);
 
-    const unsigned char* kb = lds + OFF_K + b * TILE;
-    const unsigned char* vb = lds + OFF_V + b * TILE;
-    const float* eb = reinterpret_cast<const float*>(lds + OFF_E + b * TT * 4);
+    const unsigned char* kb = cur + OFF_K;
+    const unsigned char* vb = cur + OFF_V;
+    const float* eb = reinterpret_cast<const float*>(cur + OFF_E);
 
 #pragma unroll 1
     for (int st = 0; st < SUB; ++st) {
@@ -261,6 +264,14 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
         }
       }
     }
+  };
+
+  // stages alternate between the two buffers (unrolled by two, so every
+  // access names its buffer statically)
+  if (t_begin < t_end) dma_stage(t_begin, buf0);
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += 2 * TT) {
+    stage(t0, buf0, buf1);
+    if (t0 + TT < t_end) stage(t0 + TT, buf1, buf0);
   }
 
   // ---- partial sums of this split: [W1 block h x D | W2 block D x h | W3 block h x D]
