@@ -4,12 +4,14 @@
 // memory work together" and "Update order must respect the task").
 //
 // A workgroup (4 wavefronts) owns one pair and a contiguous run of queries.
-// W1 and W3 are staged once into LDS as bf16; each wavefront keeps its
-// 32 rows of W2 in registers.  Per step of 64 (d = 64) or 32 (d = 128)
-// queries:
+// Each wavefront keeps its 32 rows of W2 and, where they fit (h = 128), the
+// W1 and W3 rows of its quarter of the hidden units as bf16 MFMA operands in
+// registers; otherwise W1 and W3 are staged once into LDS.  Per step
+// of 64 (d = 64) or 32 (d = 128) queries:
 //   1. wave w computes H1^T, H3^T = W1 Q^T, W3 Q^T for its quarter of the
-//      hidden units (A = W rows from LDS, B = query rows from LDS), gates
-//      them, G = silu(H1) * H3, and writes G (bf16) to LDS as [token][hidden];
+//      hidden units (A = W rows, B = query rows from LDS),
+//      gates them, G = silu(H1) * H3, and writes G (bf16) to LDS as
+//      [token][hidden];
 //   2. wave w computes one 32 x 32 tile of O^T = W2 G^T (A = its W2 rows,
 //      B = G rows from LDS) and stores it.
 // All LDS tiles are XOR-swizzled in 16-byte chunks (chunk c of row r sits
@@ -35,9 +37,14 @@ struct AGeo {
   static constexpr int HM = HQ / 32;           // 32-row tiles of them
   static constexpr int WROW = 2 * D;           // bytes per row of W1 / W3 / Q
   static constexpr int GROW = 2 * H;           // bytes per row of G
+  // W1, W3 operands take 2 HM D / 4 registers per lane, W2's H / 4: when
+  // that stays under 128 they live in registers (two wavefronts per SIMD);
+  // otherwise W1 and W3 are staged in LDS (one wavefront per SIMD)
+  static constexpr bool WREG = 2 * HM * D / 4 + H / 4 < 128;
+  static constexpr int WAVES_PER_SIMD = WREG ? 2 : 1;
   static constexpr int OFF_W1 = 0;
-  static constexpr int OFF_W3 = H * WROW;
-  static constexpr int OFF_Q = 2 * H * WROW;
+  static constexpr int OFF_W3 = WREG ? 0 : H * WROW;
+  static constexpr int OFF_Q = WREG ? 0 : 2 * H * WROW;
   static constexpr int OFF_G = OFF_Q + TQ * WROW;
   static constexpr int LDS = OFF_G + TQ * GROW;
 };
@@ -48,7 +55,9 @@ __device__ __forceinline__ int swz(int r, int c, int rowbytes) {
 }
 
 template <int D, int H>
-__global__ __launch_bounds__(kThreads) void k_apply_mfma(ApplyArgs a, int per_wg) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(AGeo<D, H>::WAVES_PER_SIMD, AGeo<D, H>::WAVES_PER_SIMD)))
+void k_apply_mfma(ApplyArgs a, int per_wg) {
   using G = AGeo<D, H>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[G::LDS];
 
@@ -61,8 +70,10 @@ __global__ __launch_bounds__(kThreads) void k_apply_mfma(ApplyArgs a, int per_wg
   const int lane = tid & 63, w = tid >> 6, g = lane >> 5, ln = lane & 31;
   const int64_t hd = static_cast<int64_t>(H) * D;
 
-  // ---- stage W1, W3 (bf16) into LDS
-  {
+  // ---- W1, W3 operands (A side: hidden row w HQ + 32 m + ln, features
+  // 16 ks + 8 g .. +7), in registers or staged in LDS
+  bf16x8_t w1a[G::WREG ? G::HM : 1][G::WREG ? D / 16 : 1], w3a[G::WREG ? G::HM : 1][G::WREG ? D / 16 : 1];
+  if constexpr (!G::WREG) {
     const float* W1 = a.W1 + pair * hd;
     const float* W3 = a.W3 + pair * hd;
     for (int i = tid; i < H * D / 8; i += kThreads) {
@@ -75,6 +86,21 @@ __global__ __launch_bounds__(kThreads) void k_apply_mfma(ApplyArgs a, int per_wg
       }
       *reinterpret_cast<bf16x8_t*>(lds + G::OFF_W1 + swz(r, c, G::WROW)) = v1;
       *reinterpret_cast<bf16x8_t*>(lds + G::OFF_W3 + swz(r, c, G::WROW)) = v3;
+    }
+  } else {
+    const float* W1 = a.W1 + pair * hd;
+    const float* W3 = a.W3 + pair * hd;
+#pragma unroll
+    for (int m = 0; m < G::HM; ++m) {
+      const int64_t hrow = w * G::HQ + 32 * m + ln;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          w1a[m][ks][k] = static_cast<__bf16>(W1[hrow * D + 16 * ks + 8 * g + k]);
+          w3a[m][ks][k] = static_cast<__bf16>(W3[hrow * D + 16 * ks + 8 * g + k]);
+        }
+      }
     }
   }
   // ---- this wave's phase-2 tile: rows dt*32.. of O^T, tokens tt*32..
@@ -139,11 +165,16 @@ __global__ __launch_bounds__(kThreads) void k_apply_mfma(ApplyArgs a, int per_wg
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) {
           const int ch = 2 * ks + g;
-          const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(lds + G::OFF_W1 + swz(hrow, ch, G::WROW));
-          const bf16x8_t a3 = *reinterpret_cast<const bf16x8_t*>(lds + G::OFF_W3 + swz(hrow, ch, G::WROW));
           const bf16x8_t bq = *reinterpret_cast<const bf16x8_t*>(lds + G::OFF_Q + swz(32 * t + ln, ch, G::WROW));
-          c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bq, c1, 0, 0, 0);
-          c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, bq, c3, 0, 0, 0);
+          if constexpr (G::WREG) {
+            c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w1a[m][ks], bq, c1, 0, 0, 0);
+            c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w3a[m][ks], bq, c3, 0, 0, 0);
+          } else {
+            const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(lds + G::OFF_W1 + swz(hrow, ch, G::WROW));
+            const bf16x8_t a3 = *reinterpret_cast<const bf16x8_t*>(lds + G::OFF_W3 + swz(hrow, ch, G::WROW));
+            c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bq, c1, 0, 0, 0);
+            c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3, bq, c3, 0, 0, 0);
+          }
         }
         // c[r] = H^T[hidden w HQ + 32 m + 8 (r/4) + 4 g + r%4][token 32 t + ln]
         const int tok = 32 * t + ln;
