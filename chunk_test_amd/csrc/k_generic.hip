@@ -375,6 +375,106 @@ __global__ __launch_bounds__(kThreads) void k_reduce_step(TailArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// The same tail with 16-byte accesses (W, M 16-byte aligned): each stored row
+// of length L is handled by min(64, L/4) lanes, four floats per lane per
+// chunk, so a wavefront covers 256 floats (several short rows) per access.
+// Rows of W1 and W3 (length d) come first in the grid, then rows of W2
+// (length h).  The row norm is a reduction over the lanes of a row (their
+// count is a power of two).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int off = width >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__global__ __launch_bounds__(kThreads) void k_reduce_step_v4(TailArgs a, int64_t blocks_a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const bool part_a = blockIdx.x < blocks_a;   // rows of W1 / W3, else of W2
+  const int len = part_a ? a.d : a.h;
+  const int lpr = len / 4 < 64 ? len / 4 : 64;  // lanes per row
+  const int rpw = 64 / lpr;                    // rows per wavefront
+  const int cpl = len / 4 / lpr;               // 16-byte chunks per lane
+  const int64_t blk = part_a ? blockIdx.x : blockIdx.x - blocks_a;
+  const int64_t grow = (blk * (kThreads / 64) + wave) * rpw + lane / lpr;  // global row of this part
+  const int64_t rows_per_pair = part_a ? 2 * static_cast<int64_t>(a.h) : a.d;
+  const int64_t pair = grow / rows_per_pair;
+  const bool live = pair < a.P;
+  const int r = static_cast<int>(grow % rows_per_pair);
+  const int64_t hd = static_cast<int64_t>(a.h) * a.d;
+  float* W;
+  float* M;
+  int64_t po;  // offset of the row inside its pair's [W1 | W2 | W3] partial block
+  if (part_a) {
+    const bool w3 = r >= a.h;
+    W = w3 ? a.W3 : a.W1;
+    M = w3 ? a.M3 : a.M1;
+    po = (w3 ? 2 * hd : 0) + static_cast<int64_t>(w3 ? r - a.h : r) * a.d;
+  } else {
+    W = a.W2;
+    M = a.M2;
+    po = hd + static_cast<int64_t>(r) * a.h;
+  }
+  const int64_t wo = pair * hd + (po % hd);
+  const float4* part = reinterpret_cast<const float4*>(a.partials + pair * a.splits * 3 * hd + po);
+  const int64_t sstride = 3 * hd / 4;
+  const int c0 = lane % lpr;
+  float4 v[4];
+  float ss = 0.f;
+  for (int k = 0; k < cpl; ++k) {
+    const int c = c0 + lpr * k;
+    float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (live) {
+      int sp = 0;
+      for (; sp + 4 <= a.splits; sp += 4) {  // four loads in flight, summed in split order
+        float4 t[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) t[u] = part[(sp + u) * sstride + c];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          g.x += t[u].x;
+          g.y += t[u].y;
+          g.z += t[u].z;
+          g.w += t[u].w;
+        }
+      }
+      for (; sp < a.splits; ++sp) {
+        const float4 t = part[sp * sstride + c];
+        g.x += t.x;
+        g.y += t.y;
+        g.z += t.z;
+        g.w += t.w;
+      }
+      if (M != nullptr) {
+        float4* mp = reinterpret_cast<float4*>(M + wo) + c;
+        const float4 m = *mp;
+        g.x = a.beta * m.x + g.x;
+        g.y = a.beta * m.y + g.y;
+        g.z = a.beta * m.z + g.z;
+        g.w = a.beta * m.w + g.w;
+        *mp = g;
+      }
+      const float4 w = reinterpret_cast<const float4*>(W + wo)[c];
+      g.x = w.x - a.step * g.x;
+      g.y = w.y - a.step * g.y;
+      g.z = w.z - a.step * g.z;
+      g.w = w.w - a.step * g.w;
+      ss += g.x * g.x + g.y * g.y + g.z * g.z + g.w * g.w;
+    }
+    if (k < 4) v[k] = g;
+  }
+  ss = group_sum(ss, lpr);
+  const float den = fmaxf(sqrtf(ss), a.norm_eps);
+  if (live) {
+    for (int k = 0; k < cpl; ++k) {
+      const int c = c0 + lpr * k;
+      const float4 g = v[k];
+      reinterpret_cast<float4*>(W + wo)[c] = make_float4(g.x / den, g.y / den, g.z / den, g.w / den);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Query read O = W2 (silu(W1 q) * (W3 q)).  Grid (ceil(m/32), P); hidden
 // units in slices of 256 staged through LDS.
 // ---------------------------------------------------------------------------
@@ -501,6 +601,22 @@ hipError_t launch_ns_simple(const NSArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_reduce_step(const TailArgs& a, hipStream_t s) {
+  const bool aligned = ((reinterpret_cast<uintptr_t>(a.W1) | reinterpret_cast<uintptr_t>(a.W2) |
+                         reinterpret_cast<uintptr_t>(a.W3) | reinterpret_cast<uintptr_t>(a.M1) |
+                         reinterpret_cast<uintptr_t>(a.M2) | reinterpret_cast<uintptr_t>(a.M3)) & 15) == 0;
+  // lanes per row must be a power of two (rows of d: always; rows of h:
+  // h / 4 a power of two, or h a multiple of 256 up to 1024)
+  auto pow2 = [](int x) { return x > 0 && (x & (x - 1)) == 0; };
+  const bool shape_ok = (pow2(a.h / 4) || a.h % 256 == 0) && a.h <= 1024;
+  if (aligned && shape_ok) {
+    // rows per block: 4 wavefronts x (64 / lanes per row)
+    auto rows_per_block = [](int len) { return 4 * (64 / (len / 4 < 64 ? len / 4 : 64)); };
+    const int64_t rows_a = static_cast<int64_t>(a.P) * 2 * a.h, rows_b = static_cast<int64_t>(a.P) * a.d;
+    const int64_t ba = (rows_a + rows_per_block(a.d) - 1) / rows_per_block(a.d);
+    const int64_t bb = (rows_b + rows_per_block(a.h) - 1) / rows_per_block(a.h);
+    hipLaunchKernelGGL(k_reduce_step_v4, dim3(static_cast<unsigned>(ba + bb)), dim3(kThreads), 0, s, a, ba);
+    return hipGetLastError();
+  }
   const int64_t rows = static_cast<int64_t>(a.P) * (2 * a.h + a.d);
   const unsigned blocks = static_cast<unsigned>((rows + 3) / 4);
   hipLaunchKernelGGL(k_reduce_step, dim3(blocks), dim3(kThreads), 0, s, a);
