@@ -75,8 +75,8 @@ typedef enum { LACT_APPLY_THEN_UPDATE = 0, LACT_UPDATE_THEN_APPLY = 1 } lact_ord
 typedef enum { LACT_OPT_GD = 0, LACT_OPT_MOMENTUM = 1, LACT_OPT_MUON = 2 } lact_opt;
 
 /* bf16 I/O mode only.  LACT_PRODUCTS_BF16: every product operand is rounded
- * to bf16 (the inputs already are; W, u = -eta v, and the SwiGLU values are
- * rounded), fp32 accumulation.  LACT_PRODUCTS_SPLIT: only the inputs Q, K,
+ * to bf16 (the inputs already are; the W copies and the SwiGLU values, which
+ * carry the -eta factor, are rounded), fp32 accumulation.  LACT_PRODUCTS_SPLIT: only the inputs Q, K,
  * V are bf16; every derived operand keeps ~16 significant bits (computed in
  * fp32, or as a hi + lo pair of bf16 values on the matrix cores).  Muon over
  * many chunks amplifies operand rounding from chunk to chunk, which the
@@ -157,11 +157,12 @@ int lact_mfma_path(int32_t d, int32_t h, int32_t io_dtype);
  * While enabled, every entry point records HIP events on its stream around
  * each phase; lact_profile_read() waits for the recorded events, adds their
  * durations into ms[phase] / launches[phase] (arrays of LACT_PROFILE_PHASES)
- * and clears the record.  Phases: 0 chunk gradient; 1 update tail (split
- * reduction and momentum, fused with the step and row normalisation, and
- * for bf16-mode Muon with Newton-Schulz too); 2 Newton-Schulz and 3 step +
- * row normalisation when they run as kernels of their own (fp32-arithmetic
- * Muon); 4 query read. */
+ * and clears the record.  Phases: 0 chunk gradient; 1 update tail (the
+ * fixed-order sum of the token splits and the momentum update, with the
+ * step and row normalisation, and for bf16-mode Muon with Newton-Schulz
+ * too: one or two kernels); 2 Newton-Schulz and 3 step + row normalisation
+ * when they run as kernels of their own (fp32-arithmetic Muon); 4 query
+ * read. */
 #define LACT_PROFILE_PHASES 5
 int lact_profile_enable(int on);
 int lact_profile_read(double* ms, int64_t* launches);
