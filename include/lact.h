@@ -76,11 +76,12 @@ typedef enum { LACT_OPT_GD = 0, LACT_OPT_MOMENTUM = 1, LACT_OPT_MUON = 2 } lact_
 
 /* bf16 I/O mode only.  LACT_PRODUCTS_BF16: every product operand is rounded
  * to bf16 (the inputs already are; the W copies and the SwiGLU values, which
- * carry the -eta factor, are rounded), fp32 accumulation.  LACT_PRODUCTS_SPLIT: only the inputs Q, K,
- * V are bf16; every derived operand keeps ~16 significant bits (computed in
- * fp32, or as a hi + lo pair of bf16 values on the matrix cores).  Muon over
- * many chunks amplifies operand rounding from chunk to chunk, which the
- * split mode avoids at a higher cost.  Ignored in fp32 I/O mode. */
+ * carry the -eta factor, are rounded), fp32 accumulation.
+ * LACT_PRODUCTS_SPLIT: only the inputs Q, K, V are bf16; every derived
+ * operand keeps ~16 significant bits (computed in fp32, or as a hi + lo pair
+ * of bf16 values on the matrix cores).  Muon over many chunks amplifies
+ * operand rounding from chunk to chunk, which the split mode avoids at a
+ * higher cost.  Ignored in fp32 I/O mode. */
 typedef enum { LACT_PRODUCTS_BF16 = 0, LACT_PRODUCTS_SPLIT = 1 } lact_products;
 
 typedef struct {
