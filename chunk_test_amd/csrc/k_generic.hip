@@ -382,11 +382,6 @@ __global__ __launch_bounds__(kThreads) void k_reduce_step(TailArgs a) {
 // (length h).  The row norm is a reduction over the lanes of a row (their
 // count is a power of two).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float group_sum(float v, int width) {
-  for (int off = width >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-
 __global__ __launch_bounds__(kThreads) void k_reduce_step_v4(TailArgs a, int64_t blocks_a) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;

@@ -119,6 +119,21 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
       acc[k].w += t.w;
     }
   }
+  if (Mm != nullptr) {
+    // M <- beta M + G, G <- M (all loads issued before the first store)
+    float4* M4 = reinterpret_cast<float4*>(Mm);
+    float4 mv[CPT];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) mv[k] = M4[tid + 2 * L * k];
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      acc[k].x = a.beta * mv[k].x + acc[k].x;
+      acc[k].y = a.beta * mv[k].y + acc[k].y;
+      acc[k].z = a.beta * mv[k].z + acc[k].z;
+      acc[k].w = a.beta * mv[k].w + acc[k].w;
+      M4[tid + 2 * L * k] = acc[k];
+    }
+  }
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
@@ -127,11 +142,7 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = 4 * c + q;
-      float v = g4[q];
-      if (Mm != nullptr) {
-        v = a.beta * Mm[e] + v;
-        Mm[e] = v;
-      }
+      const float v = g4[q];
       ss += v * v;
       const int i = tr ? (e % S) : (e / L);  // row of X
       const int j = tr ? (e / S) : (e % L);  // column of X
@@ -350,7 +361,19 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
     }
   }
 
-  // ---- the result X into LDS (fp32) for the row-wise step
+  // ---- W <- W - step X, then unit L2 rows.  Every thread takes GPT float4
+  // groups of the stored matrix (rows of `rowlen`, rowlen / 4 lanes per row,
+  // so a row's lanes are an aligned lane group); all W loads are issued here,
+  // before X goes to LDS, so their latency is paid once.  W1, W3 rows are
+  // columns of X, W2 rows are rows of X.
+  constexpr int GPT = NV / (2 * L);
+  const int rowlen = tr ? S : L;
+  const int lpr = rowlen / 4;
+  float4* W4 = reinterpret_cast<float4*>(Wm);
+  float4 wv[GPT];
+#pragma unroll
+  for (int k = 0; k < GPT; ++k) wv[k] = W4[tid + 2 * L * k];
+
   __syncthreads();
 #pragma unroll
   for (int ct = 0; ct < G::CT; ++ct) {
@@ -364,30 +387,21 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
     }
   }
   __syncthreads();
-  // ---- W <- W - step X, then unit L2 rows; one wavefront per stored row
-  // (W1, W3 rows are columns of X, W2 rows are rows of X)
-  const int nrows = tr ? L : S;
-  const int rowlen = tr ? S : L;
-  for (int r = w; r < nrows; r += G::NW) {
-    float v[L / 64];
+#pragma unroll
+  for (int k = 0; k < GPT; ++k) {
+    const int e = 4 * (tid + 2 * L * k);
+    const int row = e / rowlen, col = e % rowlen;
+    float v[4] = {wv[k].x, wv[k].y, wv[k].z, wv[k].w};
     float sq = 0.f;
 #pragma unroll
-    for (int k = 0; k < L / 64; ++k) {
-      const int cidx = lane + 64 * k;
-      v[k] = 0.f;
-      if (cidx < rowlen) {
-        const int i = tr ? cidx : r, j = tr ? r : cidx;
-        v[k] = Wm[static_cast<int64_t>(r) * rowlen + cidx] - a.step * *reinterpret_cast<const float*>(lds + i * XFS + 4 * j);
-        sq += v[k] * v[k];
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int i = tr ? col + q : row, j = tr ? row : col + q;  // element of X
+      v[q] -= a.step * *reinterpret_cast<const float*>(lds + i * XFS + 4 * j);
+      sq += v[q] * v[q];
     }
-    sq = wave_sum(sq);
+    sq = group_sum(sq, lpr);
     const float den = fmaxf(sqrtf(sq), a.norm_eps);
-#pragma unroll
-    for (int k = 0; k < L / 64; ++k) {
-      const int cidx = lane + 64 * k;
-      if (cidx < rowlen) Wm[static_cast<int64_t>(r) * rowlen + cidx] = v[k] / den;
-    }
+    W4[tid + 2 * L * k] = make_float4(v[0] / den, v[1] / den, v[2] / den, v[3] / den);
   }
 }
 

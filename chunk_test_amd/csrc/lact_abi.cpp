@@ -317,7 +317,12 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
     if (e != hipSuccess) return hip_fail(e, "update-tail kernel");
     return LACT_OK;
   }
-  if (p.bf16 && lact::ns_mfma_shape_ok(p.d, p.h)) {
+  // (the MFMA tail moves W and M in 16-byte pieces)
+  const bool state_aligned =
+      ((reinterpret_cast<uintptr_t>(st->W1) | reinterpret_cast<uintptr_t>(st->W2) |
+        reinterpret_cast<uintptr_t>(st->W3) | reinterpret_cast<uintptr_t>(st->M1) |
+        reinterpret_cast<uintptr_t>(st->M2) | reinterpret_cast<uintptr_t>(st->M3)) & 15) == 0;
+  if (p.bf16 && lact::ns_mfma_shape_ok(p.d, p.h) && state_aligned) {
     // bf16 mode Muon: one kernel per matrix for reduction, momentum,
     // split-bf16 MFMA Newton-Schulz, step and unit rows.  With many splits
     // the partial sum goes first to a kernel that spreads it over every CU

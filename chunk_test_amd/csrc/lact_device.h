@@ -49,4 +49,10 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// sum over aligned groups of `width` lanes (a power of two <= 64)
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int off = width >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
 }  // namespace lact
