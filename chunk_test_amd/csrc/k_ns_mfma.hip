@@ -30,6 +30,8 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 
 __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -38,6 +40,55 @@ __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
 __device__ __forceinline__ void split(float x, __bf16& hi, __bf16& lo) {
   hi = static_cast<__bf16>(x);
   lo = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+
+// the same split for two values, as packed bf16 pairs (element 0 in the low half)
+__device__ __forceinline__ void split2(float x0, float x1, unsigned& hi, unsigned& lo) {
+  bf16x2_t h, l;
+  h[0] = static_cast<__bf16>(x0);
+  h[1] = static_cast<__bf16>(x1);
+  l[0] = static_cast<__bf16>(x0 - static_cast<float>(h[0]));
+  l[1] = static_cast<__bf16>(x1 - static_cast<float>(h[1]));
+  hi = __builtin_bit_cast(unsigned, h);
+  lo = __builtin_bit_cast(unsigned, l);
+}
+
+// element k (0 or 1) of a packed bf16 pair, as a float
+__device__ __forceinline__ float bf16_half(unsigned w, int k) {
+  return __uint_as_float(k ? (w & 0xffff0000u) : (w << 16));
+}
+
+// Split-operand products of NQ 32 x 32 tiles, all over the same KSTEPS
+// k-steps: for tile q, hh[q] += P_hi Q_hi^T and cross[q] += P_hi Q_lo^T +
+// P_lo Q_hi^T, with P rows at pa[q] and Q rows at pb[q] (row-major bf16 in
+// LDS, 16-byte operand slices at +32 ks; the lo block `half` bytes after the
+// hi block).  The k loop is unrolled and the tiles interleaved inside it, so
+// the reads of one k-step overlap the products of the previous ones.
+template <int NQ, int KSTEPS>
+__device__ __forceinline__ void split_tiles(const unsigned char* const (&pa)[NQ],
+                                            const unsigned char* const (&pb)[NQ], int half,
+                                            f32x16_t (&hh)[NQ], f32x16_t (&cross)[NQ]) {
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      hh[q][r] = 0.f;
+      cross[q][r] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(pa[q] + 32 * ks);
+      const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(pa[q] + half + 32 * ks);
+      const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(pb[q] + 32 * ks);
+      const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(pb[q] + half + 32 * ks);
+      hh[q] = mfma(ah, bh, hh[q]);
+      cross[q] = mfma(ah, bl, cross[q]);
+      cross[q] = mfma(al, bh, cross[q]);
+    }
+  }
 }
 
 template <int S, int L>
@@ -174,7 +225,24 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
   unsigned char* alo = lds + G::A_HALF;
 
   for (int it = 0; it < a.iters; ++it) {
-    // ---- X row-major (hi, lo) into LDS
+    // ---- X split once into hi / lo bf16 operands, kept in registers as
+    // packed pairs in the B-operand order of B X (k-step s, slot i <->
+    // x[ct][s / 2][8 (s % 2) + i]), and written row-major into LDS for X X^T
+    u32x4_t xh[G::CT][S / 16], xl[G::CT][S / 16];
+#pragma unroll
+    for (int ct = 0; ct < G::CT; ++ct) {
+#pragma unroll
+      for (int ks = 0; ks < S / 16; ++ks) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 8 * (ks & 1) + 2 * j;
+          unsigned wh, wl;
+          split2(x[ct][ks >> 1][r], x[ct][ks >> 1][r + 1], wh, wl);
+          xh[ct][ks][j] = wh;
+          xl[ct][ks][j] = wl;
+        }
+      }
+    }
     __syncthreads();
 #pragma unroll
     for (int ct = 0; ct < G::CT; ++ct) {
@@ -184,46 +252,50 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
         unsigned char* xb = xhi + (32 * mt + 4 * g) * G::XRS + 2 * colof(ct);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          __bf16 hi, lo;
-          split(x[ct][mt][r], hi, lo);
           const int ro = (8 * (r >> 2) + (r & 3)) * G::XRS;
-          *reinterpret_cast<__bf16*>(xb + ro) = hi;
-          *reinterpret_cast<__bf16*>(xb + G::X_HALF + ro) = lo;
+          const int ks = 2 * mt + (r >> 3), j = (r & 7) >> 1, k = r & 1;
+          const unsigned wh = xh[ct][ks][j], wl = xl[ct][ks][j];
+          *reinterpret_cast<uint16_t*>(xb + ro) = static_cast<uint16_t>(k ? (wh >> 16) : wh);
+          *reinterpret_cast<uint16_t*>(xb + G::X_HALF + ro) = static_cast<uint16_t>(k ? (wl >> 16) : wl);
         }
-        // keep the scheduler from computing every split value up front
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __syncthreads();
 
-    // ---- A = X X^T: this wave's tiles (ti, tj); K = l
+    // ---- A = X X^T: this wave's tiles (ti, tj) = (t / MT, t % MT),
+    // t = w + NW q; K = l
     f32x16_t at[G::ATW];
+    if constexpr (G::ATILES % G::NW == 0) {
+      const unsigned char* pa[G::ATW];
+      const unsigned char* pb[G::ATW];
 #pragma unroll
-    for (int q = 0; q < G::ATW; ++q) {
-      const int t = w + G::NW * q;
-      f32x16_t a2;  // second accumulator chain (cross terms)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        at[q][r] = 0.f;
-        a2[r] = 0.f;
+      for (int q = 0; q < G::ATW; ++q) {
+        const int t = w + G::NW * q;
+        pa[q] = xhi + (32 * (t / G::MT) + ln) * G::XRS + 16 * g;
+        pb[q] = xhi + (32 * (t % G::MT) + ln) * G::XRS + 16 * g;
       }
-      if (t < G::ATILES) {
-        const int ti = t / G::MT, tj = t % G::MT;
-        const unsigned char* ra = xhi + (32 * ti + ln) * G::XRS + 16 * g;
-        const unsigned char* rb = xhi + (32 * tj + ln) * G::XRS + 16 * g;
-#pragma unroll 2
-        for (int ks = 0; ks < L / 16; ++ks) {
-          const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(ra + 32 * ks);
-          const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(ra + G::X_HALF + 32 * ks);
-          const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(rb + 32 * ks);
-          const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(rb + G::X_HALF + 32 * ks);
-          at[q] = mfma(ah, bh, at[q]);
-          a2 = mfma(ah, bl, a2);
-          a2 = mfma(al, bh, a2);
+      f32x16_t a2[G::ATW];
+      split_tiles<G::ATW, L / 16>(pa, pb, G::X_HALF, at, a2);
+#pragma unroll
+      for (int q = 0; q < G::ATW; ++q) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) at[q][r] += a2[q][r];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < G::ATW; ++q) {
+        const int t = w + G::NW * q;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) at[q][r] = 0.f;
+        if (t < G::ATILES) {
+          const unsigned char* pa[1] = {xhi + (32 * (t / G::MT) + ln) * G::XRS + 16 * g};
+          const unsigned char* pb[1] = {xhi + (32 * (t % G::MT) + ln) * G::XRS + 16 * g};
+          f32x16_t hh[1], a2[1];
+          split_tiles<1, L / 16>(pa, pb, G::X_HALF, hh, a2);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) at[q][r] = hh[0][r] + a2[0][r];
         }
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) at[q][r] += a2[r];
     }
     __syncthreads();  // X row-major no longer needed: the region becomes A
 
@@ -253,32 +325,35 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
     __syncthreads();
 
     // ---- B = b A + c A A on the same tiles (A symmetric: both operands are rows of A)
+    if constexpr (G::ATILES % G::NW == 0) {
+      const unsigned char* pa[G::ATW];
+      const unsigned char* pb[G::ATW];
 #pragma unroll
-    for (int q = 0; q < G::ATW; ++q) {
-      const int t = w + G::NW * q;
-      f32x16_t acc, a2;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        acc[r] = 0.f;
-        a2[r] = 0.f;
+      for (int q = 0; q < G::ATW; ++q) {
+        const int t = w + G::NW * q;
+        pa[q] = ahi + (32 * (t / G::MT) + ln) * G::ARS + 16 * g;
+        pb[q] = ahi + (32 * (t % G::MT) + ln) * G::ARS + 16 * g;
       }
-      if (t < G::ATILES) {
-        const int ti = t / G::MT, tj = t % G::MT;
-        const unsigned char* ra = ahi + (32 * ti + ln) * G::ARS + 16 * g;
-        const unsigned char* rb = ahi + (32 * tj + ln) * G::ARS + 16 * g;
-#pragma unroll 2
-        for (int ks = 0; ks < S / 16; ++ks) {
-          const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(ra + 32 * ks);
-          const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(ra + G::A_HALF + 32 * ks);
-          const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(rb + 32 * ks);
-          const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(rb + G::A_HALF + 32 * ks);
-          acc = mfma(ah, bh, acc);
-          a2 = mfma(ah, bl, a2);
-          a2 = mfma(al, bh, a2);
+      f32x16_t acc[G::ATW], a2[G::ATW];
+      split_tiles<G::ATW, S / 16>(pa, pb, G::A_HALF, acc, a2);
+#pragma unroll
+      for (int q = 0; q < G::ATW; ++q) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) at[q][r] = a.b * at[q][r] + a.c * (acc[q][r] + a2[q][r]);  // now B
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < G::ATW; ++q) {
+        const int t = w + G::NW * q;
+        if (t < G::ATILES) {
+          const unsigned char* pa[1] = {ahi + (32 * (t / G::MT) + ln) * G::ARS + 16 * g};
+          const unsigned char* pb[1] = {ahi + (32 * (t % G::MT) + ln) * G::ARS + 16 * g};
+          f32x16_t acc[1], a2[1];
+          split_tiles<1, S / 16>(pa, pb, G::A_HALF, acc, a2);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) at[q][r] = a.b * at[q][r] + a.c * (acc[0][r] + a2[0][r]);  // now B
         }
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) at[q][r] = a.b * at[q][r] + a.c * (acc[r] + a2[r]);  // now B
     }
     __syncthreads();  // all reads of A done: the region becomes B
     // B is symmetric too: same store
@@ -309,34 +384,23 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
     // 16 rows per k-step) comes from this lane's own registers; the A
     // operand (rows of B) uses the matching row order:
     // slot 8g + i of k-step s <-> row 16 s + 8 (i/4) + 4 g + i%4.
-    // (one output tile at a time keeps few registers live; the split of X
-    // into hi/lo operands is redone per tile, which is cheap VALU work)
 #pragma unroll
     for (int ct = 0; ct < G::CT; ++ct) {
       f32x16_t accs[G::MT];
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt) {
-        f32x16_t acc, a2;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          acc[r] = 0.f;
-          a2[r] = 0.f;
-        }
-        const unsigned char* rb = ahi + (32 * mt + ln) * G::ARS + 8 * g;
+        for (int r = 0; r < 16; ++r) accs[mt][r] = 0.f;
+      }
 #pragma unroll
-        for (int s = 0; s < S / 16; ++s) {
-          bf16x8_t xh, xl;
+      for (int s = 0; s < S / 16; ++s) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            __bf16 hi, lo;
-            split(x[ct][s >> 1][8 * (s & 1) + i], hi, lo);
-            xh[i] = hi;
-            xl[i] = lo;
-          }
-          const bf16x4_t h0 = *reinterpret_cast<const bf16x4_t*>(rb + 32 * s);
-          const bf16x4_t h1 = *reinterpret_cast<const bf16x4_t*>(rb + 32 * s + 16);
-          const bf16x4_t l0 = *reinterpret_cast<const bf16x4_t*>(rb + G::A_HALF + 32 * s);
-          const bf16x4_t l1 = *reinterpret_cast<const bf16x4_t*>(rb + G::A_HALF + 32 * s + 16);
+        for (int mt = 0; mt < G::MT; ++mt) {
+          const unsigned char* rb = ahi + (32 * mt + ln) * G::ARS + 8 * g + 32 * s;
+          const bf16x4_t h0 = *reinterpret_cast<const bf16x4_t*>(rb);
+          const bf16x4_t h1 = *reinterpret_cast<const bf16x4_t*>(rb + 16);
+          const bf16x4_t l0 = *reinterpret_cast<const bf16x4_t*>(rb + G::A_HALF);
+          const bf16x4_t l1 = *reinterpret_cast<const bf16x4_t*>(rb + G::A_HALF + 16);
           bf16x8_t bh, bl;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -345,18 +409,24 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
             bl[i] = l0[i];
             bl[4 + i] = l1[i];
           }
-          acc = mfma(bh, xh, acc);
-          a2 = mfma(bh, xl, a2);
-          a2 = mfma(bl, xh, a2);
+          const bf16x8_t oh = __builtin_bit_cast(bf16x8_t, xh[ct][s]);
+          const bf16x8_t ol = __builtin_bit_cast(bf16x8_t, xl[ct][s]);
+          accs[mt] = mfma(bh, oh, accs[mt]);
+          accs[mt] = mfma(bh, ol, accs[mt]);
+          accs[mt] = mfma(bl, oh, accs[mt]);
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) accs[mt][r] = acc[r] + a2[r];
       }
-      // this column tile is not read again in this iteration: update in place
+      // X <- a X + B X, with X taken as hi + lo (the fp32 X is not kept
+      // across the iteration; hi + lo carries ~16 significant bits, the
+      // precision of every product here)
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[ct][mt][r] = a.a * x[ct][mt][r] + accs[mt][r];
+        for (int r = 0; r < 16; ++r) {
+          const int ks = 2 * mt + (r >> 3), j = (r & 7) >> 1, k = r & 1;
+          const float xv = bf16_half(xh[ct][ks][j], k) + bf16_half(xl[ct][ks][j], k);
+          x[ct][mt][r] = a.a * xv + accs[mt][r];
+        }
       }
     }
   }

@@ -420,6 +420,8 @@ int run_apply(const Plan& p, const lact_state* st, const void* Q, void* O, int64
   a.d = p.d;
   a.h = p.h;
   a.bf16 = p.bf16;
+  a.w_vec = ((reinterpret_cast<uintptr_t>(st->W1) | reinterpret_cast<uintptr_t>(st->W2) |
+              reinterpret_cast<uintptr_t>(st->W3)) & 15) == 0;
   const bool use_mfma = p.bf16 && lact::apply_mfma_shape_ok(p.d, p.h) &&
                         reinterpret_cast<uintptr_t>(Q) % 16 == 0 &&
                         reinterpret_cast<uintptr_t>(O) % 16 == 0 && q_stride % 8 == 0;

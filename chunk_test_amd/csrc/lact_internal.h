@@ -75,6 +75,7 @@ struct ApplyArgs {
   const float *W1, *W2, *W3;
   int P, d, h;
   int bf16;
+  int w_vec;  // W1, W2, W3 16-byte aligned
 };
 
 // ---- generic kernels (fp32 arithmetic; any supported d, h) ----

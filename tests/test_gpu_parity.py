@@ -45,8 +45,9 @@ SMALL_CASES = [
     # operands shows the same.)
     small("posed", name="posed-tiny-chunks", H=3, T_kv=1000, T_q=70, chunk_kv=100, chunk_q=7,
           opt="momentum", beta=0.9),
-    # bf16, two 128-unit hidden slices at d = 64
-    small("posed", name="posed-h256", H=2, h=256, T_kv=5000, T_q=64, chunk_kv=5000, chunk_q=64),
+    # bf16, two 128-unit hidden slices at d = 64; 1000 queries (two query-read
+    # workgroups of several pipelined 128-query steps, the last one ragged)
+    small("posed", name="posed-h256", H=2, h=256, T_kv=5000, T_q=1000, chunk_kv=5000, chunk_q=1000),
     # bf16 Muon with momentum at d = 64 (the Muon tail's momentum buffer)
     small("posed", name="posed-muon-momentum", H=2, T_kv=9000, T_q=256, chunk_kv=9000, chunk_q=256,
           beta=0.5),
