@@ -65,6 +65,13 @@ __device__ __forceinline__ bf16x8_t load8_bf16(const float* p, bool vec) {
   return v;
 }
 
+// operand of eight consecutive weights at element offset `off`: one 16-byte
+// load from the bf16 copy when there is one, else converted from fp32
+__device__ __forceinline__ bf16x8_t weight_op(const uint16_t* wb, const float* wf, int64_t off, bool vec) {
+  if (wb != nullptr) return *reinterpret_cast<const bf16x8_t*>(wb + off);
+  return load8_bf16(wf + off, vec);
+}
+
 // byte offset of 16-byte chunk `c` of row `r` (rows of `rowbytes`), swizzled
 __device__ __forceinline__ int swz(int r, int c, int rowbytes) {
   return r * rowbytes + ((c ^ (r & 7)) << 4);
@@ -97,12 +104,11 @@ void k_apply_mfma(ApplyArgs a, int per_wg, int wg_per_pair) {
   constexpr int KS1 = D / 16;
   bf16x8_t w1a[KS1], w3a[KS1];
   {
-    const float* W1 = a.W1 + pair * hd + static_cast<int64_t>(32 * w + ln) * D;
-    const float* W3 = a.W3 + pair * hd + static_cast<int64_t>(32 * w + ln) * D;
+    const int64_t row = pair * hd + static_cast<int64_t>(32 * w + ln) * D;
 #pragma unroll
     for (int ks = 0; ks < KS1; ++ks) {
-      w1a[ks] = load8_bf16(W1 + 16 * ks + 8 * g, a.w_vec);
-      w3a[ks] = load8_bf16(W3 + 16 * ks + 8 * g, a.w_vec);
+      w1a[ks] = weight_op(a.Wb1, a.W1, row + 16 * ks + 8 * g, a.w_vec);
+      w3a[ks] = weight_op(a.Wb3, a.W3, row + 16 * ks + 8 * g, a.w_vec);
     }
   }
   // ---- this wave's phase-2 tile: rows 32 dt .. of O^T, tokens 32 tt ..
@@ -111,9 +117,9 @@ void k_apply_mfma(ApplyArgs a, int per_wg, int wg_per_pair) {
   constexpr int KS2 = H / 16;
   bf16x8_t w2b[KS2];
   {
-    const float* W2 = a.W2 + pair * hd + static_cast<int64_t>(32 * dt + ln) * H;
+    const int64_t row = pair * hd + static_cast<int64_t>(32 * dt + ln) * H;
 #pragma unroll
-    for (int ks = 0; ks < KS2; ++ks) w2b[ks] = load8_bf16(W2 + 16 * ks + 8 * g, a.w_vec);
+    for (int ks = 0; ks < KS2; ++ks) w2b[ks] = weight_op(a.Wb2, a.W2, row + 16 * ks + 8 * g, a.w_vec);
   }
 
   const uint16_t* Qg = static_cast<const uint16_t*>(a.Q) + static_cast<int64_t>(pair) * a.q_stride;

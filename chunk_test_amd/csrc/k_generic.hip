@@ -12,6 +12,8 @@
 namespace lact {
 namespace {
 
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+
 constexpr int kThreads = 256;
 constexpr int kTok = 32;  // tokens per LDS tile
 constexpr int kHS = 32;   // hidden units per workgroup
@@ -320,21 +322,25 @@ __global__ __launch_bounds__(kThreads) void k_reduce_step(TailArgs a) {
   const int64_t hd = static_cast<int64_t>(a.h) * a.d;
   float* W;
   float* M;
+  uint16_t* Wb;
   int64_t po;
   int len;
   if (r < a.h) {
     W = a.W1;
     M = a.M1;
+    Wb = a.Wb1;
     po = static_cast<int64_t>(r) * a.d;
     len = a.d;
   } else if (r < 2 * a.h) {
     W = a.W3;
     M = a.M3;
+    Wb = a.Wb3;
     po = 2 * hd + static_cast<int64_t>(r - a.h) * a.d;
     len = a.d;
   } else {
     W = a.W2;
     M = a.M2;
+    Wb = a.Wb2;
     po = hd + static_cast<int64_t>(r - 2 * a.h) * a.h;
     len = a.h;
   }
@@ -370,7 +376,11 @@ __global__ __launch_bounds__(kThreads) void k_reduce_step(TailArgs a) {
 #pragma unroll
   for (int k = 0; k < kMaxRowPerLane; ++k) {
     const int e = lane + 64 * k;
-    if (e < len) W[wo + e] = v[k] / den;
+    if (e < len) {
+      const float x = v[k] / den;
+      W[wo + e] = x;
+      if (Wb != nullptr) Wb[wo + e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+    }
   }
 }
 
@@ -399,15 +409,18 @@ __global__ __launch_bounds__(kThreads) void k_reduce_step_v4(TailArgs a, int64_t
   const int64_t hd = static_cast<int64_t>(a.h) * a.d;
   float* W;
   float* M;
+  uint16_t* Wb;
   int64_t po;  // offset of the row inside its pair's [W1 | W2 | W3] partial block
   if (part_a) {
     const bool w3 = r >= a.h;
     W = w3 ? a.W3 : a.W1;
     M = w3 ? a.M3 : a.M1;
+    Wb = w3 ? a.Wb3 : a.Wb1;
     po = (w3 ? 2 * hd : 0) + static_cast<int64_t>(w3 ? r - a.h : r) * a.d;
   } else {
     W = a.W2;
     M = a.M2;
+    Wb = a.Wb2;
     po = hd + static_cast<int64_t>(r) * a.h;
   }
   const int64_t wo = pair * hd + (po % hd);
@@ -464,7 +477,16 @@ __global__ __launch_bounds__(kThreads) void k_reduce_step_v4(TailArgs a, int64_t
     for (int k = 0; k < cpl; ++k) {
       const int c = c0 + lpr * k;
       const float4 g = v[k];
-      reinterpret_cast<float4*>(W + wo)[c] = make_float4(g.x / den, g.y / den, g.z / den, g.w / den);
+      const float4 x = make_float4(g.x / den, g.y / den, g.z / den, g.w / den);
+      reinterpret_cast<float4*>(W + wo)[c] = x;
+      if (Wb != nullptr) {
+        bf16x4_t b;
+        b[0] = static_cast<__bf16>(x.x);
+        b[1] = static_cast<__bf16>(x.y);
+        b[2] = static_cast<__bf16>(x.z);
+        b[3] = static_cast<__bf16>(x.w);
+        reinterpret_cast<bf16x4_t*>(Wb + wo)[c] = b;
+      }
     }
   }
 }

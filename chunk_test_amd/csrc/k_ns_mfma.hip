@@ -118,6 +118,7 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
   const bool tr = ((which == 1) ? a.d : a.h) > cols;  // X = G^T when G is tall
   float* Wm = (which == 0 ? a.W1 : which == 1 ? a.W2 : a.W3) + pair * hd;
   float* Mm = (a.M1 == nullptr) ? nullptr : (which == 0 ? a.M1 : which == 1 ? a.M2 : a.M3) + pair * hd;
+  uint16_t* Wbm = (a.Wb1 == nullptr) ? nullptr : (which == 0 ? a.Wb1 : which == 1 ? a.Wb2 : a.Wb3) + pair * hd;
   const float* part = a.partials + static_cast<int64_t>(pair) * a.splits * 3 * hd + which * hd;
 
   const int tid = threadIdx.x;
@@ -471,7 +472,16 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
     }
     sq = group_sum(sq, lpr);
     const float den = fmaxf(sqrtf(sq), a.norm_eps);
-    W4[tid + 2 * L * k] = make_float4(v[0] / den, v[1] / den, v[2] / den, v[3] / den);
+    const float4 xw = make_float4(v[0] / den, v[1] / den, v[2] / den, v[3] / den);
+    W4[tid + 2 * L * k] = xw;
+    if (Wbm != nullptr) {
+      bf16x4_t b4;
+      b4[0] = static_cast<__bf16>(xw.x);
+      b4[1] = static_cast<__bf16>(xw.y);
+      b4[2] = static_cast<__bf16>(xw.z);
+      b4[3] = static_cast<__bf16>(xw.w);
+      reinterpret_cast<bf16x4_t*>(Wbm)[tid + 2 * L * k] = b4;
+    }
   }
 }
 

@@ -213,7 +213,8 @@ int check_state(const Plan& p, const lact_state* st, bool need_m) {
 
 // Workspace sections (bytes), each 256-byte aligned.
 struct WsLayout {
-  size_t partials = 0, dir = 0, ns = 0, total = 0;
+  size_t partials = 0, dir = 0, ns = 0, wb = 0, total = 0;
+  bool has_wb = false;  // section for bf16 copies of W1, W2, W3 (P 3 h d values)
 };
 
 WsLayout ws_layout(const Plan& p, int64_t max_chunk_kv) {
@@ -234,6 +235,11 @@ WsLayout ws_layout(const Plan& p, int64_t max_chunk_kv) {
   off += align_up(sizeof(float) * per * p.P);
   w.ns = off;
   if (p.muon) off += align_up(sizeof(float) * lact::ns_simple_scratch_floats(p.P, p.d, p.h));
+  // the chunk scan hands the updated weights to the next query read as bf16
+  // operands (written by the update tail), where the MFMA query read runs
+  w.wb = off;
+  w.has_wb = p.bf16 && lact::apply_mfma_shape_ok(p.d, p.h);
+  if (w.has_wb) off += align_up(sizeof(uint16_t) * per * p.P);
   w.total = off;
   return w;
 }
@@ -251,10 +257,14 @@ int check_ws(const Plan& p, int64_t max_chunk_kv, void* ws, size_t ws_bytes, WsL
 
 size_t io_bytes(const Plan& p) { return p.bf16 ? 2 : 4; }
 
-// One update on validated arguments (steps 2-4).
+// One update on validated arguments (steps 2-4).  With wb non-NULL the
+// update tail also stores the new W1, W2, W3 as bf16 there (three arrays of
+// P h d values) where its kernels support it; *wb_written says whether it did.
 int run_update(const lact_config* c, const Plan& p, const lact_state* st, const void* K,
                const void* V, const float* eta, int64_t n, int64_t kv_stride,
-               int64_t eta_stride, char* ws, const WsLayout& L, hipStream_t s) {
+               int64_t eta_stride, char* ws, const WsLayout& L, hipStream_t s,
+               uint16_t* wb = nullptr, bool* wb_written = nullptr) {
+  if (wb_written != nullptr) *wb_written = false;
   const bool aligned = (reinterpret_cast<uintptr_t>(K) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(V) % 16 == 0) && (kv_stride % 8 == 0);
   const GradChoice gk = grad_choice(p, aligned, n);
@@ -310,9 +320,18 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
   ta.b = c->ns_b;
   ta.c = c->ns_c;
   ta.eps = c->ns_eps;
+  const int64_t phd = static_cast<int64_t>(p.P) * p.h * p.d;
+  auto with_wb = [&]() {
+    if (wb == nullptr) return;
+    ta.Wb1 = wb;
+    ta.Wb2 = wb + phd;
+    ta.Wb3 = wb + 2 * phd;
+    if (wb_written != nullptr) *wb_written = true;
+  };
   if (!p.muon) {
     // GD / momentum: one row-wise kernel for reduction, momentum, step, unit rows
     PhaseTimer t(1, s);
+    with_wb();
     e = lact::launch_reduce_step(ta, s);
     if (e != hipSuccess) return hip_fail(e, "update-tail kernel");
     return LACT_OK;
@@ -348,6 +367,7 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
       ta.splits = 1;
       ta.M1 = ta.M2 = ta.M3 = nullptr;
     }
+    with_wb();
     e = lact::launch_muon_tail(ta, s);
     if (e != hipSuccess) return hip_fail(e, "Muon update-tail kernel");
     return LACT_OK;
@@ -405,8 +425,10 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
   return LACT_OK;
 }
 
+// Query read; wb (or NULL): bf16 copies of the current W1, W2, W3 as the
+// update tail stores them.
 int run_apply(const Plan& p, const lact_state* st, const void* Q, void* O, int64_t m,
-              int64_t q_stride, hipStream_t s) {
+              int64_t q_stride, hipStream_t s, const uint16_t* wb = nullptr) {
   PhaseTimer t(4, s);
   lact::ApplyArgs a{};
   a.Q = Q;
@@ -425,6 +447,12 @@ int run_apply(const Plan& p, const lact_state* st, const void* Q, void* O, int64
   const bool use_mfma = p.bf16 && lact::apply_mfma_shape_ok(p.d, p.h) &&
                         reinterpret_cast<uintptr_t>(Q) % 16 == 0 &&
                         reinterpret_cast<uintptr_t>(O) % 16 == 0 && q_stride % 8 == 0;
+  if (use_mfma && wb != nullptr) {
+    const int64_t phd = static_cast<int64_t>(p.P) * p.h * p.d;
+    a.Wb1 = wb;
+    a.Wb2 = wb + phd;
+    a.Wb3 = wb + 2 * phd;
+  }
   hipError_t e = use_mfma ? lact::launch_apply_mfma(a, s) : lact::launch_apply_simple(a, s);
   if (e != hipSuccess) return hip_fail(e, "query-read kernel");
   return LACT_OK;
@@ -526,17 +554,23 @@ int lact_chunked_forward(const lact_config* cfg, const lact_state* st, const voi
   const char* Kc = static_cast<const char*>(K);
   const char* Vc = static_cast<const char*>(V);
   char* Oc = static_cast<char*>(O);
+  // bf16 copy of the weights as the last update left them (none before it)
+  uint16_t* wb = L.has_wb ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + L.wb) : nullptr;
+  bool wb_valid = false;
   for (int64_t c = 0; c < N; ++c) {
     const void* Kp = Kc + static_cast<size_t>(c * chunk_kv * p.d) * eb;
     const void* Vp = Vc + static_cast<size_t>(c * chunk_kv * p.d) * eb;
     const float* ep = eta + c * chunk_kv;
     const void* Qp = Qc + static_cast<size_t>(c * chunk_q * p.d) * eb;
     void* Op = Oc + static_cast<size_t>(c * chunk_q * p.d) * eb;
-    if (order == LACT_APPLY_THEN_UPDATE && (rc = run_apply(p, st, Qp, Op, chunk_q, T_q * p.d, s)))
+    if (order == LACT_APPLY_THEN_UPDATE &&
+        (rc = run_apply(p, st, Qp, Op, chunk_q, T_q * p.d, s, wb_valid ? wb : nullptr)))
       return rc;
-    if ((rc = run_update(cfg, p, st, Kp, Vp, ep, chunk_kv, T_kv * p.d, T_kv, static_cast<char*>(ws), L, s)))
+    if ((rc = run_update(cfg, p, st, Kp, Vp, ep, chunk_kv, T_kv * p.d, T_kv, static_cast<char*>(ws), L, s,
+                         wb, &wb_valid)))
       return rc;
-    if (order == LACT_UPDATE_THEN_APPLY && (rc = run_apply(p, st, Qp, Op, chunk_q, T_q * p.d, s)))
+    if (order == LACT_UPDATE_THEN_APPLY &&
+        (rc = run_apply(p, st, Qp, Op, chunk_q, T_q * p.d, s, wb_valid ? wb : nullptr)))
       return rc;
   }
   return LACT_OK;
