@@ -4,7 +4,8 @@
 // orthogonalisation (Muon's transform, "LaCT: Large Chunk Test-Time
 // Training" review, section "Local attention and nonlinear memory work
 // together"; coefficients as given in the layer configuration) on bf16 MFMA
-// with split operands, then W <- W - step X and unit L2 rows.
+// with split operands, then W <- W - step X and unit L2 rows (and, when
+// asked, a bf16 copy of the new W for the next query read).
 //
 // X is the s x l orientation of the gradient (s = min(d, h), l = max(d, h)),
 // X0 = G / (||G||_F + eps), then `iters` times
@@ -15,12 +16,14 @@
 // the orthogonalised result by ~3e-2 (relative) and the updated weights by
 // ~2e-2, which the split avoids.
 //
-// Work split: wave w owns CT tiles of 32 columns of X and keeps them as fp32
-// in registers, in the MFMA output layout.  That layout is directly the
-// B operand of B X (16 rows of X per k-step), so only two LDS layouts are
-// needed: X row-major (for X X^T, written once per iteration) and the
-// symmetric s x s matrices A and then B (written as the transpose of their
-// own output tiles, which for a symmetric matrix is the matrix itself).
+// Work split: wave w owns CT tiles of 32 columns of X, in registers in the
+// MFMA output layout (fp32 between steps; during a step only as packed
+// hi / lo bf16 pairs, and X <- a X + B X takes X as hi + lo, which is as
+// precise as the products).  That layout is directly the B operand of B X
+// (16 rows of X per k-step), so only two LDS layouts are needed: X
+// row-major (for X X^T, written once per iteration) and the symmetric s x s
+// matrices A and then B (written as the transpose of their own output
+// tiles, which for a symmetric matrix is the matrix itself).
 #include "lact_device.h"
 #include "lact_internal.h"
 
