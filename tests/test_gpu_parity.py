@@ -133,6 +133,37 @@ def test_resume_split_run_is_bitwise_equal():
         assert np.array_equal(dst[n].cpu().numpy(), s_full[n]), n
 
 
+def test_scan_weight_copy_matches_per_chunk_calls():
+    """Inside the chunk scan each query read loads the bf16 weight copy that
+    the update tail (here the Muon tail) wrote; per-chunk lact_update +
+    lact_apply calls convert the fp32 weights instead.  Same bits."""
+    import torch
+    import chunk_test_amd as L
+    w = small("posed", name="copy", H=2, T_kv=2 * 4096, T_q=2 * 256, chunk_kv=4096, chunk_q=256)
+    st = S.gen_weights(w)
+    x = S.gen_inputs(w)
+    O_scan, s_scan = G.run_gpu(w, x, st)
+    cfg = G.config_of(w)
+    dst = G.device_state(w, st)
+    Q, K, V = (G.to_dev(x[n], w) for n in ("Q", "K", "V"))
+    eta = G.to_dev(x["eta"], w, io=False)
+    ws = L.alloc_workspace(cfg, w.chunk_kv, w.chunk_q)
+    O = torch.empty_like(Q)
+    for c in range(2):
+        kv = slice(c * w.chunk_kv, (c + 1) * w.chunk_kv)
+        qs = slice(c * w.chunk_q, (c + 1) * w.chunk_q)
+        k, v, e = (t[:, :, kv].contiguous() for t in (K, V, eta))
+        q = Q[:, :, qs].contiguous()
+        o = torch.empty_like(q)
+        L.lact_update(cfg, dst, k, v, e, ws)
+        L.lact_apply(cfg, dst, q, o, ws=ws)
+        O[:, :, qs] = o
+    torch.cuda.synchronize()
+    assert np.array_equal(O.float().cpu().numpy(), O_scan)
+    for n in ("W1", "W2", "W3"):
+        assert np.array_equal(dst[n].cpu().numpy(), s_scan[n]), n
+
+
 def test_update_and_apply_entry_points_and_strided_views():
     import torch
     import chunk_test_amd as L
