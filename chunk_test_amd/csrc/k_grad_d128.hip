@@ -214,11 +214,31 @@ void k_grad_d128(GradArgs a, int hsl, int nbase) {
         c3[r] = 0.f;
         cg[r] = 0.f;
       }
+      // With bf16 products every group of operand reads is issued before its
+      // first use, so one wait covers the group instead of one exposed
+      // latency per read (one wavefront per SIMD: nothing else hides it);
+      // the split variant has no registers to spare for that.
+      auto kv_row = [&](int ks, bool v) {
+        return *reinterpret_cast<const bf16x8_t*>((v ? vb : kb) + chunk_off(32 * st + ln, 2 * ks + g));
+      };
+      constexpr int PRE = SPLIT ? 1 : KS;
+      bf16x8_t akv[PRE], avv[PRE];
+      if constexpr (!SPLIT) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          akv[ks] = kv_row(ks, false);
+          avv[ks] = kv_row(ks, true);
+        }
+      }
+      // eta of this lane's 16 tokens (operand slot i of half s <-> token
+      // 16 s + 8 (i / 4) + 4 g + i % 4)
+      f32x4_t eta4[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) eta4[q] = *reinterpret_cast<const f32x4_t*>(eb + 32 * st + 8 * q + 4 * g);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int off = chunk_off(32 * st + ln, 2 * ks + g);
-        const bf16x8_t ak = *reinterpret_cast<const bf16x8_t*>(kb + off);
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(vb + off);
+        const bf16x8_t ak = SPLIT ? kv_row(ks, false) : akv[SPLIT ? 0 : ks];
+        const bf16x8_t av = SPLIT ? kv_row(ks, true) : avv[SPLIT ? 0 : ks];
         c1 = mfma32(ak, w1b[ks], c1);
         c3 = mfma32(ak, w3b[ks], c3);
         cg = mfma32(av, w2b[ks], cg);
@@ -235,9 +255,30 @@ void k_grad_d128(GradArgs a, int hsl, int nbase) {
       // the d = 64 kernel for the algebra.
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const int tb = 32 * st + 16 * s + 4 * g;
-        const f32x4_t e0 = *reinterpret_cast<const f32x4_t*>(eb + tb);
-        const f32x4_t e1 = *reinterpret_cast<const f32x4_t*>(eb + tb + 8);
+        const f32x4_t e0 = eta4[2 * s], e1 = eta4[2 * s + 1];
+        // token-side operands: slots 0-3 <-> tokens 16 s + 4 g + k',
+        // slots 4-7 <-> tokens 16 s + 8 + 4 g + k' (bf16 products: read
+        // before the elementwise step, which hides their latency)
+        auto tr_op = [&](int nt, bool v) {
+          s16x4_t t[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int r = 32 * st + 16 * s + 8 * hh + 4 * (tq >> 1) + tk;
+            const int fb = 32 * nt + 16 * (tq & 1) + 4 * ta;
+            const int off = chunk_off(r, fb >> 3) + 2 * (fb & 7);
+            t[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)((v ? vb : kb) + off));
+          }
+          return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        constexpr int PRT = SPLIT ? 1 : NT;
+        bf16x8_t bkv[PRT], bvv[PRT];
+        if constexpr (!SPLIT) {
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            bkv[nt] = tr_op(nt, false);
+            bvv[nt] = tr_op(nt, true);
+          }
+        }
         bf16x8_t pg, pd1, pd3, lg, l1, l3;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -260,17 +301,8 @@ void k_grad_d128(GradArgs a, int hsl, int nbase) {
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          s16x4_t kt[2], vt[2];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int r = 32 * st + 16 * s + 8 * hh + 4 * (tq >> 1) + tk;
-            const int fb = 32 * nt + 16 * (tq & 1) + 4 * ta;
-            const int off = chunk_off(r, fb >> 3) + 2 * (fb & 7);
-            kt[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(kb + off));
-            vt[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(vb + off));
-          }
-          const bf16x8_t bk = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(kt[0], kt[1], 0, 1, 2, 3, 4, 5, 6, 7));
-          const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(vt[0], vt[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          const bf16x8_t bk = SPLIT ? tr_op(nt, false) : bkv[SPLIT ? 0 : nt];
+          const bf16x8_t bv = SPLIT ? tr_op(nt, true) : bvv[SPLIT ? 0 : nt];
           aW1[nt] = mfma32(pd1, bk, aW1[nt]);
           aW3[nt] = mfma32(pd3, bk, aW3[nt]);
           aW2[nt] = mfma32(bv, pg, aW2[nt]);
