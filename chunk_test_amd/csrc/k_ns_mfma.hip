@@ -134,7 +134,10 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
   // XFS) so the global reads stay coalesced and the register reads below use
   // immediate offsets.  X0 = G / (||G||_F + eps) in registers, MFMA output
   // layout: x[ct][mt][r] = X[32 mt + 8 (r/4) + 4 g + r%4][colof(ct)].
-  constexpr int XFS = 4 * L + 16;
+  // (an odd number of words per row: when X is G^T, a wavefront's staging
+  // stores and final reads walk down a column, rows 4 apart, and an odd
+  // stride spreads them over 16 banks instead of 1)
+  constexpr int XFS = 4 * L + 4;
   constexpr int NV = S * L / 4;  // float4 groups per matrix
   const float4* part4 = reinterpret_cast<const float4*>(part);
   const int64_t sstride4 = 3 * hd / 4;
