@@ -63,12 +63,17 @@ constexpr int BUF_BYTES = 2 * TILE + TT * 4;
 constexpr float kNegLog2e = -1.4426950408889634f;
 constexpr float kNegLn2 = -0.6931471805599453f;
 
-// XOR swizzle of the 16-byte chunks of row r: eight consecutive rows from a
-// multiple of 8 put a given chunk in eight different places (conflict-free
-// row reads), and four consecutive rows from a multiple of 4 put an aligned
-// chunk pair in four different places (conflict-free transpose reads).
-__device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
-__device__ __forceinline__ int chunk_off(int r, int c) { return r * ROW + 16 * (c ^ swz(r)); }
+// XOR swizzle of the 16-byte chunks of token row r (r_i: bit i of r),
+//     swz(r) = 4 (r1 ^ r3) + 2 r2 + r1.
+// LDS has 64 four-byte banks (256 bytes: two 128-byte rows).  A 16-byte
+// read is served 16 lanes at a time: the projections' row reads (16
+// consecutive rows, one chunk) find, among the eight rows of each parity,
+// eight different chunk positions (swz is one-to-one on r1, r2, r3).  The
+// contractions' 8-byte transpose reads are checked 32 lanes at a time: four
+// rows 4m .. 4m + 3 and an aligned quad of chunks; rows 4m and 4m + 2 (and
+// 4m + 1, 4m + 3) differ in r1, so bit 2 of swz puts their quads in the two
+// different halves of the row.  Both read kinds are free of bank conflicts.
+__device__ __forceinline__ int swz(int r) { return 4 * (((r >> 1) ^ (r >> 3)) & 1) + 2 * ((r >> 2) & 1) + ((r >> 1) & 1); }
 
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
@@ -155,6 +160,10 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
   // token (finite values); their eta is written as 0 instead of loaded, so
   // they add nothing to the sums.
   auto dma_stage = [&](int64_t t0, unsigned char* dst) {
+    // (the lane-derived offsets are recomputed per stage: a few
+    // instructions, where keeping them live would spill registers)
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int piece = 4 * wv + k;
@@ -182,6 +191,24 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
   // half, features 32 nt + 16 (Q & 1) + 4 a .. +3; lane 16 Q + 4 a + b' then
   // holds feature 32 nt + 16 (Q & 1) + 4 a + b' of those four tokens.
   const int tq = lane >> 4, tk = (lane >> 2) & 3, ta = lane & 3;
+
+  // Operand addresses as lane constants plus immediates (the XOR swizzle
+  // reduces to additions here):
+  //  row reads, token 32 st + ln, chunk 2 ks + g:  ak_off[ks] + 4096 st;
+  //  transpose reads, token 32 st + 16 s + 8 hh + L (L = 4 (tq >> 1) + tk),
+  //  features from 32 nt + 16 (tq & 1) + 4 ta:
+  //      tr_off[nt ^ hh] + 4096 st + 2048 s + 1024 hh.
+  int ak_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) ak_off[ks] = ln * ROW + 16 * ((2 * ks + g) ^ swz(ln));
+  int tr_off[2];
+  {
+    const int tl = 4 * (tq >> 1) + tk;
+    const int t1 = (tl >> 1) & 1, t2 = (tl >> 2) & 1;
+    const int low = (2 * (tq & 1) + (ta >> 1)) ^ (2 * t2 + t1);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) tr_off[x] = tl * ROW + 16 * (4 * (x ^ t1) + low) + 8 * (ta & 1);
+  }
 
   // one stage: compute on buffer cur while the next stage loads into nxt
   auto stage = [&](int64_t t0, const unsigned char* cur, unsigned char* nxt) {
@@ -212,7 +239,7 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
       bf16x8_t ak[KS], av[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int off = chunk_off(32 * st + ln, 2 * ks + g);
+        const int off = ak_off[ks] + 4096 * st;
         ak[ks] = *reinterpret_cast<const bf16x8_t*>(kb + off);
         av[ks] = *reinterpret_cast<const bf16x8_t*>(vb + off);
       }
@@ -247,9 +274,7 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
           s16x4_t kt[2], vt[2];
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const int r = 32 * st + 16 * s + 8 * hh + 4 * (tq >> 1) + tk;
-            const int fb = 32 * nt + 16 * (tq & 1) + 4 * ta;
-            const int off = chunk_off(r, fb >> 3) + 2 * (fb & 7);
+            const int off = tr_off[nt ^ hh] + 4096 * st + 2048 * s + 1024 * hh;
             kt[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(kb + off));
             vt[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(vb + off));
           }
