@@ -61,13 +61,20 @@ struct Geo {
   static constexpr int LDS = OFF_WLO + WLO_BYTES;
 };
 
-// XOR swizzle of the 16-byte chunks of row r: sixteen consecutive rows from
-// a multiple of 16 put a given chunk in sixteen different places
-// (conflict-free row reads), and four consecutive rows from a multiple of 4
-// put an aligned chunk pair in four different places (conflict-free
-// transpose reads).
-__device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1) + 8 * ((r >> 3) & 1); }
-__device__ __forceinline__ int chunk_off(int r, int c) { return r * ROW + 16 * (c ^ swz(r)); }
+// XOR swizzle of the 16-byte chunks of token row r (r_i: bit i of r),
+//     swz(r) = 8 r1 + 4 (r0 ^ r3) + 2 r0 + r2.
+// A row is one 256-byte bank window (64 four-byte banks).  The projections'
+// 16-byte row reads are served 16 lanes (16 consecutive rows, one chunk) at
+// a time: swz is one-to-one on the low four row bits, so each lane gets its
+// own 16-byte slot.  The contractions' 8-byte transpose reads are checked
+// 32 lanes at a time: four rows 4m .. 4m + 3 and an aligned quad of chunks;
+// bits 2, 3 of swz take four different values on those rows (r0, r1), so
+// the four quads fill the window.  Bits 0, 1 of swz depend on lane bits of
+// the transpose-read row only, which keeps those addresses a lane constant
+// per (nt & 1) ^ hh and nt >> 1 plus immediates.
+__device__ __forceinline__ int swz(int r) {
+  return 8 * ((r >> 1) & 1) + 4 * ((r ^ (r >> 3)) & 1) + 2 * (r & 1) + ((r >> 2) & 1);
+}
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -167,6 +174,10 @@ void k_grad_d128(GradArgs a, int hsl, int nbase) {
   // row 4 piece + l / 16, physical chunk l % 16.  Rows past the end re-read
   // the split's last token (finite values); their eta is written as 0.
   auto dma_stage = [&](int64_t t0, int b) {
+    // (the lane-derived offsets are recomputed per stage: a few
+    // instructions, where keeping them live would spill registers)
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
 #pragma unroll
     for (int k = 0; k < G::TT / 16; ++k) {
       const int piece = 4 * k + wv;
@@ -193,6 +204,27 @@ void k_grad_d128(GradArgs a, int hsl, int nbase) {
   // row Q, lane 16 Q + 4 k' + a addresses token 4 (Q >> 1) + k' (+ 8 hh) of
   // a 16-token half, features 32 nt + 16 (Q & 1) + 4 a .. +3.
   const int tq = lane >> 4, tk = (lane >> 2) & 3, ta = lane & 3;
+  // Operand addresses as lane constants plus immediates (the XOR swizzle
+  // reduces to additions here):
+  //  row reads, token 32 st + ln, chunk 2 ks + g:  ak_off[ks] + 8192 st;
+  //  transpose reads, token 32 st + 16 s + 8 hh + L (L = 4 (tq >> 1) + tk),
+  //  features from 32 nt + 16 (tq & 1) + 4 ta:
+  //      tr_off[(nt & 1) ^ hh][nt >> 1] + 8192 st + 4096 s + 2048 hh.
+  int ak_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) ak_off[ks] = ln * ROW + 16 * ((2 * ks + g) ^ swz(ln));
+  int tr_off[2][2];
+  {
+    const int tl = 4 * (tq >> 1) + tk;
+    const int r0 = tl & 1, r1 = (tl >> 1) & 1, r2 = (tl >> 2) & 1;
+    const int low = (2 * (tq & 1) + (ta >> 1)) ^ (2 * r0 + r2);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+#pragma unroll
+      for (int n1 = 0; n1 < 2; ++n1)
+        tr_off[x][n1] = tl * ROW + 16 * (8 * (n1 ^ r1) + 4 * (x ^ r0) + low) + 8 * (ta & 1);
+    }
+  }
 
   if (t_begin < t_end) dma_stage(t_begin, 0);
   int b = 0;
@@ -219,7 +251,7 @@ void k_grad_d128(GradArgs a, int hsl, int nbase) {
       // latency per read (one wavefront per SIMD: nothing else hides it);
       // the split variant has no registers to spare for that.
       auto kv_row = [&](int ks, bool v) {
-        return *reinterpret_cast<const bf16x8_t*>((v ? vb : kb) + chunk_off(32 * st + ln, 2 * ks + g));
+        return *reinterpret_cast<const bf16x8_t*>((v ? vb : kb) + ak_off[ks] + 8192 * st);
       };
       constexpr int PRE = SPLIT ? 1 : KS;
       bf16x8_t akv[PRE], avv[PRE];
@@ -263,9 +295,7 @@ void k_grad_d128(GradArgs a, int hsl, int nbase) {
           s16x4_t t[2];
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const int r = 32 * st + 16 * s + 8 * hh + 4 * (tq >> 1) + tk;
-            const int fb = 32 * nt + 16 * (tq & 1) + 4 * ta;
-            const int off = chunk_off(r, fb >> 3) + 2 * (fb & 7);
+            const int off = tr_off[(nt & 1) ^ hh][nt >> 1] + 8192 * st + 4096 * s + 2048 * hh;
             t[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)((v ? vb : kb) + off));
           }
           return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
