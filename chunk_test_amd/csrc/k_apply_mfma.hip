@@ -14,8 +14,8 @@
 //      B = G rows from LDS) and stores it.
 // Two wavefronts share each SIMD (two workgroups per CU for h = 128, one
 // of eight wavefronts for h = 256).  All LDS tiles are XOR-swizzled in
-// 16-byte chunks (chunk c of row r sits at c ^ (r & 7)) so the 16-byte
-// operand reads are conflict-free.
+// 16-byte chunks (see swz) so the operand reads and writes are free of bank
+// conflicts.
 #include "lact_device.h"
 #include "lact_internal.h"
 
@@ -72,9 +72,15 @@ __device__ __forceinline__ bf16x8_t weight_op(const uint16_t* wb, const float* w
   return load8_bf16(wf + off, vec);
 }
 
-// byte offset of 16-byte chunk `c` of row `r` (rows of `rowbytes`), swizzled
+// byte offset of 16-byte chunk `c` of row `r` (rows of `rowbytes`: 128,
+// 256 or 512), XOR-swizzled so that 16 consecutive rows put a given chunk
+// in 16 different 16-byte slots of the 256-byte bank window (LDS serves
+// these accesses 16 lanes at a time, one row each): c ^ (r & 15) for rows
+// of 16 or more chunks, c ^ ((r >> 1) & 7) for 128-byte rows (two per
+// window).
 __device__ __forceinline__ int swz(int r, int c, int rowbytes) {
-  return r * rowbytes + ((c ^ (r & 7)) << 4);
+  const int x = rowbytes >= 256 ? (r & 15) : ((r >> 1) & 7);
+  return r * rowbytes + ((c ^ x) << 4);
 }
 
 template <int D, int H>
