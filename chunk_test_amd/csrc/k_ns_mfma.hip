@@ -65,9 +65,11 @@ __device__ __forceinline__ float bf16_half(unsigned w, int k) {
 // k-steps: for tile q, hh[q] += P_hi Q_hi^T and cross[q] += P_hi Q_lo^T +
 // P_lo Q_hi^T, with P rows at pa[q] and Q rows at pb[q] (row-major bf16 in
 // LDS, 16-byte operand slices at +32 ks; the lo block `half` bytes after the
-// hi block).  The k loop is unrolled and the tiles interleaved inside it, so
+// hi block).  With PRE every operand of the phase is read before the first
+// product (one wave per SIMD has no other wave to hide the read latency);
+// otherwise the k loop is unrolled and the tiles interleaved inside it, so
 // the reads of one k-step overlap the products of the previous ones.
-template <int NQ, int KSTEPS>
+template <int NQ, int KSTEPS, bool PRE>
 __device__ __forceinline__ void split_tiles(const unsigned char* const (&pa)[NQ],
                                             const unsigned char* const (&pb)[NQ], int half,
                                             f32x16_t (&hh)[NQ], f32x16_t (&cross)[NQ]) {
@@ -79,19 +81,58 @@ __device__ __forceinline__ void split_tiles(const unsigned char* const (&pa)[NQ]
       cross[q][r] = 0.f;
     }
   }
+  if constexpr (PRE) {
+    bf16x8_t ah[KSTEPS][NQ], al[KSTEPS][NQ], bh[KSTEPS][NQ], bl[KSTEPS][NQ];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
+    for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(pa[q] + 32 * ks);
-      const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(pa[q] + half + 32 * ks);
-      const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(pb[q] + 32 * ks);
-      const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(pb[q] + half + 32 * ks);
-      hh[q] = mfma(ah, bh, hh[q]);
-      cross[q] = mfma(ah, bl, cross[q]);
-      cross[q] = mfma(al, bh, cross[q]);
+      for (int q = 0; q < NQ; ++q) {
+        ah[ks][q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + 32 * ks);
+        bh[ks][q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + 32 * ks);
+        al[ks][q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + half + 32 * ks);
+        bl[ks][q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + half + 32 * ks);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        hh[q] = mfma(ah[ks][q], bh[ks][q], hh[q]);
+        cross[q] = mfma(ah[ks][q], bl[ks][q], cross[q]);
+        cross[q] = mfma(al[ks][q], bh[ks][q], cross[q]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      bf16x8_t ah[NQ], al[NQ], bh[NQ], bl[NQ];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        ah[q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + 32 * ks);
+        al[q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + half + 32 * ks);
+        bh[q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + 32 * ks);
+        bl[q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + half + 32 * ks);
+      }
+      // the two cross products of a tile are NQ products apart
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) hh[q] = mfma(ah[q], bh[q], hh[q]);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) cross[q] = mfma(ah[q], bl[q], cross[q]);
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) cross[q] = mfma(al[q], bh[q], cross[q]);
     }
   }
+}
+
+// Column order of the stored s x s matrices A and B: inside every 16 columns
+// the two groups {0-3, 8-11} and {4-7, 12-15} are stored as contiguous runs of
+// eight, so the B X step (whose k order follows the MFMA output rows of X)
+// reads its operand as one 16-byte slice per lane.  Products over A's columns
+// read both operands in the same stored order, which leaves them unchanged.
+// Column 32 ti + 8 rg + 4 g + i (i < 4) is stored at the returned column.
+__device__ __forceinline__ int stored_col(int ti, int rg, int g) {
+  return 32 * ti + 16 * (rg >> 1) + 8 * g + 4 * (rg & 1);
 }
 
 template <int S, int L>
@@ -106,6 +147,9 @@ struct NSGeo {
   static constexpr int REGION = (2 * X_HALF > 2 * A_HALF) ? 2 * X_HALF : 2 * A_HALF;
   static constexpr int ATILES = MT * MT;
   static constexpr int ATW = (ATILES + NW - 1) / NW;  // A tiles per wave
+  // one wave per SIMD with registers to spare: read each phase's operands
+  // ahead, keep X in fp32 across the iteration, load W at the start
+  static constexpr bool PRE = (S == 64 && L == 128);
 };
 
 template <int S, int L>
@@ -139,6 +183,9 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
   // stride spreads them over 16 banks instead of 1)
   constexpr int XFS = 4 * L + 4;
   constexpr int NV = S * L / 4;  // float4 groups per matrix
+  constexpr int GPT = NV / (2 * L);
+  float4* W4 = reinterpret_cast<float4*>(Wm);
+  float4 wv[GPT];
   const float4* part4 = reinterpret_cast<const float4*>(part);
   const int64_t sstride4 = 3 * hd / 4;
   // every thread sums CPT float4 groups (tid + 2 L k) over the splits, with
@@ -177,6 +224,10 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
       acc[k].w += t.w;
     }
   }
+  if constexpr (G::PRE) {
+#pragma unroll
+    for (int k = 0; k < GPT; ++k) wv[k] = W4[tid + 2 * L * k];
+  }
   if (Mm != nullptr) {
     // M <- beta M + G, G <- M (all loads issued before the first store)
     float4* M4 = reinterpret_cast<float4*>(Mm);
@@ -207,7 +258,11 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
       *reinterpret_cast<float*>(lds + i * XFS + 4 * j) = v;
     }
   }
-  ss = wave_sum(ss);
+  {
+    float t[1] = {ss};
+    group_sums<64>(t);
+    ss = t[0];
+  }
   if (lane == 0) red[w] = ss;
   __syncthreads();
   float tot = 0.f;
@@ -282,7 +337,7 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
         pb[q] = xhi + (32 * (t % G::MT) + ln) * G::XRS + 16 * g;
       }
       f32x16_t a2[G::ATW];
-      split_tiles<G::ATW, L / 16>(pa, pb, G::X_HALF, at, a2);
+      split_tiles<G::ATW, L / 16, G::PRE>(pa, pb, G::X_HALF, at, a2);
 #pragma unroll
       for (int q = 0; q < G::ATW; ++q) {
 #pragma unroll
@@ -298,7 +353,7 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
           const unsigned char* pa[1] = {xhi + (32 * (t / G::MT) + ln) * G::XRS + 16 * g};
           const unsigned char* pb[1] = {xhi + (32 * (t % G::MT) + ln) * G::XRS + 16 * g};
           f32x16_t hh[1], a2[1];
-          split_tiles<1, L / 16>(pa, pb, G::X_HALF, hh, a2);
+          split_tiles<1, L / 16, false>(pa, pb, G::X_HALF, hh, a2);
 #pragma unroll
           for (int r = 0; r < 16; ++r) at[q][r] = hh[0][r] + a2[0][r];
         }
@@ -307,7 +362,8 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
     __syncthreads();  // X row-major no longer needed: the region becomes A
 
     // A is symmetric: tile (ti, tj) transposed lands at rows 32 tj + ln,
-    // columns 32 ti + 8 (r/4) + 4 g .. +3 (four consecutive bf16 per store)
+    // columns 32 ti + 8 (r/4) + 4 g .. +3 (four consecutive bf16 per store,
+    // at their stored columns)
 #pragma unroll
     for (int q = 0; q < G::ATW; ++q) {
       const int t = w + G::NW * q;
@@ -323,7 +379,7 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
             h4[i] = hi;
             l4[i] = lo;
           }
-          const int off = (32 * tj + ln) * G::ARS + 2 * (32 * ti + 8 * rg + 4 * g);
+          const int off = (32 * tj + ln) * G::ARS + 2 * stored_col(ti, rg, g);
           *reinterpret_cast<bf16x4_t*>(ahi + off) = h4;
           *reinterpret_cast<bf16x4_t*>(alo + off) = l4;
         }
@@ -342,7 +398,7 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
         pb[q] = ahi + (32 * (t % G::MT) + ln) * G::ARS + 16 * g;
       }
       f32x16_t acc[G::ATW], a2[G::ATW];
-      split_tiles<G::ATW, S / 16>(pa, pb, G::A_HALF, acc, a2);
+      split_tiles<G::ATW, S / 16, G::PRE>(pa, pb, G::A_HALF, acc, a2);
 #pragma unroll
       for (int q = 0; q < G::ATW; ++q) {
 #pragma unroll
@@ -356,7 +412,7 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
           const unsigned char* pa[1] = {ahi + (32 * (t / G::MT) + ln) * G::ARS + 16 * g};
           const unsigned char* pb[1] = {ahi + (32 * (t % G::MT) + ln) * G::ARS + 16 * g};
           f32x16_t acc[1], a2[1];
-          split_tiles<1, S / 16>(pa, pb, G::A_HALF, acc, a2);
+          split_tiles<1, S / 16, false>(pa, pb, G::A_HALF, acc, a2);
 #pragma unroll
           for (int r = 0; r < 16; ++r) at[q][r] = a.b * at[q][r] + a.c * (acc[0][r] + a2[0][r]);  // now B
         }
@@ -379,7 +435,7 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
             h4[i] = hi;
             l4[i] = lo;
           }
-          const int off = (32 * tj + ln) * G::ARS + 2 * (32 * ti + 8 * rg + 4 * g);
+          const int off = (32 * tj + ln) * G::ARS + 2 * stored_col(ti, rg, g);
           *reinterpret_cast<bf16x4_t*>(ahi + off) = h4;
           *reinterpret_cast<bf16x4_t*>(alo + off) = l4;
         }
@@ -390,7 +446,8 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
     // ---- X <- a X + B X for this wave's 32 columns.  The B operand (X,
     // 16 rows per k-step) comes from this lane's own registers; the A
     // operand (rows of B) uses the matching row order:
-    // slot 8g + i of k-step s <-> row 16 s + 8 (i/4) + 4 g + i%4.
+    // slot 8g + i of k-step s <-> row 16 s + 8 (i/4) + 4 g + i%4, which is
+    // stored column 16 s + 8 g + i (one 16-byte read per lane and half).
 #pragma unroll
     for (int ct = 0; ct < G::CT; ++ct) {
       f32x16_t accs[G::MT];
@@ -399,40 +456,55 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) accs[mt][r] = 0.f;
       }
+      bf16x8_t bh[G::PRE ? S / 16 : 1][G::MT], bl[G::PRE ? S / 16 : 1][G::MT];
+      if constexpr (G::PRE) {
+#pragma unroll
+        for (int s = 0; s < S / 16; ++s) {
+#pragma unroll
+          for (int mt = 0; mt < G::MT; ++mt) {
+            const unsigned char* rb = ahi + (32 * mt + ln) * G::ARS + 16 * g + 32 * s;
+            bh[s][mt] = *reinterpret_cast<const bf16x8_t*>(rb);
+            bl[s][mt] = *reinterpret_cast<const bf16x8_t*>(rb + G::A_HALF);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // products of one k-step, the MT tiles interleaved (a tile's three
+      // products are MT apart)
 #pragma unroll
       for (int s = 0; s < S / 16; ++s) {
+        const int sp = G::PRE ? s : 0;
+        if constexpr (!G::PRE) {
 #pragma unroll
-        for (int mt = 0; mt < G::MT; ++mt) {
-          const unsigned char* rb = ahi + (32 * mt + ln) * G::ARS + 8 * g + 32 * s;
-          const bf16x4_t h0 = *reinterpret_cast<const bf16x4_t*>(rb);
-          const bf16x4_t h1 = *reinterpret_cast<const bf16x4_t*>(rb + 16);
-          const bf16x4_t l0 = *reinterpret_cast<const bf16x4_t*>(rb + G::A_HALF);
-          const bf16x4_t l1 = *reinterpret_cast<const bf16x4_t*>(rb + G::A_HALF + 16);
-          bf16x8_t bh, bl;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            bh[i] = h0[i];
-            bh[4 + i] = h1[i];
-            bl[i] = l0[i];
-            bl[4 + i] = l1[i];
+          for (int mt = 0; mt < G::MT; ++mt) {
+            const unsigned char* rb = ahi + (32 * mt + ln) * G::ARS + 16 * g + 32 * s;
+            bh[0][mt] = *reinterpret_cast<const bf16x8_t*>(rb);
+            bl[0][mt] = *reinterpret_cast<const bf16x8_t*>(rb + G::A_HALF);
           }
-          const bf16x8_t oh = __builtin_bit_cast(bf16x8_t, xh[ct][s]);
-          const bf16x8_t ol = __builtin_bit_cast(bf16x8_t, xl[ct][s]);
-          accs[mt] = mfma(bh, oh, accs[mt]);
-          accs[mt] = mfma(bh, ol, accs[mt]);
-          accs[mt] = mfma(bl, oh, accs[mt]);
         }
+        const bf16x8_t oh = __builtin_bit_cast(bf16x8_t, xh[ct][s]);
+        const bf16x8_t ol = __builtin_bit_cast(bf16x8_t, xl[ct][s]);
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) accs[mt] = mfma(bh[sp][mt], oh, accs[mt]);
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) accs[mt] = mfma(bh[sp][mt], ol, accs[mt]);
+#pragma unroll
+        for (int mt = 0; mt < G::MT; ++mt) accs[mt] = mfma(bl[sp][mt], oh, accs[mt]);
       }
-      // X <- a X + B X, with X taken as hi + lo (the fp32 X is not kept
-      // across the iteration; hi + lo carries ~16 significant bits, the
-      // precision of every product here)
+      // X <- a X + B X.  With PRE the fp32 X stays live across the
+      // iteration; otherwise X is taken as hi + lo (~16 significant bits,
+      // the precision of every product here), which frees its registers.
 #pragma unroll
       for (int mt = 0; mt < G::MT; ++mt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int ks = 2 * mt + (r >> 3), j = (r & 7) >> 1, k = r & 1;
-          const float xv = bf16_half(xh[ct][ks][j], k) + bf16_half(xl[ct][ks][j], k);
-          x[ct][mt][r] = a.a * xv + accs[mt][r];
+          if constexpr (G::PRE) {
+            x[ct][mt][r] = a.a * x[ct][mt][r] + accs[mt][r];
+          } else {
+            const int ks = 2 * mt + (r >> 3), j = (r & 7) >> 1, k = r & 1;
+            const float xv = bf16_half(xh[ct][ks][j], k) + bf16_half(xl[ct][ks][j], k);
+            x[ct][mt][r] = a.a * xv + accs[mt][r];
+          }
         }
       }
     }
@@ -440,16 +512,16 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
 
   // ---- W <- W - step X, then unit L2 rows.  Every thread takes GPT float4
   // groups of the stored matrix (rows of `rowlen`, rowlen / 4 lanes per row,
-  // so a row's lanes are an aligned lane group); all W loads are issued here,
-  // before X goes to LDS, so their latency is paid once.  W1, W3 rows are
-  // columns of X, W2 rows are rows of X.
-  constexpr int GPT = NV / (2 * L);
-  const int rowlen = tr ? S : L;
-  const int lpr = rowlen / 4;
-  float4* W4 = reinterpret_cast<float4*>(Wm);
-  float4 wv[GPT];
+  // so a row's lanes are an aligned lane group); all W loads are issued
+  // together (with PRE at the start of the kernel, otherwise here, before X
+  // goes to LDS), so their latency is paid once.  W1, W3 rows are columns
+  // of X, W2 rows are rows of X.
+  const int rowlen = tr ? S : L;  // (S and L are powers of two)
+  const int lg_rowlen = tr ? __builtin_ctz(S) : __builtin_ctz(L);
+  if constexpr (!G::PRE) {
 #pragma unroll
-  for (int k = 0; k < GPT; ++k) wv[k] = W4[tid + 2 * L * k];
+    for (int k = 0; k < GPT; ++k) wv[k] = W4[tid + 2 * L * k];
+  }
 
   __syncthreads();
 #pragma unroll
@@ -464,21 +536,37 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
     }
   }
   __syncthreads();
+  // (every row's squared norm first, then all GPT group reductions together,
+  // so their shuffle latencies overlap)
+  float v[GPT][4], sq[GPT];
 #pragma unroll
   for (int k = 0; k < GPT; ++k) {
     const int e = 4 * (tid + 2 * L * k);
-    const int row = e / rowlen, col = e % rowlen;
-    float v[4] = {wv[k].x, wv[k].y, wv[k].z, wv[k].w};
-    float sq = 0.f;
+    const int row = e >> lg_rowlen, col = e & (rowlen - 1);
+    v[k][0] = wv[k].x;
+    v[k][1] = wv[k].y;
+    v[k][2] = wv[k].z;
+    v[k][3] = wv[k].w;
+    sq[k] = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = tr ? col + q : row, j = tr ? row : col + q;  // element of X
-      v[q] -= a.step * *reinterpret_cast<const float*>(lds + i * XFS + 4 * j);
-      sq += v[q] * v[q];
+      v[k][q] -= a.step * *reinterpret_cast<const float*>(lds + i * XFS + 4 * j);
+      sq[k] += v[k][q] * v[k][q];
     }
-    sq = group_sum(sq, lpr);
-    const float den = fmaxf(sqrtf(sq), a.norm_eps);
-    const float4 xw = make_float4(v[0] / den, v[1] / den, v[2] / den, v[3] / den);
+  }
+  const float inv_eps = 1.f / a.norm_eps;
+  if (tr) {
+    group_sums<S / 4>(sq);
+  } else {
+    group_sums<L / 4>(sq);
+  }
+#pragma unroll
+  for (int k = 0; k < GPT; ++k) {
+    // 1 / max(||r||, eps) as min(1 / sqrt(||r||^2), 1 / eps), the
+    // reciprocal square root from the hardware approximation (~1 ulp)
+    const float inv = fminf(__builtin_amdgcn_rsqf(sq[k]), inv_eps);
+    const float4 xw = make_float4(v[k][0] * inv, v[k][1] * inv, v[k][2] * inv, v[k][3] * inv);
     W4[tid + 2 * L * k] = xw;
     if (Wbm != nullptr) {
       bf16x4_t b4;

@@ -55,4 +55,47 @@ __device__ __forceinline__ float group_sum(float v, int width) {
   return v;
 }
 
+// v from another lane of the same 16-lane row (DPP lane permutation; no LDS
+// round trip): quad_perm [1,0,3,2] (xor 1), quad_perm [2,3,0,1] (xor 2),
+// row_half_mirror (i <-> 7 - i within 8), row_mirror (i <-> 15 - i).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sums over aligned groups of W lanes (W a power of two <= 64) of N values
+// at once, every lane of a group receiving its group's sum.  Inside a
+// 16-lane row the butterfly runs on DPP moves (after the two quad steps
+// every lane holds its quad's sum, the half-mirror adds the other quad of
+// its half-row, the mirror the other half-row); wider groups add lane
+// shuffles.  The N reductions are independent, so their latencies overlap.
+template <int W, int N>
+__device__ __forceinline__ void group_sums(float (&v)[N]) {
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "group width");
+  if constexpr (W >= 2) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_mov<0xB1>(v[i]);
+  }
+  if constexpr (W >= 4) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_mov<0x4E>(v[i]);
+  }
+  if constexpr (W >= 8) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_mov<0x141>(v[i]);
+  }
+  if constexpr (W >= 16) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += dpp_mov<0x140>(v[i]);
+  }
+  if constexpr (W >= 32) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += __shfl_xor(v[i], 16, 64);
+  }
+  if constexpr (W >= 64) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += __shfl_xor(v[i], 32, 64);
+  }
+}
+
 }  // namespace lact
