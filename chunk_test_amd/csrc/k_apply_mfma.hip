@@ -65,10 +65,12 @@ __device__ __forceinline__ bf16x8_t load8_bf16(const float* p, bool vec) {
   return v;
 }
 
-// operand of eight consecutive weights at element offset `off`: one 16-byte
-// load from the bf16 copy when there is one, else converted from fp32
-__device__ __forceinline__ bf16x8_t weight_op(const uint16_t* wb, const float* wf, int64_t off, bool vec) {
-  if (wb != nullptr) return *reinterpret_cast<const bf16x8_t*>(wb + off);
+// operand of eight consecutive weights: from the bf16 copy when there is
+// one (element offset `toff` in its operand order, 16 consecutive bytes per
+// lane), else converted from the fp32 weights at element offset `off`
+__device__ __forceinline__ bf16x8_t weight_op(const uint16_t* wb, int64_t toff, const float* wf, int64_t off,
+                                              bool vec) {
+  if (wb != nullptr) return *reinterpret_cast<const bf16x8_t*>(wb + toff);
   return load8_bf16(wf + off, vec);
 }
 
@@ -111,10 +113,12 @@ void k_apply_mfma(ApplyArgs a, int per_wg, int wg_per_pair) {
   bf16x8_t w1a[KS1], w3a[KS1];
   {
     const int64_t row = pair * hd + static_cast<int64_t>(32 * w + ln) * D;
+    // (the copy's block (w, ks), lane slice = wb_tiled(32 w + ln, 16 ks + 8 g, D))
+    const int64_t tb = pair * hd + static_cast<int64_t>(w) * (D / 16) * 512 + 8 * lane;
 #pragma unroll
     for (int ks = 0; ks < KS1; ++ks) {
-      w1a[ks] = weight_op(a.Wb1, a.W1, row + 16 * ks + 8 * g, a.w_vec);
-      w3a[ks] = weight_op(a.Wb3, a.W3, row + 16 * ks + 8 * g, a.w_vec);
+      w1a[ks] = weight_op(a.Wb1, tb + 512 * ks, a.W1, row + 16 * ks + 8 * g, a.w_vec);
+      w3a[ks] = weight_op(a.Wb3, tb + 512 * ks, a.W3, row + 16 * ks + 8 * g, a.w_vec);
     }
   }
   // ---- this wave's phase-2 tile: rows 32 dt .. of O^T, tokens 32 tt ..
@@ -124,8 +128,10 @@ void k_apply_mfma(ApplyArgs a, int per_wg, int wg_per_pair) {
   bf16x8_t w2b[KS2];
   {
     const int64_t row = pair * hd + static_cast<int64_t>(32 * dt + ln) * H;
+    const int64_t tb = pair * hd + static_cast<int64_t>(dt) * (H / 16) * 512 + 8 * lane;
 #pragma unroll
-    for (int ks = 0; ks < KS2; ++ks) w2b[ks] = weight_op(a.Wb2, a.W2, row + 16 * ks + 8 * g, a.w_vec);
+    for (int ks = 0; ks < KS2; ++ks)
+      w2b[ks] = weight_op(a.Wb2, tb + 512 * ks, a.W2, row + 16 * ks + 8 * g, a.w_vec);
   }
 
   const uint16_t* Qg = static_cast<const uint16_t*>(a.Q) + static_cast<int64_t>(pair) * a.q_stride;

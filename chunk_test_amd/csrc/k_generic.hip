@@ -436,7 +436,9 @@ __global__ __launch_bounds__(kThreads) void k_reduce_step(TailArgs a) {
     if (e < len) {
       const float x = v[k] / den;
       W[wo + e] = x;
-      if (Wb != nullptr) Wb[wo + e] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+      if (Wb != nullptr)
+        Wb[pair * hd + wb_tiled(static_cast<int>((po % hd) / len), e, len)] =
+            __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
     }
   }
 }
@@ -542,7 +544,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_step_v4(TailArgs a, int64_t
         b[1] = static_cast<__bf16>(x.y);
         b[2] = static_cast<__bf16>(x.z);
         b[3] = static_cast<__bf16>(x.w);
-        reinterpret_cast<bf16x4_t*>(Wb + wo)[c] = b;
+        *reinterpret_cast<bf16x4_t*>(Wb + pair * hd + wb_tiled(static_cast<int>((po % hd) / len), 4 * c, len)) = b;
       }
     }
   }

@@ -574,7 +574,8 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
       b4[1] = static_cast<__bf16>(xw.y);
       b4[2] = static_cast<__bf16>(xw.z);
       b4[3] = static_cast<__bf16>(xw.w);
-      reinterpret_cast<bf16x4_t*>(Wbm)[tid + 2 * L * k] = b4;
+      const int e = 4 * (tid + 2 * L * k);
+      *reinterpret_cast<bf16x4_t*>(Wbm + wb_tiled(e >> lg_rowlen, e & (rowlen - 1), rowlen)) = b4;
     }
   }
 }

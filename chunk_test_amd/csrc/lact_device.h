@@ -36,6 +36,19 @@ __device__ __forceinline__ void store_io(void* base, int64_t i, float v) {
   }
 }
 
+// Offset of element (r, c) of a rows x cols matrix (rows a multiple of 32,
+// cols of 16) in the bf16 operand copy of the fast weights.  The copy is
+// stored in the order the query read loads it as 32x32x16 MFMA operands:
+// blocks of 32 rows x 16 columns, row-block major, each block as the 64
+// 16-byte slices of its lanes (lane 32 (c / 8 % 2) + r % 32 holds the eight
+// columns 16 (c / 16) + 8 (c / 8 % 2) .. +7 of row r), so a wavefront reads
+// one block as 1 KiB of consecutive bytes.  Four elements c .. c + 3 with
+// c % 4 == 0 stay adjacent.
+__device__ __forceinline__ int64_t wb_tiled(int r, int c, int cols) {
+  return ((static_cast<int64_t>(r >> 5) * (cols >> 4) + (c >> 4)) * 64 + ((c >> 3) & 1) * 32 + (r & 31)) * 8 +
+         (c & 7);
+}
+
 // logistic function without overflow for either sign (full-precision expf)
 __device__ __forceinline__ float sigmoid_f(float z) {
   if (z >= 0.f) return 1.f / (1.f + expf(-z));

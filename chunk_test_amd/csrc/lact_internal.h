@@ -56,8 +56,9 @@ struct TailArgs {
   float step, norm_eps;
   int P, d, h, iters;
   float a, b, c, eps;     // Newton-Schulz (Muon only)
-  // when non-NULL: also store the updated W1, W2, W3 rounded to bf16 (same
-  // shapes), the operand copy a following query read can load directly
+  // when non-NULL: also store the updated W1, W2, W3 rounded to bf16 (P h d
+  // values each, every matrix in the operand order of wb_tiled), the copy a
+  // following query read loads directly
   uint16_t *Wb1, *Wb2, *Wb3;
 };
 
@@ -79,8 +80,9 @@ struct ApplyArgs {
   int P, d, h;
   int bf16;
   int w_vec;  // W1, W2, W3 16-byte aligned
-  // when non-NULL: bf16 copies of W1, W2, W3 (as stored by the update tail),
-  // read instead of converting the fp32 weights
+  // when non-NULL: bf16 copies of W1, W2, W3 (as stored by the update tail,
+  // in the operand order of wb_tiled), read instead of converting the fp32
+  // weights
   const uint16_t *Wb1, *Wb2, *Wb3;
 };
 
