@@ -262,14 +262,14 @@ void k_apply_mfma(ApplyArgs a, int per_wg, int wg_per_pair) {
 template <int D, int H>
 hipError_t launch_dh(const ApplyArgs& a, hipStream_t s) {
   // queries per workgroup (a multiple of the step): the workgroups of all
-  // pairs fill the CUs about once (each workgroup converts its pair's W once)
+  // pairs fill the CUs about once (each workgroup loads its pair's W once)
   using G = AGeo<D, H>;
   constexpr int TQ = G::TQ;
   const int64_t slots = 256 * G::WG_PER_CU;
   const int64_t per_pair = a.P >= slots ? 1 : slots / a.P;
   int64_t per = (a.m + per_pair - 1) / per_pair;
   per = (per + TQ - 1) / TQ * TQ;
-  if (per < 4 * TQ) per = 4 * TQ;
+  if (per < 2 * TQ) per = 2 * TQ;  // at least one pipelined step pair
   const int64_t gx = (a.m + per - 1) / per;
   const unsigned blocks = static_cast<unsigned>((gx * a.P + 7) / 8 * 8);
   hipLaunchKernelGGL((k_apply_mfma<D, H>), dim3(blocks), dim3(G::THREADS), 0, s, a, static_cast<int>(per),
