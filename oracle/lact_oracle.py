@@ -37,6 +37,12 @@ The pages print no formulas.  The plainest reading used here:
   X0 = G / (||G||_F + eps), then I times  A = X X^T, X <- a X + (b A + c A A) X.
 * after each update every stored row r of W1, W3 (length d) and W2 (length h)
   becomes r / max(||r||_2, norm_eps).  The initial weights are not normalised.
+* variant ``norm_keep`` (weight normalisation with the magnitude held: the
+  reference list's "Weight Normalization" separates a row's direction from
+  its length; here the update moves only the direction): the stepped row u
+  is rescaled to the length the row had before the update,
+  u * ||r_old||_2 / max(||u||_2, norm_eps), so every row keeps its initial
+  length through the scan.
 * every query of a chunk reads the same W (no causality inside a chunk).
 
 Every routine takes a ``dtype`` (float64 for parity, float32 for the timed
@@ -189,13 +195,15 @@ def row_normalize(W, eps=1e-12):
 
 
 def optimizer_step(W, dW, M, *, opt, beta, ns_iters, ns_coeffs, ns_eps, step,
-                   norm_eps, normalize=True):
+                   norm_eps, normalize=True, norm_keep=False):
     """One update of one fast-weight matrix.  Returns (W_new, M_new).
 
     GD: direction = dW.  Momentum: M <- beta M + dW, direction = M.
     Muon: direction = NS(dW), or NS(M) after the momentum update when
     beta > 0.  Then W <- W - step * direction, then row-wise L2
-    normalisation (unless ``normalize`` is False, used by the linear pins).
+    normalisation (unless ``normalize`` is False, used by the linear pins);
+    with ``norm_keep`` each row is rescaled to its length before the step
+    instead of to 1.
     """
     if opt not in OPTIMIZERS:
         raise ValueError(f"unknown optimizer {opt!r}")
@@ -208,9 +216,12 @@ def optimizer_step(W, dW, M, *, opt, beta, ns_iters, ns_coeffs, ns_eps, step,
         g = M
     if opt == OPT_MUON:
         g = newton_schulz(g, ns_iters, ns_coeffs, ns_eps)
+    W_old = W
     W = W - step * g
     if normalize:
         W = row_normalize(W, norm_eps)
+        if norm_keep:
+            W = W * np.sqrt(np.sum(W_old * W_old, axis=1, keepdims=True))
     return W, M
 
 
@@ -223,12 +234,14 @@ class Hyper:
 
     ``net`` selects the fast net: "swiglu" (the layer) or "linear" (the test
     mode of the closed-form pins, with a single matrix W in R^{d x d}).
-    ``normalize`` turns the row normalisation off for the linear pins.
+    ``normalize`` turns the row normalisation off for the linear pins;
+    ``norm_keep`` rescales every updated row to its length before the update
+    instead of to 1.
     """
 
     def __init__(self, opt=OPT_GD, beta=0.0, ns_iters=5, ns_coeffs=MUON_COEFFS,
                  ns_eps=1e-7, step=1.0, norm_eps=1e-12, token_block=None,
-                 net="swiglu", normalize=True):
+                 net="swiglu", normalize=True, norm_keep=False):
         if opt not in OPTIMIZERS:
             raise ValueError(f"unknown optimizer {opt!r}")
         if net not in ("swiglu", "linear"):
@@ -243,6 +256,7 @@ class Hyper:
         self.token_block = token_block
         self.net = net
         self.normalize = bool(normalize)
+        self.norm_keep = bool(norm_keep)
 
     def uses_momentum(self):
         return self.opt == OPT_MOMENTUM or (self.opt == OPT_MUON and self.beta > 0)
@@ -275,7 +289,8 @@ def update_pair(W, M, K, V, eta, hp: Hyper):
         Wn, Mn = optimizer_step(Wx, dWx, Mx, opt=hp.opt, beta=hp.beta,
                                 ns_iters=hp.ns_iters, ns_coeffs=hp.ns_coeffs,
                                 ns_eps=hp.ns_eps, step=hp.step,
-                                norm_eps=hp.norm_eps, normalize=hp.normalize)
+                                norm_eps=hp.norm_eps, normalize=hp.normalize,
+                                norm_keep=hp.norm_keep)
         out_w.append(Wn)
         out_m.append(Mn)
     return tuple(out_w), (tuple(out_m) if hp.uses_momentum() else None)

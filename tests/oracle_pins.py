@@ -287,11 +287,12 @@ def pin_set_semantics(o, seed=9):
     return max(max(rel_err(a, b) for a, b in zip(Wa, Wb)), rel_err(Op, O[p]))
 
 
-def per_token_reference(W, Q, K, V, eta, order, opt, beta, iters=5):
+def per_token_reference(W, Q, K, V, eta, order, opt, beta, iters=5, keep=False):
     """Token-by-token scan written independently of the oracle.
 
     Gradient by torch.autograd, Newton-Schulz by its SVD form, heavy-ball
-    momentum, unit-norm rows after every token.
+    momentum, unit-norm rows after every token (with ``keep``: each row back
+    to the length it had before the token's update).
     """
     W = [np.array(x, np.float64) for x in W]
     M = [np.zeros_like(x) for x in W]
@@ -314,19 +315,20 @@ def per_token_reference(W, Q, K, V, eta, order, opt, beta, iters=5):
                 step = M[m]
             if opt == "muon":
                 step = ns_by_svd(step, iters)
+            length = np.linalg.norm(W[m], axis=1, keepdims=True) if keep else 1.0
             W[m] = W[m] - step
-            W[m] = W[m] / np.linalg.norm(W[m], axis=1, keepdims=True)
+            W[m] = length * W[m] / np.linalg.norm(W[m], axis=1, keepdims=True)
         if order == "update_then_apply":
             O[t] = read(t)
     return O, W
 
 
-def pin_chunk1(o, order, opt, beta=0.0, seed=10):
+def pin_chunk1(o, order, opt, beta=0.0, seed=10, keep=False):
     W, Q, K, V, eta = _small_problem(seed, d=4, h=8, T=12)
-    hp = o.Hyper(opt=opt, beta=beta)
+    hp = o.Hyper(opt=opt, beta=beta, norm_keep=keep)
     M = tuple(np.zeros_like(x) for x in W) if hp.uses_momentum() else None
     O, Wn, _ = o.chunked_forward_pair(W, M, Q, K, V, eta, 1, 1, order, hp)
-    Or, Wr = per_token_reference(W, Q, K, V, eta, order, opt, beta)
+    Or, Wr = per_token_reference(W, Q, K, V, eta, order, opt, beta, keep=keep)
     return max(rel_err(O, Or), max(rel_err(a, b) for a, b in zip(Wn, Wr)))
 
 
@@ -351,6 +353,41 @@ def pin_eta_zero(o, seed=11):
             if order == "apply_then_update":
                 ref[:8] = read(W, Q[:8])
             worst = max(worst, rel_err(O, ref))
+    return worst
+
+
+def pin_norm_keep_lengths(o, seed=13):
+    """norm_keep: after a scan every row still has its initial length (rows of
+    random lengths, every optimizer)."""
+    W, Q, K, V, eta = _small_problem(seed)
+    worst = 0.0
+    for opt, beta in (("gd", 0.0), ("momentum", 0.9), ("muon", 0.0), ("muon", 0.5)):
+        hp = o.Hyper(opt=opt, beta=beta, norm_keep=True)
+        M = tuple(np.zeros_like(x) for x in W) if hp.uses_momentum() else None
+        _, Wn, _ = o.chunked_forward_pair(W, M, Q, K, V, eta, 8, 8, "apply_then_update", hp)
+        for x, x0 in zip(Wn, W):
+            n0 = np.linalg.norm(x0, axis=1)
+            worst = max(worst, float(np.max(np.abs(np.linalg.norm(x, axis=1) - n0) / n0)))
+    return worst
+
+
+def pin_norm_keep_direction(o, seed=14):
+    """norm_keep moves only the lengths: one update from the same state gives
+    the unit rule's rows scaled by the old lengths; from unit-length rows the
+    two rules agree over a whole scan."""
+    W, Q, K, V, eta = _small_problem(seed)
+    worst = 0.0
+    for opt in ("gd", "muon"):
+        Wu, _ = o.update_pair(W, None, K, V, eta, o.Hyper(opt=opt))
+        Wk, _ = o.update_pair(W, None, K, V, eta, o.Hyper(opt=opt, norm_keep=True))
+        for a, b, x0 in zip(Wk, Wu, W):
+            worst = max(worst, rel_err(a, b * np.linalg.norm(x0, axis=1, keepdims=True)))
+        Wunit = tuple(unit_rows(x) for x in W)
+        Ou, Wu, _ = o.chunked_forward_pair(Wunit, None, Q, K, V, eta, 8, 8, "update_then_apply",
+                                           o.Hyper(opt=opt))
+        Ok, Wk, _ = o.chunked_forward_pair(Wunit, None, Q, K, V, eta, 8, 8, "update_then_apply",
+                                           o.Hyper(opt=opt, norm_keep=True))
+        worst = max(worst, rel_err(Ok, Ou), max(rel_err(a, b) for a, b in zip(Wk, Wu)))
     return worst
 
 
@@ -390,4 +427,8 @@ ALL_PINS = {
     "chunk1_uta_muon_mom": (lambda o: pin_chunk1(o, "update_then_apply", "muon", 0.5), 1e-10),
     "eta_zero": (lambda o: pin_eta_zero(o), 1e-12),
     "resume": (lambda o: pin_resume(o), 0.0),
+    "norm_keep_lengths": (lambda o: pin_norm_keep_lengths(o), 1e-12),
+    "norm_keep_direction": (lambda o: pin_norm_keep_direction(o), 1e-12),
+    "chunk1_atu_gd_keep": (lambda o: pin_chunk1(o, "apply_then_update", "gd", keep=True), 1e-10),
+    "chunk1_uta_muon_keep": (lambda o: pin_chunk1(o, "update_then_apply", "muon", 0.5, keep=True), 1e-10),
 }

@@ -31,6 +31,10 @@ MUTATIONS = [
     ("last chunk not updated", "W, M = update_pair(W, M, K[ks], V[ks], eta[ks], hp)",
      "W, M = update_pair(W, M, K[ks], V[ks], eta[ks], hp) if c < N - 1 else (W, M)"),
     ("step sign flipped", "W = W - step * g", "W = W + step * g"),
+    ("kept length taken after the step", "W = W * np.sqrt(np.sum(W_old * W_old, axis=1, keepdims=True))",
+     "W = W * np.sqrt(np.sum(W * W, axis=1, keepdims=True))"),
+    ("kept length squared", "W = W * np.sqrt(np.sum(W_old * W_old, axis=1, keepdims=True))",
+     "W = W * np.sum(W_old * W_old, axis=1, keepdims=True)"),
 ]
 
 
