@@ -316,8 +316,9 @@ __global__ __launch_bounds__(kNSThreads) void k_ns_generic(NSArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// W <- W - step * dir, then every row to unit L2 norm.  One wavefront per
-// row; rows of W1 and W3 have d entries, rows of W2 have h (<= 1024).
+// W <- W - step * dir, then every row to unit L2 norm (or, with norm_keep,
+// back to its length before the step).  One wavefront per row; rows of W1
+// and W3 have d entries, rows of W2 have h (<= 1024).
 // ---------------------------------------------------------------------------
 constexpr int kMaxRowPerLane = 16;
 
@@ -346,28 +347,32 @@ __global__ __launch_bounds__(kThreads) void k_step_norm(StepArgs a) {
     len = a.h;
   }
   float v[kMaxRowPerLane];
-  float ss = 0.f;
+  float ss = 0.f, ss_old = 0.f;
 #pragma unroll
   for (int k = 0; k < kMaxRowPerLane; ++k) {
     const int e = lane + 64 * k;
     v[k] = 0.f;
     if (e < len) {
-      v[k] = W[e] - a.step * dr[e];
+      const float w = W[e];
+      ss_old += w * w;
+      v[k] = w - a.step * dr[e];
       ss += v[k] * v[k];
     }
   }
   ss = wave_sum(ss);
   const float den = fmaxf(sqrtf(ss), a.norm_eps);
+  const float len_new = a.norm_keep ? sqrtf(wave_sum(ss_old)) : 1.f;
 #pragma unroll
   for (int k = 0; k < kMaxRowPerLane; ++k) {
     const int e = lane + 64 * k;
-    if (e < len) W[e] = v[k] / den;
+    if (e < len) W[e] = len_new * (v[k] / den);
   }
 }
 
 // ---------------------------------------------------------------------------
 // GD / momentum update tail, one wavefront per stored row: fixed-order sum of
-// the split partials, M <- beta M + g (when kept), W <- W - step g, unit row.
+// the split partials, M <- beta M + g (when kept), W <- W - step g, unit row
+// (or, with norm_keep, the row back to its length before the step).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void k_reduce_step(TailArgs a) {
   const int lane = threadIdx.x & 63;
@@ -404,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_step(TailArgs a) {
   const int64_t wo = pair * hd + (po % hd);  // offset of this row inside its matrix
   const float* part = a.partials + pair * a.splits * 3 * hd + po;
   float v[kMaxRowPerLane];
-  float ss = 0.f;
+  float ss = 0.f, ss_old = 0.f;
 #pragma unroll
   for (int k = 0; k < kMaxRowPerLane; ++k) {
     const int e = lane + 64 * k;
@@ -424,17 +429,20 @@ __global__ __launch_bounds__(kThreads) void k_reduce_step(TailArgs a) {
         g = a.beta * M[wo + e] + g;
         M[wo + e] = g;
       }
-      v[k] = W[wo + e] - a.step * g;
+      const float w = W[wo + e];
+      ss_old += w * w;
+      v[k] = w - a.step * g;
       ss += v[k] * v[k];
     }
   }
   ss = wave_sum(ss);
   const float den = fmaxf(sqrtf(ss), a.norm_eps);
+  const float len_new = a.norm_keep ? sqrtf(wave_sum(ss_old)) : 1.f;
 #pragma unroll
   for (int k = 0; k < kMaxRowPerLane; ++k) {
     const int e = lane + 64 * k;
     if (e < len) {
-      const float x = v[k] / den;
+      const float x = len_new * (v[k] / den);
       W[wo + e] = x;
       if (Wb != nullptr)
         Wb[pair * hd + wb_tiled(static_cast<int>((po % hd) / len), e, len)] =
@@ -487,7 +495,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_step_v4(TailArgs a, int64_t
   const int64_t sstride = 3 * hd / 4;
   const int c0 = lane % lpr;
   float4 v[4];
-  float ss = 0.f;
+  float ss = 0.f, ss_old = 0.f;
   for (int k = 0; k < cpl; ++k) {
     const int c = c0 + lpr * k;
     float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -522,6 +530,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce_step_v4(TailArgs a, int64_t
         *mp = g;
       }
       const float4 w = reinterpret_cast<const float4*>(W + wo)[c];
+      ss_old += w.x * w.x + w.y * w.y + w.z * w.z + w.w * w.w;
       g.x = w.x - a.step * g.x;
       g.y = w.y - a.step * g.y;
       g.z = w.z - a.step * g.z;
@@ -532,11 +541,13 @@ __global__ __launch_bounds__(kThreads) void k_reduce_step_v4(TailArgs a, int64_t
   }
   ss = group_sum(ss, lpr);
   const float den = fmaxf(sqrtf(ss), a.norm_eps);
+  const float len_new = a.norm_keep ? sqrtf(group_sum(ss_old, lpr)) : 1.f;
   if (live) {
     for (int k = 0; k < cpl; ++k) {
       const int c = c0 + lpr * k;
       const float4 g = v[k];
-      const float4 x = make_float4(g.x / den, g.y / den, g.z / den, g.w / den);
+      const float4 x = make_float4(len_new * (g.x / den), len_new * (g.y / den), len_new * (g.z / den),
+                                   len_new * (g.w / den));
       reinterpret_cast<float4*>(W + wo)[c] = x;
       if (Wb != nullptr) {
         bf16x4_t b;

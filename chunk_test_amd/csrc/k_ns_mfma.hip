@@ -4,7 +4,8 @@
 // orthogonalisation (Muon's transform, "LaCT: Large Chunk Test-Time
 // Training" review, section "Local attention and nonlinear memory work
 // together"; coefficients as given in the layer configuration) on bf16 MFMA
-// with split operands, then W <- W - step X and unit L2 rows (and, when
+// with split operands, then W <- W - step X and unit L2 rows (or rows back
+// to their length before the step, norm_keep) (and, when
 // asked, a bf16 copy of the new W for the next query read).
 //
 // X is the s x l orientation of the gradient (s = min(d, h), l = max(d, h)),
@@ -538,7 +539,7 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
   __syncthreads();
   // (every row's squared norm first, then all GPT group reductions together,
   // so their shuffle latencies overlap)
-  float v[GPT][4], sq[GPT];
+  float v[GPT][4], sq[GPT], sq_old[GPT];
 #pragma unroll
   for (int k = 0; k < GPT; ++k) {
     const int e = 4 * (tid + 2 * L * k);
@@ -547,6 +548,7 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
     v[k][1] = wv[k].y;
     v[k][2] = wv[k].z;
     v[k][3] = wv[k].w;
+    sq_old[k] = v[k][0] * v[k][0] + v[k][1] * v[k][1] + v[k][2] * v[k][2] + v[k][3] * v[k][3];
     sq[k] = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -558,14 +560,17 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
   const float inv_eps = 1.f / a.norm_eps;
   if (tr) {
     group_sums<S / 4>(sq);
+    if (a.norm_keep) group_sums<S / 4>(sq_old);
   } else {
     group_sums<L / 4>(sq);
+    if (a.norm_keep) group_sums<L / 4>(sq_old);
   }
 #pragma unroll
   for (int k = 0; k < GPT; ++k) {
     // 1 / max(||r||, eps) as min(1 / sqrt(||r||^2), 1 / eps), the
     // reciprocal square root from the hardware approximation (~1 ulp)
-    const float inv = fminf(__builtin_amdgcn_rsqf(sq[k]), inv_eps);
+    float inv = fminf(__builtin_amdgcn_rsqf(sq[k]), inv_eps);
+    if (a.norm_keep) inv *= sqrtf(sq_old[k]);  // back to the length before the step
     const float4 xw = make_float4(v[k][0] * inv, v[k][1] * inv, v[k][2] * inv, v[k][3] * inv);
     W4[tid + 2 * L * k] = xw;
     if (Wbm != nullptr) {

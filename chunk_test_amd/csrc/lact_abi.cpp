@@ -187,6 +187,8 @@ int check_config(const lact_config* c, Plan* p) {
     return fail(LACT_ERR_INVALID_ARG, "products %d unknown", c->products);
   if (!finite(c->norm_eps) || c->norm_eps <= 0.f)
     return fail(LACT_ERR_INVALID_ARG, "norm_eps %g must be finite and > 0", c->norm_eps);
+  if (c->norm_mode != LACT_NORM_UNIT && c->norm_mode != LACT_NORM_KEEP)
+    return fail(LACT_ERR_INVALID_ARG, "norm_mode %d unknown", c->norm_mode);
   const int mf = lact_mfma_path(c->d, c->h, c->io_dtype);
   if (mf < 0)
     return fail(LACT_ERR_UNSUPPORTED,
@@ -312,6 +314,7 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
   ta.W3 = st->W3;
   ta.step = c->step;
   ta.norm_eps = c->norm_eps;
+  ta.norm_keep = c->norm_mode == LACT_NORM_KEEP;
   ta.P = p.P;
   ta.d = p.d;
   ta.h = p.h;
@@ -416,6 +419,7 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
     a.dir = dir;
     a.step = c->step;
     a.norm_eps = c->norm_eps;
+    a.norm_keep = c->norm_mode == LACT_NORM_KEEP;
     a.P = p.P;
     a.d = p.d;
     a.h = p.h;
@@ -476,6 +480,7 @@ void lact_config_default(lact_config* c) {
   c->step = 1.f;
   c->norm_eps = 1e-12f;
   c->products = LACT_PRODUCTS_BF16;
+  c->norm_mode = LACT_NORM_UNIT;
 }
 
 int lact_mfma_path(int32_t d, int32_t h, int32_t io_dtype) {

@@ -54,6 +54,7 @@ struct TailArgs {
   float beta;
   float *W1, *W2, *W3;
   float step, norm_eps;
+  int norm_keep;          // rows back to their length before the update (else unit)
   int P, d, h, iters;
   float a, b, c, eps;     // Newton-Schulz (Muon only)
   // when non-NULL: also store the updated W1, W2, W3 rounded to bf16 (P h d
@@ -67,6 +68,7 @@ struct StepArgs {
   float *W1, *W2, *W3;
   const float* dir;  // [P, 3hd]
   float step, norm_eps;
+  int norm_keep;     // rows back to their length before the update (else unit)
   int P, d, h;
 };
 

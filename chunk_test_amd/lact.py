@@ -29,6 +29,7 @@ ORDER_CODES = {"apply_then_update": LACT_APPLY_THEN_UPDATE, "update_then_apply":
 OPT_CODES = {"gd": LACT_OPT_GD, "momentum": LACT_OPT_MOMENTUM, "muon": LACT_OPT_MUON}
 DTYPE_CODES = {"fp32": LACT_F32, "bf16": LACT_BF16}
 PRODUCT_CODES = {"bf16": 0, "split": 1}
+NORM_CODES = {"unit": 0, "keep": 1}
 
 EXPORTED = (
     "lact_config_default", "lact_workspace_bytes", "lact_update", "lact_apply",
@@ -43,6 +44,7 @@ class LactConfig(ctypes.Structure):
         ("io_dtype", c_int32), ("opt", c_int32), ("beta", c_float),
         ("ns_iters", c_int32), ("ns_a", c_float), ("ns_b", c_float), ("ns_c", c_float),
         ("ns_eps", c_float), ("step", c_float), ("norm_eps", c_float), ("products", c_int32),
+        ("norm_mode", c_int32),
     ]
 
 
@@ -123,12 +125,13 @@ class Config:
     step: float = 1.0
     norm_eps: float = 1e-12
     products: str = "bf16"
+    norm: str = "unit"  # "unit" | "keep": updated rows to unit length, or kept at their length
 
     def to_c(self) -> LactConfig:
         return LactConfig(self.B, self.H, self.d, self.h, DTYPE_CODES[self.io_dtype],
                           OPT_CODES[self.opt], self.beta, self.ns_iters, self.ns_a, self.ns_b,
                           self.ns_c, self.ns_eps, self.step, self.norm_eps,
-                          PRODUCT_CODES[self.products])
+                          PRODUCT_CODES[self.products], NORM_CODES[self.norm])
 
     def uses_momentum(self) -> bool:
         return self.opt == "momentum" or (self.opt == "muon" and self.beta > 0)

@@ -84,6 +84,18 @@ typedef enum { LACT_OPT_GD = 0, LACT_OPT_MOMENTUM = 1, LACT_OPT_MUON = 2 } lact_
  * higher cost.  Ignored in fp32 I/O mode. */
 typedef enum { LACT_PRODUCTS_BF16 = 0, LACT_PRODUCTS_SPLIT = 1 } lact_products;
 
+/* Length of the updated rows (step (4)).  LACT_NORM_UNIT: every stored row r
+ * of W1, W3 (length d) and W2 (length h) becomes r / max(||r||_2, norm_eps).
+ * LACT_NORM_KEEP: the stepped row u is rescaled to the length the row had
+ * before the update, u * ||r_old||_2 / max(||u||_2, norm_eps), so the update
+ * turns the rows and every row keeps its initial length through the scan (the
+ * direction / length split of weight normalisation, with the length held;
+ * "Weight Normalization: A Simple Reparameterization to Accelerate Training
+ * of Deep Neural Networks" is in the reference list of the "Test-Time
+ * Training Done Right" arXiv page).  Identical to LACT_NORM_UNIT for rows of
+ * unit length. */
+typedef enum { LACT_NORM_UNIT = 0, LACT_NORM_KEEP = 1 } lact_norm_mode;
+
 typedef struct {
   int32_t B, H;      /* batch and heads: P = B*H independent pairs                        */
   int32_t d, h;      /* head dim and SwiGLU hidden dim                                    */
@@ -96,6 +108,7 @@ typedef struct {
   float step;        /* W <- W - step * direction                                         */
   float norm_eps;    /* row r <- r / max(||r||_2, norm_eps)                               */
   int32_t products;  /* lact_products: how bf16-mode products treat derived operands      */
+  int32_t norm_mode; /* lact_norm_mode: rows to unit length, or kept at their length      */
 } lact_config;
 
 typedef struct {
@@ -106,7 +119,7 @@ typedef struct {
 /* Defaults: opt GD, beta 0, ns_iters 5, (a,b,c) = (3.4445, -4.7750, 2.0315)
  * (the quintic published with the Muon optimizer; the pages only name
  * Newton-Schulz), ns_eps 1e-7, step 1, norm_eps 1e-12, io_dtype LACT_BF16,
- * products LACT_PRODUCTS_BF16.
+ * products LACT_PRODUCTS_BF16, norm_mode LACT_NORM_UNIT.
  * B, H, d, h are set to 0 and must be filled in. */
 void lact_config_default(lact_config* cfg);
 

@@ -73,6 +73,7 @@ class Workload:
     io_dtype: str = "bf16"  # "fp32" | "bf16"
     seed: int = 0
     products: str = "bf16"  # "bf16" | "split": precision of derived product operands
+    norm: str = "unit"      # "unit" | "keep": updated rows to unit length or kept at their length
 
     @property
     def n_chunks(self) -> int:

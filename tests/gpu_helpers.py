@@ -33,7 +33,7 @@ def tol_of(w: S.Workload):
 def config_of(w: S.Workload):
     from chunk_test_amd import Config
     return Config(B=w.B, H=w.H, d=w.d, h=w.h, io_dtype=w.io_dtype, opt=w.opt, beta=w.beta,
-                  ns_iters=w.ns_iters, products=w.products)
+                  ns_iters=w.ns_iters, products=w.products, norm=w.norm)
 
 
 def to_dev(x, w: S.Workload, io=True):
@@ -75,7 +75,8 @@ def run_gpu(w: S.Workload, x, st_np, ws=None):
 
 def run_oracle(w: S.Workload, x, st_np, pairs=None, token_block=65536):
     import oracle
-    hp = oracle.Hyper(opt=w.opt, beta=w.beta, ns_iters=w.ns_iters, token_block=token_block)
+    hp = oracle.Hyper(opt=w.opt, beta=w.beta, ns_iters=w.ns_iters, token_block=token_block,
+                      norm_keep=w.norm == "keep")
     return oracle.lact_chunked_forward(st_np, x["Q"], x["K"], x["V"], x["eta"], w.chunk_kv,
                                        w.chunk_q, w.order, hp, pairs=pairs)
 

@@ -58,6 +58,19 @@ SMALL_CASES = [
     # bf16 at d = 128 with four 128-unit hidden slices, ragged chunks
     small("lm", name="lm-h512-ragged", B=1, H=2, h=512, T_kv=3000, T_q=600, chunk_kv=1500,
           chunk_q=300),
+    # rows kept at their length (norm_mode LACT_NORM_KEEP) through every update tail:
+    # fp32 GD / momentum (row-wise tail), fp32 Muon (step-and-normalise kernel), bf16
+    # momentum (16-byte row-group tail), bf16 Muon at d = 64 and split-product Muon at
+    # d = 128 (Newton-Schulz tails)
+    TINY.replace(name="tiny-keep", norm="keep"),
+    TINY.replace(name="tiny-muon-keep", opt="muon", norm="keep", order="update_then_apply"),
+    TINY.replace(name="fp32-d128-keep", B=1, H=2, d=128, h=256, opt="momentum", beta=0.9,
+                 norm="keep"),
+    small("lm", name="lm-keep", B=1, H=2, T_kv=4096, T_q=4096, chunk_kv=1024, chunk_q=1024,
+          norm="keep"),
+    small("posed", name="posed-keep", H=2, T_kv=16384, T_q=512, chunk_kv=16384, chunk_q=512,
+          norm="keep"),
+    small("video", name="video-keep", H=1, T_kv=2 * 4096, T_q=2 * 4096, norm="keep"),
 ]
 
 
@@ -189,6 +202,42 @@ def test_update_and_apply_entry_points_and_strided_views():
     assert np.all(O[:, :, 256:].cpu().numpy() == 0)  # nothing written past m
     for n in ("W1", "W2", "W3"):
         assert np.array_equal(dst[n].cpu().numpy(), s_scan[n]), n
+
+
+@pytest.mark.parametrize("opt,norm", [("momentum", "unit"), ("momentum", "keep"),
+                                      ("muon", "unit"), ("muon", "keep")])
+def test_unaligned_state_parity(opt, norm):
+    """Weights and momentum 4 bytes past a 16-byte boundary: the row-wise
+    tails with 4-byte accesses (GD / momentum) and the fp32-arithmetic Muon
+    path (the MFMA Muon tail needs 16-byte rows) against the oracle."""
+    import torch
+    import chunk_test_amd as L
+    w = small("lm", name=f"unaligned-{opt}-{norm}", B=1, H=2, T_kv=2048, T_q=2048, chunk_kv=1024,
+              chunk_q=1024, opt=opt, beta=0.9 if opt == "momentum" else 0.0, norm=norm)
+    G.say(f"case {w.name}")
+    st = S.gen_weights(w)
+    x = S.gen_inputs(w)
+    cfg = G.config_of(w)
+    dst = {}
+    for n in ("W1", "W2", "W3"):
+        buf = torch.zeros(st[n].size + 1, device="cuda")
+        dst[n] = buf[1:].view(st[n].shape)
+        dst[n].copy_(torch.from_numpy(st[n]))
+        assert dst[n].data_ptr() % 16 != 0
+    if cfg.uses_momentum():
+        for n in ("M1", "M2", "M3"):
+            buf = torch.zeros(dst["W" + n[1]].numel() + 1, device="cuda")
+            dst[n] = buf[1:].view(dst["W" + n[1]].shape)
+    Q, K, V = (G.to_dev(x[n], w) for n in ("Q", "K", "V"))
+    eta = G.to_dev(x["eta"], w, io=False)
+    O = torch.empty_like(Q)
+    ws = L.alloc_workspace(cfg, w.chunk_kv, w.chunk_q)
+    L.lact_chunked_forward(cfg, dst, Q, K, V, eta, O, w.chunk_kv, w.chunk_q, w.order, ws)
+    torch.cuda.synchronize()
+    s_gpu = {n: t.cpu().numpy() for n, t in dst.items()}
+    O_ref, s_ref = G.run_oracle(w, x, st)
+    _, bad = G.compare(w, O.float().cpu().numpy(), s_gpu, O_ref, s_ref)
+    assert not bad, bad
 
 
 def test_edge_sizes_one_token_one_query():
