@@ -37,6 +37,10 @@ The pages print no formulas.  The plainest reading used here:
   X0 = G / (||G||_F + eps), then I times  A = X X^T, X <- a X + (b A + c A A) X.
 * after each update every stored row r of W1, W3 (length d) and W2 (length h)
   becomes r / max(||r||_2, norm_eps).  The initial weights are not normalised.
+* variant with a learning rate per token and matrix (eta of shape [n, 3],
+  columns for W1, W2, W3): each matrix follows the gradient of the loss
+  written with its own rates, dW_m = d/dW_m (- sum_i eta_{i,m} <f_W(k_i), v_i>);
+  with three equal columns this is the shared-rate rule.
 * variant ``norm_keep`` (weight normalisation with the magnitude held: the
   reference list's "Weight Normalization" separates a row's direction from
   its length; here the update moves only the direction): the stepped row u
@@ -112,6 +116,9 @@ def swiglu_loss(W1, W2, W3, K, V, eta):
 def swiglu_grad(W1, W2, W3, K, V, eta, token_block=None):
     """Gradient of ``swiglu_loss`` with respect to (W1, W2, W3).
 
+    ``eta`` is [n] (one rate per token) or [n, 3] (a rate per token and
+    matrix: column m weights the loss whose gradient W1, W2, W3 follow).
+
     Back-propagation through f_W: with U_i = dL/df(k_i) = -eta_i v_i,
       dW2 = U^T G,  dG = U W2,  dH3 = dG * A,  dH1 = dG * H3 * silu'(H1),
       dW1 = dH1^T K,  dW3 = dH3^T K,
@@ -130,18 +137,28 @@ def swiglu_grad(W1, W2, W3, K, V, eta, token_block=None):
     dW1 = np.zeros_like(W1)
     dW2 = np.zeros_like(W2)
     dW3 = np.zeros_like(W3)
+    eta = np.asarray(eta)
     for s, e in blocks:
-        Kb, Vb, eb = K[s:e], V[s:e], eta[s:e]
+        Kb, Vb = K[s:e], V[s:e]
         H1 = Kb @ W1.T
         H3 = Kb @ W3.T
         S = sigmoid(H1)
         A = H1 * S
         G = A * H3
-        U = -eb[:, None] * Vb
-        dW2 += U.T @ G
-        dG = U @ W2
-        dH3 = dG * A
-        dH1 = dG * H3 * (S * (1.0 + H1 * (1.0 - S)))
+        dA = S * (1.0 + H1 * (1.0 - S))  # silu'(H1)
+        if eta.ndim == 1:
+            eb = eta[s:e]
+            U = -eb[:, None] * Vb
+            dW2 += U.T @ G
+            dG = U @ W2
+            dH3 = dG * A
+            dH1 = dG * H3 * dA
+        else:
+            # U_m = -eta_{i,m} v_i: the output gradient of the loss matrix m follows
+            U1, U2, U3 = (-eta[s:e, m][:, None] * Vb for m in range(3))
+            dW2 += U2.T @ G
+            dH3 = (U3 @ W2) * A
+            dH1 = (U1 @ W2) * H3 * dA
         dW1 += dH1.T @ Kb
         dW3 += dH3.T @ Kb
     return dW1, dW2, dW3
@@ -347,18 +364,26 @@ def lact_apply(state, Q, dtype=np.float64):
     return O
 
 
+def _pair_eta(eta, b, h, dtype):
+    """Rates of pair (b, h): eta [B, H, T] -> [T]; per matrix, [3, B, H, T] -> [T, 3]."""
+    if eta.ndim == 4:
+        return np.asarray(eta[:, b, h], dtype=dtype).T
+    return np.asarray(eta[b, h], dtype=dtype)
+
+
 def lact_update(state, K, V, eta, hp: Hyper, dtype=np.float64):
-    """One update of every pair on one chunk.  Returns a new state dict."""
+    """One update of every pair on one chunk.  Returns a new state dict.
+    ``eta`` is [B, H, T], or [3, B, H, T] for a rate per token and matrix."""
     K = np.asarray(K, dtype=dtype)
     V = np.asarray(V, dtype=dtype)
-    eta = np.asarray(eta, dtype=dtype)
+    eta = np.asarray(eta)
     B, H = K.shape[:2]
     new = {k: np.array(v, dtype=dtype, copy=True) for k, v in state.items()}
     for b, h in _pairs(B, H):
         W = tuple(new[n][b, h] for n in ("W1", "W2", "W3"))
         M = (tuple(new[n][b, h] for n in ("M1", "M2", "M3"))
              if hp.uses_momentum() and "M1" in new else None)
-        W, M = update_pair(W, M, K[b, h], V[b, h], eta[b, h], hp)
+        W, M = update_pair(W, M, K[b, h], V[b, h], _pair_eta(eta, b, h, dtype), hp)
         for n, x in zip(("W1", "W2", "W3"), W):
             new[n][b, h] = x
         if M is not None:
@@ -374,6 +399,7 @@ def lact_chunked_forward(state, Q, K, V, eta, chunk_kv, chunk_q, order, hp: Hype
     ``pairs`` optionally restricts the work to a list of (b, h) pairs (the
     other outputs stay zero and their state is copied unchanged); the pairs
     are independent, so this is how large configurations are sampled.
+    ``eta`` is [B, H, T_kv], or [3, B, H, T_kv] for a rate per token and matrix.
     """
     B, H = K.shape[:2]
     new = {k: np.array(v, dtype=dtype, copy=True) for k, v in state.items()}
@@ -388,8 +414,9 @@ def lact_chunked_forward(state, Q, K, V, eta, chunk_kv, chunk_q, order, hp: Hype
         W = tuple(new[n][b, h] for n in ("W1", "W2", "W3"))
         M = (tuple(new[n][b, h] for n in ("M1", "M2", "M3"))
              if hp.uses_momentum() else None)
-        O[b, h], W, M = chunked_forward_pair(W, M, cast(Q), cast(K), cast(V), cast(eta),
-                                             chunk_kv, chunk_q, order, hp)
+        O[b, h], W, M = chunked_forward_pair(W, M, cast(Q), cast(K), cast(V),
+                                             _pair_eta(eta, b, h, dtype), chunk_kv, chunk_q,
+                                             order, hp)
         for n, x in zip(("W1", "W2", "W3"), W):
             new[n][b, h] = x
         if M is not None:

@@ -391,6 +391,36 @@ def pin_norm_keep_direction(o, seed=14):
     return worst
 
 
+def pin_eta_per_matrix_columns(o, seed=15, d=16, h=32, n=64):
+    """A rate per token and matrix: each matrix's gradient equals the shared-rate
+    gradient computed with that matrix's column of rates."""
+    r = rng(seed)
+    W = rand_weights(r, d, h)
+    K, V = r.normal(size=(n, d)), r.normal(size=(n, d))
+    E = np.abs(r.normal(size=(n, 3)))
+    g = o.swiglu_grad(*W, K, V, E, token_block=17)
+    return max(rel_err(g[m], o.swiglu_grad(*W, K, V, E[:, m])[m]) for m in range(3))
+
+
+def pin_eta_per_matrix_special(o, seed=16):
+    """Three equal columns reproduce the shared-rate scan; a zero column for W2
+    leaves W2 at its normalised initial value while W1 and W3 move (batched
+    entry point, [3, B, H, T] rates)."""
+    W, Q, K, V, eta = _small_problem(seed)
+    hp = o.Hyper(opt="muon")
+    st = {n: x[None, None] for n, x in zip(("W1", "W2", "W3"), W)}
+    Q4, K4, V4 = (x[None, None] for x in (Q, K, V))
+    O_s, S_s = o.lact_chunked_forward(st, Q4, K4, V4, eta[None, None], 8, 8, "apply_then_update", hp)
+    E3 = np.stack([eta, eta, eta])[:, None, None]
+    O_p, S_p = o.lact_chunked_forward(st, Q4, K4, V4, E3, 8, 8, "apply_then_update", hp)
+    worst = max(rel_err(O_p, O_s), max(rel_err(S_p[n], S_s[n]) for n in ("W1", "W2", "W3")))
+    E3 = np.stack([eta, np.zeros_like(eta), eta])[:, None, None]
+    _, S_z = o.lact_chunked_forward(st, Q4, K4, V4, E3, 8, 8, "apply_then_update", hp)
+    worst = max(worst, rel_err(S_z["W2"][0, 0], unit_rows(W[1])))
+    moved = min(rel_err(S_z[n][0, 0], unit_rows(x)) for n, x in (("W1", W[0]), ("W3", W[2])))
+    return worst if moved > 1e-3 else float("inf")
+
+
 def pin_resume(o, seed=12):
     """Chunks [0, k) then [k, N) with the state handed over == one run."""
     W, Q, K, V, eta = _small_problem(seed, T=48)
@@ -428,6 +458,8 @@ ALL_PINS = {
     "eta_zero": (lambda o: pin_eta_zero(o), 1e-12),
     "resume": (lambda o: pin_resume(o), 0.0),
     "norm_keep_lengths": (lambda o: pin_norm_keep_lengths(o), 1e-12),
+    "eta_per_matrix_columns": (lambda o: pin_eta_per_matrix_columns(o), 1e-12),
+    "eta_per_matrix_special": (lambda o: pin_eta_per_matrix_special(o), 1e-12),
     "norm_keep_direction": (lambda o: pin_norm_keep_direction(o), 1e-12),
     "chunk1_atu_gd_keep": (lambda o: pin_chunk1(o, "apply_then_update", "gd", keep=True), 1e-10),
     "chunk1_uta_muon_keep": (lambda o: pin_chunk1(o, "update_then_apply", "muon", 0.5, keep=True), 1e-10),

@@ -33,6 +33,12 @@ MUTATIONS = [
     ("step sign flipped", "W = W - step * g", "W = W + step * g"),
     ("kept length taken after the step", "W = W * np.sqrt(np.sum(W_old * W_old, axis=1, keepdims=True))",
      "W = W * np.sqrt(np.sum(W * W, axis=1, keepdims=True))"),
+    ("per-matrix rates of W1 and W3 swapped",
+     "U1, U2, U3 = (-eta[s:e, m][:, None] * Vb for m in range(3))",
+     "U3, U2, U1 = (-eta[s:e, m][:, None] * Vb for m in range(3))"),
+    ("per-matrix W2 follows the W1 rates",
+     "U1, U2, U3 = (-eta[s:e, m][:, None] * Vb for m in range(3))",
+     "U1, U2, U3 = (-eta[s:e, m][:, None] * Vb for m in (0, 0, 2))"),
     ("kept length squared", "W = W * np.sqrt(np.sum(W_old * W_old, axis=1, keepdims=True))",
      "W = W * np.sum(W_old * W_old, axis=1, keepdims=True)"),
 ]
