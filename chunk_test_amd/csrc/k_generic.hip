@@ -24,9 +24,11 @@ constexpr int kHS = 32;   // hidden units per workgroup
 //   h1 = k.W1[j], h3 = k.W3[j], dg = u.W2[:, j]  (u = -eta v)
 //   a = silu(h1), g = a h3, dh3 = dg a, dh1 = dg h3 silu'(h1)
 //   dW1[j] += dh1 k,  dW3[j] += dh3 k,  dW2[:, j] += g u.
-// Tokens past the split end load as zero and contribute nothing.
+// Tokens past the split end load as zero and contribute nothing.  PM: a rate
+// per token and matrix (rows for W1, W2, W3, a.eta_mat elements apart): u = v
+// is staged unscaled, dg of W1 / W3 takes -eta1 / -eta3 and g takes -eta2.
 // ---------------------------------------------------------------------------
-template <bool BF16, int D>
+template <bool BF16, int D, bool PM>
 __global__ __launch_bounds__(kThreads) void k_grad_generic(GradArgs a) {
   constexpr int NACC = 3 * kHS * D / kThreads;
   __shared__ float sW1[kHS][D + 1];
@@ -37,6 +39,7 @@ __global__ __launch_bounds__(kThreads) void k_grad_generic(GradArgs a) {
   __shared__ float sdh1[kTok][kHS + 1];
   __shared__ float sdh3[kTok][kHS + 1];
   __shared__ float sg[kTok][kHS + 1];
+  __shared__ float sE[PM ? 3 : 1][kTok];  // with PM: -eta of W1, W2, W3 per token
 
   const int split = blockIdx.x;
   const int j0 = blockIdx.y * kHS;
@@ -75,10 +78,17 @@ __global__ __launch_bounds__(kThreads) void k_grad_generic(GradArgs a) {
       float kv = 0.f, u = 0.f;
       if (tok < t_end) {
         kv = load_io<BF16>(a.K, kv_base + tok * D + e);
-        u = -eta[tok] * load_io<BF16>(a.V, kv_base + tok * D + e);
+        u = (PM ? 1.f : -eta[tok]) * load_io<BF16>(a.V, kv_base + tok * D + e);
       }
       sK[t][e] = kv;
       sU[t][e] = u;
+    }
+    if constexpr (PM) {
+      for (int i = tid; i < 3 * kTok; i += kThreads) {
+        const int m = i / kTok, t = i % kTok;
+        const int64_t tok = t0 + t;
+        sE[m][t] = tok < t_end ? -eta[m * a.eta_mat + tok] : 0.f;
+      }
     }
     __syncthreads();
     {
@@ -96,9 +106,15 @@ __global__ __launch_bounds__(kThreads) void k_grad_generic(GradArgs a) {
         }
         const float s = sigmoid_f(h1);
         const float act = h1 * s;
-        sg[t][jj] = act * h3;
-        sdh3[t][jj] = dg * act;
-        sdh1[t][jj] = dg * h3 * (s * (1.f + h1 * (1.f - s)));
+        float dg1 = dg, dg3 = dg, gv = act * h3;
+        if constexpr (PM) {
+          dg1 = sE[0][t] * dg;
+          gv = sE[1][t] * gv;
+          dg3 = sE[2][t] * dg;
+        }
+        sg[t][jj] = gv;
+        sdh3[t][jj] = dg3 * act;
+        sdh1[t][jj] = dg1 * h3 * (s * (1.f + h1 * (1.f - s)));
       }
     }
     __syncthreads();
@@ -628,9 +644,17 @@ template <int D>
 hipError_t grad_d(const GradArgs& a, hipStream_t s) {
   dim3 grid(a.S, a.h / kHS, a.P);
   if (a.bf16) {
-    hipLaunchKernelGGL((k_grad_generic<true, D>), grid, dim3(kThreads), 0, s, a);
+    if (a.eta_mat != 0) {
+      hipLaunchKernelGGL((k_grad_generic<true, D, true>), grid, dim3(kThreads), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((k_grad_generic<true, D, false>), grid, dim3(kThreads), 0, s, a);
+    }
   } else {
-    hipLaunchKernelGGL((k_grad_generic<false, D>), grid, dim3(kThreads), 0, s, a);
+    if (a.eta_mat != 0) {
+      hipLaunchKernelGGL((k_grad_generic<false, D, true>), grid, dim3(kThreads), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((k_grad_generic<false, D, false>), grid, dim3(kThreads), 0, s, a);
+    }
   }
   return hipGetLastError();
 }

@@ -48,15 +48,16 @@ constexpr int ROW = 2 * D;    // bytes per token row (sixteen 16-byte chunks)
 constexpr float kNegLog2e = -1.4426950408889634f;
 constexpr float kNegLn2 = -0.6931471805599453f;
 
-template <bool SPLIT>
+template <bool SPLIT, bool PM>
 struct Geo {
   static constexpr int TT = SPLIT ? 64 : 128;  // tokens per LDS stage
   static constexpr int SUB = TT / 32;
   static constexpr int TILE = TT * ROW;
+  static constexpr int NE = PM ? 3 : 1;        // rows of rates per stage (W1, W2, W3 with PM)
   static constexpr int OFF_K = 0;              // K[2]
   static constexpr int OFF_V = 2 * TILE;       // V[2]
-  static constexpr int OFF_E = 4 * TILE;       // eta[2]
-  static constexpr int OFF_WLO = 4 * TILE + 2 * TT * 4;  // W1_lo, W3_lo operands (split)
+  static constexpr int OFF_E = 4 * TILE;       // eta[2][NE][TT]
+  static constexpr int OFF_WLO = 4 * TILE + 2 * NE * TT * 4;  // W1_lo, W3_lo operands (split)
   static constexpr int WLO_BYTES = SPLIT ? 2 * 4 * KS * 64 * 16 : 0;
   static constexpr int LDS = OFF_WLO + WLO_BYTES;
 };
@@ -85,10 +86,12 @@ __device__ __forceinline__ __bf16 lo_bf16(float x, __bf16 hi) {
   return static_cast<__bf16>(x - static_cast<float>(hi));
 }
 
-template <bool SPLIT>
+// PM: a learning rate per token and matrix (rows of rates for W1, W2, W3,
+// a.eta_mat elements apart); otherwise one rate per token.
+template <bool SPLIT, bool PM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_grad_d128(GradArgs a, int hsl, int nbase) {
-  using G = Geo<SPLIT>;
+  using G = Geo<SPLIT, PM>;
   __shared__ __attribute__((aligned(16))) unsigned char lds[G::LDS];
 
   // XCD-aware block order: the hidden slices of one (pair, split) land on
@@ -189,13 +192,21 @@ void k_grad_d128(GradArgs a, int hsl, int nbase) {
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Kg + off), (lds_ptr_t)(lds + G::OFF_K + b * G::TILE + 1024 * piece), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Vg + off), (lds_ptr_t)(lds + G::OFF_V + b * G::TILE + 1024 * piece), 16, 0, 0);
     }
-    if (wv < G::TT / 64) {
-      const int tok = static_cast<int>(t0) + 64 * wv + lane;
-      if (tok <= t_last) {
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(etag + static_cast<unsigned>(tok)),
-                                         (lds_ptr_t)(lds + G::OFF_E + b * G::TT * 4 + 256 * wv), 4, 0, 0);
-      } else {
-        *reinterpret_cast<float*>(lds + G::OFF_E + b * G::TT * 4 + 256 * wv + 4 * lane) = 0.f;
+    // rates: pieces of 64 (matrix piece / (TT / 64), tokens 64 (piece % (TT / 64)) ..),
+    // wave wv moving pieces wv and wv + 4
+    constexpr int HPM = G::TT / 64;  // pieces per row of rates
+#pragma unroll
+    for (int pc = 0; pc < 2; ++pc) {
+      const int piece = wv + 4 * pc;
+      if (piece < G::NE * HPM) {
+        const int tok = static_cast<int>(t0) + 64 * (piece % HPM) + lane;
+        const float* src = etag + (PM ? (piece / HPM) * a.eta_mat : 0);
+        unsigned char* dst = lds + G::OFF_E + b * G::NE * G::TT * 4 + 256 * piece;
+        if (tok <= t_last) {
+          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + static_cast<unsigned>(tok)), (lds_ptr_t)dst, 4, 0, 0);
+        } else {
+          *reinterpret_cast<float*>(dst + 4 * lane) = 0.f;
+        }
       }
     }
   };
@@ -235,7 +246,8 @@ void k_grad_d128(GradArgs a, int hsl, int nbase) {
 
     const unsigned char* kb = lds + G::OFF_K + b * G::TILE;
     const unsigned char* vb = lds + G::OFF_V + b * G::TILE;
-    const float* eb = reinterpret_cast<const float*>(lds + G::OFF_E + b * G::TT * 4);
+    // rates of this stage (with PM rows for W1, W2, W3)
+    const float* eb = reinterpret_cast<const float*>(lds + G::OFF_E + b * G::NE * G::TT * 4);
 
 #pragma unroll 1
     for (int st = 0; st < G::SUB; ++st) {
@@ -263,10 +275,12 @@ void k_grad_d128(GradArgs a, int hsl, int nbase) {
         }
       }
       // eta of this lane's 16 tokens (operand slot i of half s <-> token
-      // 16 s + 8 (i / 4) + 4 g + i % 4)
+      // 16 s + 8 (i / 4) + 4 g + i % 4); with PM the rates of W2 (read per
+      // half below, with those of W1 and W3)
       f32x4_t eta4[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) eta4[q] = *reinterpret_cast<const f32x4_t*>(eb + 32 * st + 8 * q + 4 * g);
+      for (int q = 0; q < 4; ++q)
+        eta4[q] = *reinterpret_cast<const f32x4_t*>(eb + (PM ? G::TT : 0) + 32 * st + 8 * q + 4 * g);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8_t ak = SPLIT ? kv_row(ks, false) : akv[SPLIT ? 0 : ks];
@@ -288,6 +302,14 @@ void k_grad_d128(GradArgs a, int hsl, int nbase) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const f32x4_t e0 = eta4[2 * s], e1 = eta4[2 * s + 1];
+        // with PM: rates of W1 (x1) and W3 (x3) for the same slots
+        f32x4_t x10, x11, x30, x31;
+        if constexpr (PM) {
+          x10 = *reinterpret_cast<const f32x4_t*>(eb + 32 * st + 16 * s + 4 * g);
+          x11 = *reinterpret_cast<const f32x4_t*>(eb + 32 * st + 16 * s + 8 + 4 * g);
+          x30 = *reinterpret_cast<const f32x4_t*>(eb + 2 * G::TT + 32 * st + 16 * s + 4 * g);
+          x31 = *reinterpret_cast<const f32x4_t*>(eb + 2 * G::TT + 32 * st + 16 * s + 8 + 4 * g);
+        }
         // token-side operands: slots 0-3 <-> tokens 16 s + 4 g + k',
         // slots 4-7 <-> tokens 16 s + 8 + 4 g + k' (bf16 products: read
         // before the elementwise step, which hides their latency)
@@ -314,12 +336,16 @@ void k_grad_d128(GradArgs a, int hsl, int nbase) {
         for (int i = 0; i < 8; ++i) {
           const int r = 8 * s + i;
           const float ne = -((i < 4) ? e0[i & 3] : e1[i & 3]);
-          const float z = c1[r], h3 = c3[r], dg = ne * cg[r];
+          const float z = c1[r], h3 = c3[r];
+          // dG of the losses W1 and W3 follow (the same one without PM)
+          const float dg = ne * cg[r];
+          const float dg1 = PM ? -((i < 4) ? x10[i & 3] : x11[i & 3]) * cg[r] : dg;
+          const float dg3 = PM ? -((i < 4) ? x30[i & 3] : x31[i & 3]) * cg[r] : dg;
           const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(z));
           const float act = z * sg;
           const float gs = act * h3;
           const float t = fmaf(h3, kNegLog2e, -gs);
-          const float vg = ne * gs, v3 = dg * act, v1 = dg * fmaf(sg, t, gs);
+          const float vg = ne * gs, v3 = dg3 * act, v1 = dg1 * fmaf(sg, t, gs);
           pg[i] = static_cast<__bf16>(vg);
           pd3[i] = static_cast<__bf16>(v3);
           pd1[i] = static_cast<__bf16>(v1);
@@ -366,17 +392,22 @@ bool grad_d128_shape_ok(int d, int h) {
   return d == D && h % kHidPerWG == 0 && h >= kHidPerWG && h <= 1024;
 }
 
-int grad_d128_stage_tokens(bool split) { return split ? Geo<true>::TT : Geo<false>::TT; }
+int grad_d128_stage_tokens(bool split) { return split ? Geo<true, false>::TT : Geo<false, false>::TT; }
 
 hipError_t launch_grad_d128(const GradArgs& a, bool split, hipStream_t s) {
   if (a.d != D) return hipErrorInvalidValue;
   const int hsl = a.h / kHidPerWG;
   const int nbase = a.S * a.P;
   const int blocks = ((nbase + 7) / 8) * 8 * hsl;
-  if (split) {
-    hipLaunchKernelGGL(k_grad_d128<true>, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  const bool pm = a.eta_mat != 0;
+  if (split && pm) {
+    hipLaunchKernelGGL((k_grad_d128<true, true>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  } else if (split) {
+    hipLaunchKernelGGL((k_grad_d128<true, false>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  } else if (pm) {
+    hipLaunchKernelGGL((k_grad_d128<false, true>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
   } else {
-    hipLaunchKernelGGL(k_grad_d128<false>, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+    hipLaunchKernelGGL((k_grad_d128<false, false>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
   }
   return hipGetLastError();
 }

@@ -55,8 +55,9 @@ constexpr int TILE = TT * ROW;       // one stage of K (or V)
 // and puts no wait for the in-flight loads before them)
 constexpr int OFF_K = 0;
 constexpr int OFF_V = TILE;
-constexpr int OFF_E = 2 * TILE;
-constexpr int BUF_BYTES = 2 * TILE + TT * 4;
+constexpr int OFF_E = 2 * TILE;  // eta: one row of TT rates, or three (W1, W2, W3)
+template <bool PM>
+constexpr int buf_bytes() { return 2 * TILE + (PM ? 3 : 1) * TT * 4; }
 
 // W1 enters pre-scaled by -log2(e) (sigmoid(h1) = 1 / (1 + 2^z), z = -log2(e) h1);
 // G, dH3 and dH1 then carry that factor, removed at the end (times -ln 2).
@@ -87,10 +88,13 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// PM: a learning rate per token and matrix (rows of rates for W1, W2, W3,
+// a.eta_mat elements apart); otherwise one rate per token.
+template <bool PM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_grad_d64(GradArgs a, int hsl, int nbase) {
-  __shared__ __attribute__((aligned(16))) unsigned char buf0[BUF_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char buf1[BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char buf0[buf_bytes<PM>()];
+  __shared__ __attribute__((aligned(16))) unsigned char buf1[buf_bytes<PM>()];
 
   // XCD-aware block order: the hidden slices of one (pair, split) land on
   // the same XCD (block ids congruent mod 8) so their key/value reads share L2.
@@ -156,7 +160,8 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
   // DMA of one stage into buffer b: wave wv moves rows 32 wv .. 32 wv + 31
   // of K and V (four 1 KiB pieces each; lane l of piece k lands at byte 16 l
   // of it: row 8 (4 wv + k) + l / 8, physical chunk l % 8) and waves 0, 1
-  // move 64 eta values each.  Rows past the end re-read the split's last
+  // move 64 eta values each (with PM waves wv and wv + 4 < 6 move rates
+  // 64 (wv % 2) .. of matrix wv / 2).  Rows past the end re-read the split's last
   // token (finite values); their eta is written as 0 instead of loaded, so
   // they add nothing to the sums.
   auto dma_stage = [&](int64_t t0, unsigned char* dst) {
@@ -175,13 +180,18 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Kg + off), (lds_ptr_t)(dst + OFF_K + 1024 * piece), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Vg + off), (lds_ptr_t)(dst + OFF_V + 1024 * piece), 16, 0, 0);
     }
-    if (wv < 2) {
-      const int tok = static_cast<int>(t0) + 64 * wv + lane;
-      if (tok <= t_last) {
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(etag + static_cast<unsigned>(tok)),
-                                         (lds_ptr_t)(dst + OFF_E + 256 * wv), 4, 0, 0);
-      } else {
-        *reinterpret_cast<float*>(dst + OFF_E + 256 * wv + 4 * lane) = 0.f;
+#pragma unroll
+    for (int pc = 0; pc < (PM ? 2 : 1); ++pc) {
+      const int piece = wv + 4 * pc;  // 64 rates: matrix piece / 2, tokens 64 (piece % 2) ..
+      if (piece < (PM ? 6 : 2)) {
+        const int tok = static_cast<int>(t0) + 64 * (piece & 1) + lane;
+        const float* src = etag + (PM ? (piece >> 1) * a.eta_mat : 0);
+        if (tok <= t_last) {
+          __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src + static_cast<unsigned>(tok)),
+                                           (lds_ptr_t)(dst + OFF_E + 256 * piece), 4, 0, 0);
+        } else {
+          *reinterpret_cast<float*>(dst + OFF_E + 256 * piece + 4 * lane) = 0.f;
+        }
       }
     }
   };
@@ -244,10 +254,12 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
         av[ks] = *reinterpret_cast<const bf16x8_t*>(vb + off);
       }
       // eta of this lane's 16 tokens (operand slot i of half s <-> token
-      // 16 s + 8 (i / 4) + 4 g + i % 4)
+      // 16 s + 8 (i / 4) + 4 g + i % 4); with PM the rates of W2 (read per
+      // half below, with those of W1 and W3)
       f32x4_t eta4[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) eta4[q] = *reinterpret_cast<const f32x4_t*>(eb + 32 * st + 8 * q + 4 * g);
+      for (int q = 0; q < 4; ++q)
+        eta4[q] = *reinterpret_cast<const f32x4_t*>(eb + (PM ? TT : 0) + 32 * st + 8 * q + 4 * g);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         c1 = mfma32(ak[ks], w1b[ks], c1);
@@ -265,6 +277,14 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const f32x4_t e0 = eta4[2 * s], e1 = eta4[2 * s + 1];
+        // with PM: rates of W1 (x1) and W3 (x3) for the same slots
+        f32x4_t x10, x11, x30, x31;
+        if constexpr (PM) {
+          x10 = *reinterpret_cast<const f32x4_t*>(eb + 32 * st + 16 * s + 4 * g);
+          x11 = *reinterpret_cast<const f32x4_t*>(eb + 32 * st + 16 * s + 8 + 4 * g);
+          x30 = *reinterpret_cast<const f32x4_t*>(eb + 2 * TT + 32 * st + 16 * s + 4 * g);
+          x31 = *reinterpret_cast<const f32x4_t*>(eb + 2 * TT + 32 * st + 16 * s + 8 + 4 * g);
+        }
         // token-side operands: slots 0-3 <-> tokens 16 s + 4 g + k',
         // slots 4-7 <-> tokens 16 s + 8 + 4 g + k' (read before the
         // elementwise step, which hides their latency)
@@ -286,14 +306,18 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
         for (int i = 0; i < 8; ++i) {
           const int r = 8 * s + i;
           const float ne = -((i < 4) ? e0[i & 3] : e1[i & 3]);
-          const float z = c1[r], h3 = c3[r], dg = ne * cg[r];
+          const float z = c1[r], h3 = c3[r];
+          // dG of the losses W1 and W3 follow (the same one without PM)
+          const float dg = ne * cg[r];
+          const float dg1 = PM ? -((i < 4) ? x10[i & 3] : x11[i & 3]) * cg[r] : dg;
+          const float dg3 = PM ? -((i < 4) ? x30[i & 3] : x31[i & 3]) * cg[r] : dg;
           const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(z));
           const float act = z * sg;
           const float gs = act * h3;
           pg[i] = static_cast<__bf16>(ne * gs);
-          pd3[i] = static_cast<__bf16>(dg * act);
+          pd3[i] = static_cast<__bf16>(dg3 * act);
           const float t = fmaf(h3, kNegLog2e, -gs);
-          pd1[i] = static_cast<__bf16>(dg * fmaf(sg, t, gs));
+          pd1[i] = static_cast<__bf16>(dg1 * fmaf(sg, t, gs));
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
@@ -338,7 +362,11 @@ hipError_t launch_grad_d64(const GradArgs& a, hipStream_t s) {
   const int hsl = a.h / kHidPerWG;
   const int nbase = a.S * a.P;
   const int blocks = ((nbase + 7) / 8) * 8 * hsl;
-  hipLaunchKernelGGL(k_grad_d64, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  if (a.eta_mat != 0) {
+    hipLaunchKernelGGL(k_grad_d64<true>, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  } else {
+    hipLaunchKernelGGL(k_grad_d64<false>, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  }
   return hipGetLastError();
 }
 

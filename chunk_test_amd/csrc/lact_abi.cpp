@@ -189,6 +189,8 @@ int check_config(const lact_config* c, Plan* p) {
     return fail(LACT_ERR_INVALID_ARG, "norm_eps %g must be finite and > 0", c->norm_eps);
   if (c->norm_mode != LACT_NORM_UNIT && c->norm_mode != LACT_NORM_KEEP)
     return fail(LACT_ERR_INVALID_ARG, "norm_mode %d unknown", c->norm_mode);
+  if (c->eta_mode != LACT_ETA_SHARED && c->eta_mode != LACT_ETA_PER_MATRIX)
+    return fail(LACT_ERR_INVALID_ARG, "eta_mode %d unknown", c->eta_mode);
   const int mf = lact_mfma_path(c->d, c->h, c->io_dtype);
   if (mf < 0)
     return fail(LACT_ERR_UNSUPPORTED,
@@ -283,6 +285,8 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
     g.n = n;
     g.kv_stride = kv_stride;
     g.eta_stride = eta_stride;
+    // per-matrix rates: three blocks of P pairs each
+    g.eta_mat = c->eta_mode == LACT_ETA_PER_MATRIX ? static_cast<int64_t>(p.P) * eta_stride : 0;
     g.W1 = st->W1;
     g.W2 = st->W2;
     g.W3 = st->W3;
@@ -481,6 +485,7 @@ void lact_config_default(lact_config* c) {
   c->norm_eps = 1e-12f;
   c->products = LACT_PRODUCTS_BF16;
   c->norm_mode = LACT_NORM_UNIT;
+  c->eta_mode = LACT_ETA_SHARED;
 }
 
 int lact_mfma_path(int32_t d, int32_t h, int32_t io_dtype) {

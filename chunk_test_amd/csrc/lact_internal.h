@@ -17,6 +17,7 @@ struct GradArgs {
   int64_t n;           // keys in the chunk
   int64_t kv_stride;   // elements between pairs in K and V
   int64_t eta_stride;  // elements between pairs in eta
+  int64_t eta_mat;     // elements between the rates of W1, W2, W3 (0: one rate per token)
   const float* W1;     // [P, h, d]
   const float* W2;     // [P, d, h]
   const float* W3;     // [P, h, d]

@@ -44,7 +44,7 @@ class LactConfig(ctypes.Structure):
         ("io_dtype", c_int32), ("opt", c_int32), ("beta", c_float),
         ("ns_iters", c_int32), ("ns_a", c_float), ("ns_b", c_float), ("ns_c", c_float),
         ("ns_eps", c_float), ("step", c_float), ("norm_eps", c_float), ("products", c_int32),
-        ("norm_mode", c_int32),
+        ("norm_mode", c_int32), ("eta_mode", c_int32),
     ]
 
 
@@ -126,12 +126,14 @@ class Config:
     norm_eps: float = 1e-12
     products: str = "bf16"
     norm: str = "unit"  # "unit" | "keep": updated rows to unit length, or kept at their length
+    eta_per_matrix: bool = False  # rates [3,B,H,T]: one per token and matrix (W1, W2, W3)
 
     def to_c(self) -> LactConfig:
         return LactConfig(self.B, self.H, self.d, self.h, DTYPE_CODES[self.io_dtype],
                           OPT_CODES[self.opt], self.beta, self.ns_iters, self.ns_a, self.ns_b,
                           self.ns_c, self.ns_eps, self.step, self.norm_eps,
-                          PRODUCT_CODES[self.products], NORM_CODES[self.norm])
+                          PRODUCT_CODES[self.products], NORM_CODES[self.norm],
+                          1 if self.eta_per_matrix else 0)
 
     def uses_momentum(self) -> bool:
         return self.opt == "momentum" or (self.opt == "muon" and self.beta > 0)
@@ -197,18 +199,26 @@ def alloc_workspace(cfg: Config, max_chunk_kv: int, max_chunk_q: int, device="cu
                        device=device)
 
 
+def _check_eta(cfg: Config, eta, K):
+    import torch
+    _check_tensor("eta", eta, torch.float32)
+    want = (3,) + tuple(K.shape[:2]) if cfg.eta_per_matrix else tuple(K.shape[:2])
+    if tuple(eta.shape[:-1]) != want:
+        raise ValueError(f"eta of shape {tuple(eta.shape)}: leading dims {want} expected")
+
+
 def lact_update(cfg: Config, st: dict, K, V, eta, ws, stream=None, n=None,
                 kv_stride_bh=None, eta_stride_bh=None):
-    """One update on chunk tensors K, V [B,H,n,d] and eta [B,H,n] (in place on st)."""
-    import torch
+    """One update on chunk tensors K, V [B,H,n,d] and eta [B,H,n] (per matrix:
+    [3,B,H,n]) (in place on st)."""
     lib = load_library()
     _check_state(cfg, st)
     _check_tensor("K", K, _io_dtype(cfg))
     _check_tensor("V", V, _io_dtype(cfg))
-    _check_tensor("eta", eta, torch.float32)
+    _check_eta(cfg, eta, K)
     n = K.shape[2] if n is None else n
     kv_stride_bh = K.shape[2] * cfg.d if kv_stride_bh is None else kv_stride_bh
-    eta_stride_bh = eta.shape[2] if eta_stride_bh is None else eta_stride_bh
+    eta_stride_bh = eta.shape[-1] if eta_stride_bh is None else eta_stride_bh
     c, s = cfg.to_c(), _state(st)
     _check(lib.lact_update(ctypes.byref(c), ctypes.byref(s), _ptr(K), _ptr(V), _ptr(eta), n,
                            kv_stride_bh, eta_stride_bh, _ptr(ws), ws.numel(), _stream(stream)))
@@ -229,13 +239,13 @@ def lact_apply(cfg: Config, st: dict, Q, O, ws=None, stream=None, m=None, q_stri
 
 def lact_chunked_forward(cfg: Config, st: dict, Q, K, V, eta, O, chunk_kv: int, chunk_q: int,
                          order: str, ws, stream=None):
-    """The whole layer over contiguous [B,H,T,d] tensors (state updated in place)."""
-    import torch
+    """The whole layer over contiguous [B,H,T,d] tensors and eta [B,H,T_kv] (per
+    matrix: [3,B,H,T_kv]) (state updated in place)."""
     lib = load_library()
     _check_state(cfg, st)
     for name, t in (("Q", Q), ("K", K), ("V", V), ("O", O)):
         _check_tensor(name, t, _io_dtype(cfg))
-    _check_tensor("eta", eta, torch.float32)
+    _check_eta(cfg, eta, K)
     c, s = cfg.to_c(), _state(st)
     _check(lib.lact_chunked_forward(ctypes.byref(c), ctypes.byref(s), _ptr(Q), _ptr(K), _ptr(V),
                                     _ptr(eta), _ptr(O), K.shape[2], Q.shape[2], chunk_kv, chunk_q,

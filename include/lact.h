@@ -96,6 +96,17 @@ typedef enum { LACT_PRODUCTS_BF16 = 0, LACT_PRODUCTS_SPLIT = 1 } lact_products;
  * unit length. */
 typedef enum { LACT_NORM_UNIT = 0, LACT_NORM_KEEP = 1 } lact_norm_mode;
 
+/* Learning rates.  LACT_ETA_SHARED: one rate eta_i per token, shared by W1,
+ * W2 and W3 (the loss of step (2)).  LACT_ETA_PER_MATRIX: three rates per
+ * token, and each matrix follows the gradient of the loss written with its
+ * own rates: dW_m = d/dW_m (-sum_i eta_{i,m} <f_W(k_i), v_i>), m = W1, W2,
+ * W3.  The rates are then three blocks laid out like the shared ones, W1's
+ * first: the rate of matrix m, pair p, token t sits at
+ * eta[m * P * eta_stride_bh + p * eta_stride_bh + t] (P = B*H), i.e. a
+ * [3, B, H, T] array for lact_chunked_forward.  Three equal blocks give the
+ * shared-rate result. */
+typedef enum { LACT_ETA_SHARED = 0, LACT_ETA_PER_MATRIX = 1 } lact_eta_mode;
+
 typedef struct {
   int32_t B, H;      /* batch and heads: P = B*H independent pairs                        */
   int32_t d, h;      /* head dim and SwiGLU hidden dim                                    */
@@ -109,6 +120,7 @@ typedef struct {
   float norm_eps;    /* row r <- r / max(||r||_2, norm_eps)                               */
   int32_t products;  /* lact_products: how bf16-mode products treat derived operands      */
   int32_t norm_mode; /* lact_norm_mode: rows to unit length, or kept at their length      */
+  int32_t eta_mode;  /* lact_eta_mode: one rate per token, or one per token and matrix    */
 } lact_config;
 
 typedef struct {
@@ -119,7 +131,7 @@ typedef struct {
 /* Defaults: opt GD, beta 0, ns_iters 5, (a,b,c) = (3.4445, -4.7750, 2.0315)
  * (the quintic published with the Muon optimizer; the pages only name
  * Newton-Schulz), ns_eps 1e-7, step 1, norm_eps 1e-12, io_dtype LACT_BF16,
- * products LACT_PRODUCTS_BF16, norm_mode LACT_NORM_UNIT.
+ * products LACT_PRODUCTS_BF16, norm_mode LACT_NORM_UNIT, eta_mode LACT_ETA_SHARED.
  * B, H, d, h are set to 0 and must be filled in. */
 void lact_config_default(lact_config* cfg);
 
@@ -131,8 +143,8 @@ size_t lact_workspace_bytes(const lact_config* cfg, int64_t max_chunk_kv, int64_
 
 /* One large-chunk update of every pair: steps (2)-(4) above on n keys.
  * K, V: pair p's rows start at K + p*kv_stride_bh (elements); eta: pair p
- * starts at eta + p*eta_stride_bh.  n >= 1 (any n: ragged tails are
- * handled).  The state is read and written. */
+ * starts at eta + p*eta_stride_bh (per matrix: see lact_eta_mode).  n >= 1
+ * (any n: ragged tails are handled).  The state is read and written. */
 int lact_update(const lact_config* cfg, const lact_state* st,
                 const void* K, const void* V, const float* eta,
                 int64_t n, int64_t kv_stride_bh, int64_t eta_stride_bh,

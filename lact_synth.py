@@ -29,7 +29,8 @@ import dataclasses
 
 import numpy as np
 
-TENSOR_IDS = {"W1": 0, "W3": 1, "W2": 2, "Q": 3, "K": 4, "V": 5, "eta": 6}
+TENSOR_IDS = {"W1": 0, "W3": 1, "W2": 2, "Q": 3, "K": 4, "V": 5, "eta": 6,
+              "eta_W1": 7, "eta_W2": 8, "eta_W3": 9}
 
 
 def block_rng(seed: int, tensor: str, b: int, h: int) -> np.random.Generator:
@@ -74,6 +75,7 @@ class Workload:
     seed: int = 0
     products: str = "bf16"  # "bf16" | "split": precision of derived product operands
     norm: str = "unit"      # "unit" | "keep": updated rows to unit length or kept at their length
+    eta_per_matrix: bool = False  # rates [3,B,H,T_kv]: one per token and matrix (W1, W2, W3)
 
     @property
     def n_chunks(self) -> int:
@@ -156,13 +158,14 @@ def gen_tokens_block(w: Workload, tensor: str, b: int, hh: int, rows: int) -> np
     return x
 
 
-def gen_eta_block(w: Workload, b: int, hh: int, rows: int) -> np.ndarray:
-    z = block_rng(w.seed, "eta", b, hh).standard_normal(rows)
+def gen_eta_block(w: Workload, b: int, hh: int, rows: int, tensor: str = "eta") -> np.ndarray:
+    z = block_rng(w.seed, tensor, b, hh).standard_normal(rows)
     return (0.01 * np.logaddexp(0.0, z)).astype(np.float32)
 
 
 def gen_inputs(w: Workload, heads=None, batches=None):
-    """All inputs as float32 numpy arrays [B,H,T,d] (eta [B,H,T_kv]).
+    """All inputs as float32 numpy arrays [B,H,T,d] (eta [B,H,T_kv], or
+    [3,B,H,T_kv] with a rate per token and matrix: three independent draws).
 
     ``heads`` / ``batches`` optionally restrict generation to some blocks
     (the others are left zero) so that large workloads can be sampled.
@@ -172,11 +175,15 @@ def gen_inputs(w: Workload, heads=None, batches=None):
     Q = np.zeros((w.B, w.H, w.T_q, w.d), np.float32)
     K = np.zeros((w.B, w.H, w.T_kv, w.d), np.float32)
     V = np.zeros((w.B, w.H, w.T_kv, w.d), np.float32)
-    eta = np.zeros((w.B, w.H, w.T_kv), np.float32)
+    eta = np.zeros(((3,) if w.eta_per_matrix else ()) + (w.B, w.H, w.T_kv), np.float32)
     for b in bs:
         for hh in hs:
             Q[b, hh] = gen_tokens_block(w, "Q", b, hh, w.T_q)
             K[b, hh] = gen_tokens_block(w, "K", b, hh, w.T_kv)
             V[b, hh] = gen_tokens_block(w, "V", b, hh, w.T_kv)
-            eta[b, hh] = gen_eta_block(w, b, hh, w.T_kv)
+            if w.eta_per_matrix:
+                for m, t in enumerate(("eta_W1", "eta_W2", "eta_W3")):
+                    eta[m, b, hh] = gen_eta_block(w, b, hh, w.T_kv, t)
+            else:
+                eta[b, hh] = gen_eta_block(w, b, hh, w.T_kv)
     return {"Q": Q, "K": K, "V": V, "eta": eta}

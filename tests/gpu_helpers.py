@@ -33,7 +33,8 @@ def tol_of(w: S.Workload):
 def config_of(w: S.Workload):
     from chunk_test_amd import Config
     return Config(B=w.B, H=w.H, d=w.d, h=w.h, io_dtype=w.io_dtype, opt=w.opt, beta=w.beta,
-                  ns_iters=w.ns_iters, products=w.products, norm=w.norm)
+                  ns_iters=w.ns_iters, products=w.products, norm=w.norm,
+                  eta_per_matrix=w.eta_per_matrix)
 
 
 def to_dev(x, w: S.Workload, io=True):

@@ -71,6 +71,18 @@ SMALL_CASES = [
     small("posed", name="posed-keep", H=2, T_kv=16384, T_q=512, chunk_kv=16384, chunk_q=512,
           norm="keep"),
     small("video", name="video-keep", H=1, T_kv=2 * 4096, T_q=2 * 4096, norm="keep"),
+    # a learning rate per token and matrix (eta_mode LACT_ETA_PER_MATRIX), in every gradient
+    # kernel: fp32 generic (d = 64 and 128), bf16 MFMA at d = 64, bf16 and split-product MFMA
+    # at d = 128; ragged chunks for the stage logic
+    TINY.replace(name="tiny-eta3", eta_per_matrix=True, opt="momentum", beta=0.9),
+    TINY.replace(name="fp32-d128-eta3", B=1, H=2, d=128, h=256, opt="muon", eta_per_matrix=True),
+    small("posed", name="posed-eta3", H=2, T_kv=16384, T_q=512, chunk_kv=16384, chunk_q=512,
+          eta_per_matrix=True),
+    small("posed", name="posed-eta3-ragged", H=3, T_kv=3000, T_q=210, chunk_kv=1000, chunk_q=70,
+          opt="momentum", beta=0.9, eta_per_matrix=True),
+    small("lm", name="lm-eta3", B=1, H=2, T_kv=3000, T_q=3000, chunk_kv=1500, chunk_q=1500,
+          eta_per_matrix=True),
+    small("video", name="video-eta3", H=1, T_kv=2 * 4096, T_q=2 * 4096, eta_per_matrix=True),
 ]
 
 
