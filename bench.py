@@ -61,7 +61,8 @@ def cpu_baseline(w: S.Workload, x, st, budget_s: float = 15.0):
     """The float32 oracle on a bounded sample: whole pairs of the workload,
     as many as fit the time budget (at least one)."""
     import oracle
-    hp = oracle.Hyper(opt=w.opt, beta=w.beta, ns_iters=w.ns_iters, token_block=65536)
+    hp = oracle.Hyper(opt=w.opt, beta=w.beta, ns_iters=w.ns_iters, token_block=65536,
+                      norm_keep=w.norm == "keep")
     per_pair = w.flops() / w.pairs
     done, t_used, pairs = 0, 0.0, []
     for b in range(w.B):
@@ -94,6 +95,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="posed", choices=sorted(S.WORKLOADS))
+    ap.add_argument("--norm", default="unit", choices=("unit", "keep"),
+                    help="variant: updated rows to unit length (default) or kept at their length")
+    ap.add_argument("--eta-per-matrix", action="store_true",
+                    help="variant: a learning rate per token and matrix (W1, W2, W3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -110,12 +115,19 @@ def main():
     import chunk_test_amd as L
 
     w = S.WORKLOADS[args.workload]
+    if args.norm != "unit" or args.eta_per_matrix:
+        # a variant of the workload (its own name: the committed counter
+        # summaries belong to the plain workloads)
+        w = w.replace(name=w.name + ("-keep" if args.norm == "keep" else "")
+                      + ("-eta3" if args.eta_per_matrix else ""),
+                      norm=args.norm, eta_per_matrix=args.eta_per_matrix)
     log(f"[bench] workload {w.name}: generating inputs")
     st = S.gen_weights(w)
     x = S.gen_inputs(w)
     io = torch.bfloat16 if w.io_dtype == "bf16" else torch.float32
     cfg = L.Config(B=w.B, H=w.H, d=w.d, h=w.h, io_dtype=w.io_dtype, opt=w.opt, beta=w.beta,
-                   ns_iters=w.ns_iters, products=w.products)
+                   ns_iters=w.ns_iters, products=w.products, norm=w.norm,
+                   eta_per_matrix=w.eta_per_matrix)
     dev = {n: torch.from_numpy(st[n]).cuda() for n in ("W1", "W2", "W3")}
     if cfg.uses_momentum():
         for n in ("M1", "M2", "M3"):
@@ -193,7 +205,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "d": w.d, "h": w.h,
                    "T_kv": w.T_kv, "T_q": w.T_q, "chunk_kv": w.chunk_kv, "chunk_q": w.chunk_q,
                    "order": w.order, "opt": w.opt, "beta": w.beta, "ns_iters": w.ns_iters,
-                   "products": w.products,
+                   "products": w.products, "norm": w.norm, "eta_per_matrix": w.eta_per_matrix,
                    "mfma_path": L.mfma_path(w.d, w.h, w.io_dtype)},
         "tokens_per_s": round(w.B * w.T_kv / (ms * 1e-3), 1),
         "query_tokens_per_s": round(w.B * w.T_q / (ms * 1e-3), 1),
