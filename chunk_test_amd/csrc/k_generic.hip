@@ -209,25 +209,24 @@ __global__ __launch_bounds__(kThreads) void k_reduce_v4(ReduceArgs a) {
   const int64_t pair = i / per4, e4 = i % per4;
   const float4* src = reinterpret_cast<const float4*>(a.partials) + pair * a.S * per4 + e4;
   float4 g = make_float4(0.f, 0.f, 0.f, 0.f);
-  int s = 0;
-  for (; s + 8 <= a.S; s += 8) {  // eight 16-byte loads in flight, summed in split order
-    float4 t[8];
+  // the splits in rounds of 16: every load of a round is issued before the
+  // first add (the last round masked), and the adds run in split order
+  constexpr int U = 16;
+  for (int s = 0; s < a.S; s += U) {
+    float4 t[U];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) t[u] = src[static_cast<int64_t>(s + u) * per4];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      g.x += t[u].x;
-      g.y += t[u].y;
-      g.z += t[u].z;
-      g.w += t[u].w;
+    for (int u = 0; u < U; ++u) {
+      if (s + u < a.S) t[u] = src[static_cast<int64_t>(s + u) * per4];
     }
-  }
-  for (; s < a.S; ++s) {
-    const float4 t = src[static_cast<int64_t>(s) * per4];
-    g.x += t.x;
-    g.y += t.y;
-    g.z += t.z;
-    g.w += t.w;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s + u < a.S) {
+        g.x += t[u].x;
+        g.y += t[u].y;
+        g.z += t[u].z;
+        g.w += t[u].w;
+      }
+    }
   }
   if (a.M1 != nullptr) {
     const int64_t e = 4 * e4;
