@@ -201,10 +201,10 @@ def alloc_workspace(cfg: Config, max_chunk_kv: int, max_chunk_q: int, device="cu
 
 def _check_eta(cfg: Config, eta, K):
     import torch
-    _check_tensor("eta", eta, torch.float32)
     want = (3,) + tuple(K.shape[:2]) if cfg.eta_per_matrix else tuple(K.shape[:2])
-    if tuple(eta.shape[:-1]) != want:
+    if eta is not None and tuple(eta.shape[:-1]) != want:
         raise ValueError(f"eta of shape {tuple(eta.shape)}: leading dims {want} expected")
+    _check_tensor("eta", eta, torch.float32)
 
 
 def lact_update(cfg: Config, st: dict, K, V, eta, ws, stream=None, n=None,

@@ -140,3 +140,26 @@ def test_products_mode_validation():
                            1 << 30, None) == B.LACT_ERR_INVALID_ARG
     assert "products" in lib.lact_last_error().decode()
     assert L.workspace_bytes(L.Config(1, 1, 64, 128, products="split"), 128, 128) > 0
+
+
+@pytest.mark.parametrize("field", ["norm_mode", "eta_mode"])
+def test_variant_mode_validation(field):
+    lib = L.load_library()
+    c = L.Config(1, 1, 64, 128).to_c()
+    setattr(c, field, 5)
+    assert lib.lact_workspace_bytes(ctypes.byref(c), 128, 128) == 0
+    s = B.LactState(256, 256, 256, None, None, None)
+    assert lib.lact_update(ctypes.byref(c), ctypes.byref(s), 256, 256, 256, 16, 16 * 64, 16, 256,
+                           1 << 30, None) == B.LACT_ERR_INVALID_ARG
+    assert field in lib.lact_last_error().decode()
+    ok = L.Config(1, 1, 64, 128, norm="keep", eta_per_matrix=True)
+    assert L.workspace_bytes(ok, 128, 128) > 0
+
+
+def test_binding_checks_the_rate_shape():
+    import torch
+    K = torch.zeros(1, 2, 16, 64)
+    for per_matrix, bad in ((True, (1, 2, 16)), (False, (3, 1, 2, 16))):
+        cfg = L.Config(1, 2, 64, 128, eta_per_matrix=per_matrix)
+        with pytest.raises(ValueError, match="leading dims"):
+            B._check_eta(cfg, torch.zeros(bad), K)
