@@ -254,12 +254,13 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
         av[ks] = *reinterpret_cast<const bf16x8_t*>(vb + off);
       }
       // eta of this lane's 16 tokens (operand slot i of half s <-> token
-      // 16 s + 8 (i / 4) + 4 g + i % 4); with PM the rates of W2 (read per
-      // half below, with those of W1 and W3)
-      f32x4_t eta4[4];
+      // 16 s + 8 (i / 4) + 4 g + i % 4); with PM all rates are read per half
+      // below
+      f32x4_t eta4[PM ? 1 : 4];
+      if constexpr (!PM) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        eta4[q] = *reinterpret_cast<const f32x4_t*>(eb + (PM ? TT : 0) + 32 * st + 8 * q + 4 * g);
+        for (int q = 0; q < 4; ++q) eta4[q] = *reinterpret_cast<const f32x4_t*>(eb + 32 * st + 8 * q + 4 * g);
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         c1 = mfma32(ak[ks], w1b[ks], c1);
@@ -276,10 +277,15 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
       // and the contraction with v takes e g'.
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const f32x4_t e0 = eta4[2 * s], e1 = eta4[2 * s + 1];
-        // with PM: rates of W1 (x1) and W3 (x3) for the same slots
-        f32x4_t x10, x11, x30, x31;
-        if constexpr (PM) {
+        // with PM: rates of W2 (e), W1 (x1) and W3 (x3) for the half's slots,
+        // read here (registers are short before the projections)
+        f32x4_t e0, e1, x10, x11, x30, x31;
+        if constexpr (!PM) {
+          e0 = eta4[2 * s];
+          e1 = eta4[2 * s + 1];
+        } else {
+          e0 = *reinterpret_cast<const f32x4_t*>(eb + TT + 32 * st + 16 * s + 4 * g);
+          e1 = *reinterpret_cast<const f32x4_t*>(eb + TT + 32 * st + 16 * s + 8 + 4 * g);
           x10 = *reinterpret_cast<const f32x4_t*>(eb + 32 * st + 16 * s + 4 * g);
           x11 = *reinterpret_cast<const f32x4_t*>(eb + 32 * st + 16 * s + 8 + 4 * g);
           x30 = *reinterpret_cast<const f32x4_t*>(eb + 2 * TT + 32 * st + 16 * s + 4 * g);
