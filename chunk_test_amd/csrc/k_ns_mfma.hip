@@ -4,9 +4,10 @@
 // orthogonalisation (Muon's transform, "LaCT: Large Chunk Test-Time
 // Training" review, section "Local attention and nonlinear memory work
 // together"; coefficients as given in the layer configuration) on bf16 MFMA
-// with split operands, then W <- W - step X and unit L2 rows (or rows back
-// to their length before the step, norm_keep) (and, when
-// asked, a bf16 copy of the new W for the next query read).
+// with split operands, then W <- W - step X and the row normalisation (unit
+// rows, or with norm_keep every row back to its length before the step) and,
+// when asked, a bf16 copy of the new W for the next query read (in the
+// operand order of wb_tiled).
 //
 // X is the s x l orientation of the gradient (s = min(d, h), l = max(d, h)),
 // X0 = G / (||G||_F + eps), then `iters` times
@@ -20,7 +21,8 @@
 // Work split: wave w owns CT tiles of 32 columns of X, in registers in the
 // MFMA output layout (fp32 between steps; during a step only as packed
 // hi / lo bf16 pairs, and X <- a X + B X takes X as hi + lo, which is as
-// precise as the products).  That layout is directly the B operand of B X
+// precise as the products; at s = 64, l = 128 the fp32 X stays live, see
+// NSGeo::PRE).  That layout is directly the B operand of B X
 // (16 rows of X per k-step), so only two LDS layouts are needed: X
 // row-major (for X X^T, written once per iteration) and the symmetric s x s
 // matrices A and then B (written as the transpose of their own output
