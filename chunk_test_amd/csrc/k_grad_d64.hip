@@ -76,14 +76,6 @@ constexpr float kNegLn2 = -0.6931471805599453f;
 // different halves of the row.  Both read kinds are free of bank conflicts.
 __device__ __forceinline__ int swz(int r) { return 4 * (((r >> 1) ^ (r >> 3)) & 1) + 2 * ((r >> 2) & 1) + ((r >> 1) & 1); }
 
-__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-  bf16x2_t v;
-  v[0] = static_cast<__bf16>(lo);
-  v[1] = static_cast<__bf16>(hi);
-  return __builtin_bit_cast(unsigned, v);
-}
-
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
