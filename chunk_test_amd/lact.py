@@ -155,7 +155,9 @@ def _stream(stream):
     return c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def _check_tensor(name, t, dtype, device=None):
+def _check_tensor(name, t, dtype, device=None, rows_only=False):
+    """Device tensor of the given dtype, contiguous (with rows_only: only its
+    last dimension dense, for views addressed through explicit strides)."""
     import torch
     if t is None:
         raise ValueError(f"{name} is None")
@@ -163,7 +165,7 @@ def _check_tensor(name, t, dtype, device=None):
         raise ValueError(f"{name} must be a device tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
-    if not t.is_contiguous():
+    if not (t.stride(-1) == 1 if rows_only else t.is_contiguous()):
         raise ValueError(f"{name} must be contiguous")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
@@ -199,26 +201,40 @@ def alloc_workspace(cfg: Config, max_chunk_kv: int, max_chunk_q: int, device="cu
                        device=device)
 
 
-def _check_eta(cfg: Config, eta, K):
+def _check_eta(cfg: Config, eta, K, rows_only=False):
     import torch
     want = (3,) + tuple(K.shape[:2]) if cfg.eta_per_matrix else tuple(K.shape[:2])
     if eta is not None and tuple(eta.shape[:-1]) != want:
         raise ValueError(f"eta of shape {tuple(eta.shape)}: leading dims {want} expected")
-    _check_tensor("eta", eta, torch.float32)
+    _check_tensor("eta", eta, torch.float32, rows_only=rows_only)
 
 
 def lact_update(cfg: Config, st: dict, K, V, eta, ws, stream=None, n=None,
                 kv_stride_bh=None, eta_stride_bh=None):
     """One update on chunk tensors K, V [B,H,n,d] and eta [B,H,n] (per matrix:
-    [3,B,H,n]) (in place on st)."""
+    [3,B,H,n]) (in place on st).  With explicit strides the tensors may be
+    views into longer sequences (rows dense, pairs and rate blocks at the
+    given strides)."""
     lib = load_library()
     _check_state(cfg, st)
-    _check_tensor("K", K, _io_dtype(cfg))
-    _check_tensor("V", V, _io_dtype(cfg))
-    _check_eta(cfg, eta, K)
+    views = kv_stride_bh is not None or eta_stride_bh is not None
+    _check_tensor("K", K, _io_dtype(cfg), rows_only=views)
+    _check_tensor("V", V, _io_dtype(cfg), rows_only=views)
+    _check_eta(cfg, eta, K, rows_only=views)
     n = K.shape[2] if n is None else n
     kv_stride_bh = K.shape[2] * cfg.d if kv_stride_bh is None else kv_stride_bh
     eta_stride_bh = eta.shape[-1] if eta_stride_bh is None else eta_stride_bh
+    if views:
+        # the strides the library is given must be the views' own
+        for name, t, inner, ps in (("K", K, cfg.d, kv_stride_bh), ("V", V, cfg.d, kv_stride_bh)):
+            if t.stride(2) != inner or t.stride(1) != ps or t.stride(0) != t.shape[1] * ps:
+                raise ValueError(f"{name}: strides {t.stride()} do not match kv_stride_bh={ps}")
+        lead = eta.dim() - 3  # 1 with a rate block per matrix
+        if (eta.stride(-2) != eta_stride_bh or eta.stride(-3) != eta.shape[-2] * eta_stride_bh
+                or (lead and eta.stride(0) != eta.shape[1] * eta.shape[2] * eta_stride_bh)):
+            raise ValueError(f"eta: strides {eta.stride()} do not match eta_stride_bh={eta_stride_bh}")
+        if n > K.shape[2] or n > eta.shape[-1]:
+            raise ValueError(f"n={n} beyond the views ({K.shape[2]} keys, {eta.shape[-1]} rates)")
     c, s = cfg.to_c(), _state(st)
     _check(lib.lact_update(ctypes.byref(c), ctypes.byref(s), _ptr(K), _ptr(V), _ptr(eta), n,
                            kv_stride_bh, eta_stride_bh, _ptr(ws), ws.numel(), _stream(stream)))

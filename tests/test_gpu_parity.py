@@ -216,6 +216,39 @@ def test_update_and_apply_entry_points_and_strided_views():
         assert np.array_equal(dst[n].cpu().numpy(), s_scan[n]), n
 
 
+def test_per_matrix_rates_on_chunk_views_match_the_scan():
+    """lact_update on views into one [3, B, H, T] rate tensor (pair stride T,
+    the three blocks B*H*T apart) gives the scan's result bit for bit."""
+    import torch
+    import chunk_test_amd as L
+    w = small("posed", name="eta3-views", H=2, T_kv=2 * 4096, T_q=2 * 256, chunk_kv=4096,
+              chunk_q=256, eta_per_matrix=True, opt="momentum", beta=0.9,
+              order="apply_then_update")
+    st = S.gen_weights(w)
+    x = S.gen_inputs(w)
+    O_scan, s_scan = G.run_gpu(w, x, st)
+    cfg = G.config_of(w)
+    dst = G.device_state(w, st)
+    Q, K, V = (G.to_dev(x[n], w) for n in ("Q", "K", "V"))
+    eta = G.to_dev(x["eta"], w, io=False)  # [3, B, H, T_kv]
+    ws = L.alloc_workspace(cfg, w.chunk_kv, w.chunk_q)
+    O = torch.empty_like(Q)
+    for c in range(2):
+        qs = slice(c * w.chunk_q, (c + 1) * w.chunk_q)
+        q = Q[:, :, qs].contiguous()
+        o = torch.empty_like(q)
+        L.lact_apply(cfg, dst, q, o, ws=ws)
+        O[:, :, qs] = o
+        # strided views: keys/values and rates of chunk c inside the full tensors
+        off = c * w.chunk_kv
+        L.lact_update(cfg, dst, K[:, :, off:], V[:, :, off:], eta[..., off:], ws, n=w.chunk_kv,
+                      kv_stride_bh=w.T_kv * w.d, eta_stride_bh=w.T_kv)
+    torch.cuda.synchronize()
+    assert np.array_equal(O.float().cpu().numpy(), O_scan)
+    for n in ("W1", "W2", "W3", "M1", "M2", "M3"):
+        assert np.array_equal(dst[n].cpu().numpy(), s_scan[n]), n
+
+
 @pytest.mark.parametrize("opt,norm", [("momentum", "unit"), ("momentum", "keep"),
                                       ("muon", "unit"), ("muon", "keep")])
 def test_unaligned_state_parity(opt, norm):
