@@ -97,6 +97,39 @@ def test_small_parity(w):
     assert not bad, bad
 
 
+def random_case(seed):
+    """A seeded draw over the supported shapes and options (sizes small enough for
+    the oracle): head dim, hidden width, I/O type, optimizer, order, ragged chunk
+    sizes and the two variants.  bf16 Muon gets chunks of at least 1,000 keys
+    (shorter bf16 Muon chunks are ill-conditioned, see the tiny-chunk case)."""
+    r = np.random.default_rng(1000 + seed)
+    d = int(r.choice([32, 64, 128]))
+    h = int(r.choice([32, 64, 96, 128, 160, 256, 384]))
+    io = str(r.choice(["fp32", "bf16"]))
+    opt = str(r.choice(["gd", "momentum", "muon"]))
+    n_chunks = int(r.integers(1, 4))
+    chunk_kv = int(r.integers(1000 if (io == "bf16" and opt == "muon") else 40, 1600))
+    chunk_q = int(r.integers(1, 300))
+    return TINY.replace(
+        name=f"random-{seed}", B=int(r.integers(1, 3)), H=int(r.integers(1, 3)), d=d, h=h,
+        io_dtype=io, opt=opt, beta=float(r.choice([0.0, 0.5, 0.9])) if opt != "gd" else 0.0,
+        order=str(r.choice(["apply_then_update", "update_then_apply"])),
+        T_kv=n_chunks * chunk_kv, chunk_kv=chunk_kv, T_q=n_chunks * chunk_q, chunk_q=chunk_q,
+        norm=str(r.choice(["unit", "keep"])), eta_per_matrix=bool(r.integers(0, 2)), seed=seed)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_config_parity(seed):
+    w = random_case(seed)
+    G.say(f"case {w}")
+    st = S.gen_weights(w)
+    x = S.gen_inputs(w)
+    O, st_gpu = G.run_gpu(w, x, st)
+    O_ref, st_ref = G.run_oracle(w, x, st)
+    _, bad = G.compare(w, O, st_gpu, O_ref, st_ref)
+    assert not bad, bad
+
+
 FULL = [
     ("posed", [(0, 0), (0, 7)]),
     ("million", [(0, 3)]),
