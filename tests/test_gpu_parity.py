@@ -131,16 +131,20 @@ def test_random_config_parity(seed):
 
 
 FULL = [
-    ("posed", [(0, 0), (0, 7)]),
-    ("million", [(0, 3)]),
-    ("lm", [(0, 0), (5, 3)]),
-    ("video", [(0, 0), (0, 39)]),
+    ("posed", [(0, 0), (0, 7)], {}),
+    ("million", [(0, 3)], {}),
+    ("lm", [(0, 0), (5, 3)], {}),
+    ("video", [(0, 0), (0, 39)], {}),
+    # the variants at full size
+    ("posed", [(0, 5)], {"eta_per_matrix": True}),
+    ("lm", [(2, 6)], {"norm": "keep"}),
 ]
 
 
-@pytest.mark.parametrize("name,pairs", FULL, ids=[f[0] for f in FULL])
-def test_full_size_sampled_parity(name, pairs):
-    w = S.WORKLOADS[name]
+@pytest.mark.parametrize("name,pairs,variant", FULL,
+                         ids=[f[0] + "".join(f"-{k}" for k in f[2]) for f in FULL])
+def test_full_size_sampled_parity(name, pairs, variant):
+    w = S.WORKLOADS[name].replace(**variant)
     G.say(f"case {name} full size, oracle pairs {pairs}")
     st = S.gen_weights(w)
     x = S.gen_inputs(w)
@@ -148,10 +152,11 @@ def test_full_size_sampled_parity(name, pairs):
     O_ref, st_ref = G.run_oracle(w, x, st, pairs=pairs)
     _, bad = G.compare(w, O, st_gpu, O_ref, st_ref, pairs=pairs)
     assert not bad, bad
-    # properties that hold for every pair: unit rows, finite outputs
+    # properties that hold for every pair: unit rows (or the initial lengths), finite outputs
     for n in ("W1", "W2", "W3"):
         norms = np.linalg.norm(st_gpu[n], axis=-1)
-        assert np.max(np.abs(norms - 1.0)) < 1e-4, n
+        want = np.linalg.norm(st[n], axis=-1) if w.norm == "keep" else 1.0
+        assert np.max(np.abs(norms - want)) < 1e-4, n
     assert np.all(np.isfinite(O))
 
 
