@@ -183,7 +183,8 @@ int check_config(const lact_config* c, Plan* p) {
       return fail(LACT_ERR_INVALID_ARG, "Newton-Schulz coefficients must be finite, eps >= 0");
   }
   if (!finite(c->step)) return fail(LACT_ERR_INVALID_ARG, "step must be finite");
-  if (c->products != LACT_PRODUCTS_BF16 && c->products != LACT_PRODUCTS_SPLIT)
+  if (c->products != LACT_PRODUCTS_BF16 && c->products != LACT_PRODUCTS_SPLIT &&
+      c->products != LACT_PRODUCTS_AUTO)
     return fail(LACT_ERR_INVALID_ARG, "products %d unknown", c->products);
   if (!finite(c->norm_eps) || c->norm_eps <= 0.f)
     return fail(LACT_ERR_INVALID_ARG, "norm_eps %g must be finite and > 0", c->norm_eps);
@@ -207,6 +208,40 @@ int check_config(const lact_config* c, Plan* p) {
   return LACT_OK;
 }
 
+// bf16 operand products under Muon.  Newton-Schulz maps every singular value
+// of the gradient towards one, so operand rounding that moves the small
+// singular directions moves the update as much as the large ones: on chunks
+// of ~100 keys bf16 operands alone change the result by ~7e-2, and over a scan
+// the change compounds by ~1.4x per chunk (3e-3 after one chunk of 4096
+// keys, 1.5e-2 after five, 0.25 after fourteen).  Inside these limits bf16
+// products stay within 2e-2 of the exact result; outside them AUTO keeps the
+// derived operands split and an explicit request for bf16 is refused.
+constexpr int64_t kMuonBf16MinKeys = 1024;
+constexpr int64_t kMuonBf16MaxChunks = 4;
+
+// Settles the product precision of a run of `chunks` chunks of `n` keys.
+int resolve_products(const lact_config* c, Plan* p, int64_t n, int64_t chunks) {
+  if (!p->bf16) {
+    p->split = false;
+    return LACT_OK;
+  }
+  const bool bf16_ok = !p->muon || (n >= kMuonBf16MinKeys && chunks <= kMuonBf16MaxChunks);
+  if (c->products == LACT_PRODUCTS_SPLIT) {
+    p->split = true;
+  } else if (c->products == LACT_PRODUCTS_AUTO) {
+    p->split = !bf16_ok;
+  } else if (!bf16_ok) {
+    return fail(LACT_ERR_UNSUPPORTED,
+                "bf16 operand products with Muon need chunks of >= %lld keys and at most %lld chunks "
+                "(got %lld keys x %lld chunks): use LACT_PRODUCTS_SPLIT or LACT_PRODUCTS_AUTO",
+                (long long)kMuonBf16MinKeys, (long long)kMuonBf16MaxChunks, (long long)n,
+                (long long)chunks);
+  } else {
+    p->split = false;
+  }
+  return LACT_OK;
+}
+
 int check_state(const Plan& p, const lact_state* st, bool need_m) {
   if (st == nullptr) return fail(LACT_ERR_INVALID_ARG, "state is NULL");
   if (!st->W1 || !st->W2 || !st->W3) return fail(LACT_ERR_INVALID_ARG, "W1, W2, W3 must be non-NULL");
@@ -226,11 +261,16 @@ WsLayout ws_layout(const Plan& p, int64_t max_chunk_kv) {
   const size_t per = static_cast<size_t>(3) * p.h * p.d;
   const int64_t n = max_chunk_kv < 1 ? 1 : max_chunk_kv;
   // every kernel the update may pick for up to n tokens
+  // (for either product precision: AUTO settles it per call)
   int64_t S = split_bound(generic_rule(p), n);
-  const GradChoice k = grad_choice(p, true, 0);
-  if (k.kind != GradKind::Generic) {
-    const int64_t sm = split_bound(mfma_rule(p, k), n);
-    if (sm > S) S = sm;
+  for (int split = 0; split < 2; ++split) {
+    Plan q = p;
+    q.split = q.bf16 && split;
+    const GradChoice k = grad_choice(q, true, 0);
+    if (k.kind != GradKind::Generic) {
+      const int64_t sm = split_bound(mfma_rule(q, k), n);
+      if (sm > S) S = sm;
+    }
   }
   size_t off = 0;
   w.partials = off;
@@ -483,7 +523,7 @@ void lact_config_default(lact_config* c) {
   c->ns_eps = 1e-7f;
   c->step = 1.f;
   c->norm_eps = 1e-12f;
-  c->products = LACT_PRODUCTS_BF16;
+  c->products = LACT_PRODUCTS_AUTO;
   c->norm_mode = LACT_NORM_UNIT;
   c->eta_mode = LACT_ETA_SHARED;
 }
@@ -514,6 +554,7 @@ int lact_update(const lact_config* cfg, const lact_state* st, const void* K, con
   if (kv_stride_bh < n * p.d)
     return fail(LACT_ERR_INVALID_ARG, "kv_stride_bh %lld below n*d", (long long)kv_stride_bh);
   if (eta_stride_bh < n) return fail(LACT_ERR_INVALID_ARG, "eta_stride_bh %lld below n", (long long)eta_stride_bh);
+  if ((rc = resolve_products(cfg, &p, n, 1))) return rc;
   WsLayout L;
   if ((rc = check_ws(p, n, ws, ws_bytes, &L))) return rc;
   return run_update(cfg, p, st, K, V, eta, n, kv_stride_bh, eta_stride_bh, static_cast<char*>(ws), L,
@@ -556,6 +597,7 @@ int lact_chunked_forward(const lact_config* cfg, const lact_state* st, const voi
                 (long long)(T_q / chunk_q));
   if (order != LACT_APPLY_THEN_UPDATE && order != LACT_UPDATE_THEN_APPLY)
     return fail(LACT_ERR_INVALID_ARG, "order %d unknown", order);
+  if ((rc = resolve_products(cfg, &p, chunk_kv, N))) return rc;
   WsLayout L;
   if ((rc = check_ws(p, chunk_kv, ws, ws_bytes, &L))) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);

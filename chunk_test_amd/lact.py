@@ -28,7 +28,7 @@ PROFILE_PHASES = ("gradient", "tail", "newton_schulz", "step_norm", "apply")
 ORDER_CODES = {"apply_then_update": LACT_APPLY_THEN_UPDATE, "update_then_apply": LACT_UPDATE_THEN_APPLY}
 OPT_CODES = {"gd": LACT_OPT_GD, "momentum": LACT_OPT_MOMENTUM, "muon": LACT_OPT_MUON}
 DTYPE_CODES = {"fp32": LACT_F32, "bf16": LACT_BF16}
-PRODUCT_CODES = {"bf16": 0, "split": 1}
+PRODUCT_CODES = {"bf16": 0, "split": 1, "auto": 2}
 NORM_CODES = {"unit": 0, "keep": 1}
 
 EXPORTED = (
@@ -124,7 +124,7 @@ class Config:
     ns_eps: float = 1e-7
     step: float = 1.0
     norm_eps: float = 1e-12
-    products: str = "bf16"
+    products: str = "auto"  # "auto" | "bf16" | "split" (lact_products)
     norm: str = "unit"  # "unit" | "keep": updated rows to unit length, or kept at their length
     eta_per_matrix: bool = False  # rates [3,B,H,T]: one per token and matrix (W1, W2, W3)
 
@@ -171,18 +171,50 @@ def _check_tensor(name, t, dtype, device=None, rows_only=False):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _check_shape(name, t, want, min_last=None):
+    """t.shape == want; with min_last, the token axis (the last of eta, -2 of
+    the [B,H,T,d] tensors) may instead hold any length >= min_last (views
+    into longer sequences)."""
+    if t is None:
+        raise ValueError(f"{name} is None")
+    got, want = tuple(t.shape), tuple(want)
+    if min_last is None or len(got) != len(want):
+        ok = got == want
+    else:
+        tok = len(want) - (1 if name == "eta" else 2)
+        ok = (all(g == w for i, (g, w) in enumerate(zip(got, want)) if i != tok)
+              and got[tok] >= min_last)
+    if not ok:
+        raise ValueError(f"{name} has shape {got}, expected {want}"
+                         + (" (or longer along the tokens)" if min_last is not None else ""))
+
+
 def _io_dtype(cfg: Config):
     import torch
     return torch.bfloat16 if cfg.io_dtype == "bf16" else torch.float32
 
 
+def _state_shapes(cfg: Config, st):
+    """W1, W3 (M1, M3): [B,H,h,d]; W2 (M2): [B,H,d,h]."""
+    names = ("W1", "W2", "W3") + (("M1", "M2", "M3") if cfg.uses_momentum() else ())
+    for n in names:
+        want = (cfg.B, cfg.H, cfg.d, cfg.h) if n[1] == "2" else (cfg.B, cfg.H, cfg.h, cfg.d)
+        _check_shape(n, st.get(n), want)
+    return names
+
+
 def _check_state(cfg: Config, st):
     import torch
-    for n in ("W1", "W2", "W3"):
+    names = _state_shapes(cfg, st)
+    for n in names:
         _check_tensor(n, st[n], torch.float32)
-    if cfg.uses_momentum():
-        for n in ("M1", "M2", "M3"):
-            _check_tensor(n, st.get(n), torch.float32)
+    return [st[n] for n in names]
+
+
+def _same_device(tensors):
+    devs = {t.device for t in tensors if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on several devices: {sorted(str(d) for d in devs)}")
 
 
 def workspace_bytes(cfg: Config, max_chunk_kv: int, max_chunk_q: int) -> int:
@@ -201,6 +233,10 @@ def alloc_workspace(cfg: Config, max_chunk_kv: int, max_chunk_q: int, device="cu
                        device=device)
 
 
+def _eta_shape(cfg: Config, T):
+    return ((3,) if cfg.eta_per_matrix else ()) + (cfg.B, cfg.H, T)
+
+
 def _check_eta(cfg: Config, eta, K, rows_only=False):
     import torch
     want = (3,) + tuple(K.shape[:2]) if cfg.eta_per_matrix else tuple(K.shape[:2])
@@ -216,12 +252,20 @@ def lact_update(cfg: Config, st: dict, K, V, eta, ws, stream=None, n=None,
     views into longer sequences (rows dense, pairs and rate blocks at the
     given strides)."""
     lib = load_library()
-    _check_state(cfg, st)
     views = kv_stride_bh is not None or eta_stride_bh is not None
+    n = (K.shape[2] if K is not None and K.dim() == 4 else 0) if n is None else n
+    # shapes first: the library cannot see buffer sizes
+    _state_shapes(cfg, st)
+    for name, t in (("K", K), ("V", V)):
+        _check_shape(name, t, (cfg.B, cfg.H, n, cfg.d), min_last=n if views else None)
+    _check_shape("eta", eta, _eta_shape(cfg, n), min_last=n if views else None)
+    if n < 1:
+        raise ValueError(f"n={n} must be >= 1")
+    sts = _check_state(cfg, st)
     _check_tensor("K", K, _io_dtype(cfg), rows_only=views)
     _check_tensor("V", V, _io_dtype(cfg), rows_only=views)
     _check_eta(cfg, eta, K, rows_only=views)
-    n = K.shape[2] if n is None else n
+    _same_device(sts + [K, V, eta, ws])
     kv_stride_bh = K.shape[2] * cfg.d if kv_stride_bh is None else kv_stride_bh
     eta_stride_bh = eta.shape[-1] if eta_stride_bh is None else eta_stride_bh
     if views:
@@ -233,21 +277,31 @@ def lact_update(cfg: Config, st: dict, K, V, eta, ws, stream=None, n=None,
         if (eta.stride(-2) != eta_stride_bh or eta.stride(-3) != eta.shape[-2] * eta_stride_bh
                 or (lead and eta.stride(0) != eta.shape[1] * eta.shape[2] * eta_stride_bh)):
             raise ValueError(f"eta: strides {eta.stride()} do not match eta_stride_bh={eta_stride_bh}")
-        if n > K.shape[2] or n > eta.shape[-1]:
-            raise ValueError(f"n={n} beyond the views ({K.shape[2]} keys, {eta.shape[-1]} rates)")
     c, s = cfg.to_c(), _state(st)
     _check(lib.lact_update(ctypes.byref(c), ctypes.byref(s), _ptr(K), _ptr(V), _ptr(eta), n,
                            kv_stride_bh, eta_stride_bh, _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def lact_apply(cfg: Config, st: dict, Q, O, ws=None, stream=None, m=None, q_stride_bh=None):
-    """O = f_W(Q) for Q, O [B,H,m,d]."""
+    """O = f_W(Q) for Q, O [B,H,m,d] (with explicit m and q_stride_bh: the
+    first m rows of every pair of contiguous [B,H,T,d] tensors, T >= m)."""
     lib = load_library()
-    _check_state(cfg, st)
+    views = m is not None or q_stride_bh is not None
+    m = (Q.shape[2] if Q is not None and Q.dim() == 4 else 0) if m is None else m
+    _state_shapes(cfg, st)
+    for name, t in (("Q", Q), ("O", O)):
+        _check_shape(name, t, (cfg.B, cfg.H, m, cfg.d), min_last=m if views else None)
+    if tuple(Q.shape) != tuple(O.shape):
+        raise ValueError(f"Q {tuple(Q.shape)} and O {tuple(O.shape)} differ")
+    if m < 1:
+        raise ValueError(f"m={m} must be >= 1")
+    sts = _check_state(cfg, st)
     _check_tensor("Q", Q, _io_dtype(cfg))
     _check_tensor("O", O, _io_dtype(cfg))
-    m = Q.shape[2] if m is None else m
+    _same_device(sts + [Q, O] + ([ws] if ws is not None else []))
     q_stride_bh = Q.shape[2] * cfg.d if q_stride_bh is None else q_stride_bh
+    if q_stride_bh != Q.shape[2] * cfg.d:
+        raise ValueError(f"q_stride_bh={q_stride_bh} is not the tensors' pair stride {Q.shape[2] * cfg.d}")
     c, s = cfg.to_c(), _state(st)
     _check(lib.lact_apply(ctypes.byref(c), ctypes.byref(s), _ptr(Q), _ptr(O), m, q_stride_bh,
                           _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
@@ -258,13 +312,20 @@ def lact_chunked_forward(cfg: Config, st: dict, Q, K, V, eta, O, chunk_kv: int, 
     """The whole layer over contiguous [B,H,T,d] tensors and eta [B,H,T_kv] (per
     matrix: [3,B,H,T_kv]) (state updated in place)."""
     lib = load_library()
-    _check_state(cfg, st)
+    _state_shapes(cfg, st)
+    T_kv = K.shape[2] if K is not None and K.dim() == 4 else -1
+    T_q = Q.shape[2] if Q is not None and Q.dim() == 4 else -1
+    for name, t, T in (("K", K, T_kv), ("V", V, T_kv), ("Q", Q, T_q), ("O", O, T_q)):
+        _check_shape(name, t, (cfg.B, cfg.H, T, cfg.d))
+    _check_shape("eta", eta, _eta_shape(cfg, T_kv))
+    sts = _check_state(cfg, st)
     for name, t in (("Q", Q), ("K", K), ("V", V), ("O", O)):
         _check_tensor(name, t, _io_dtype(cfg))
     _check_eta(cfg, eta, K)
+    _same_device(sts + [Q, K, V, eta, O, ws])
     c, s = cfg.to_c(), _state(st)
     _check(lib.lact_chunked_forward(ctypes.byref(c), ctypes.byref(s), _ptr(Q), _ptr(K), _ptr(V),
-                                    _ptr(eta), _ptr(O), K.shape[2], Q.shape[2], chunk_kv, chunk_q,
+                                    _ptr(eta), _ptr(O), T_kv, T_q, chunk_kv, chunk_q,
                                     ORDER_CODES[order], _ptr(ws), ws.numel(), _stream(stream)))
 
 

@@ -43,7 +43,12 @@
  *     and are not meaningful after the call.  Two calls in flight at once
  *     must not share a workspace.
  *   - Results are deterministic: a fixed launch plan derived from the
- *     shapes only, and fixed-order reductions.
+ *     shapes, the options and the alignment of the buffers (16-byte aligned
+ *     Q, K, V, O, W and M, and strides of whole 16-byte rows, select the
+ *     matrix-core kernels; other buffers run fp32-arithmetic kernels whose
+ *     results agree within the stated tolerances but not bit for bit), and
+ *     fixed-order reductions.  The same call on the same buffers gives the
+ *     same bits.
  *   - Return value: LACT_OK or a negative lact_status.  Nothing is enqueued
  *     when validation fails.  lact_last_error() gives a thread-local text.
  *   - NaN / Inf inputs propagate; there is no device-side check.
@@ -79,10 +84,18 @@ typedef enum { LACT_OPT_GD = 0, LACT_OPT_MOMENTUM = 1, LACT_OPT_MUON = 2 } lact_
  * carry the -eta factor, are rounded), fp32 accumulation.
  * LACT_PRODUCTS_SPLIT: only the inputs Q, K, V are bf16; every derived
  * operand keeps ~16 significant bits (computed in fp32, or as a hi + lo pair
- * of bf16 values on the matrix cores).  Muon over many chunks amplifies
- * operand rounding from chunk to chunk, which the split mode avoids at a
- * higher cost.  Ignored in fp32 I/O mode. */
-typedef enum { LACT_PRODUCTS_BF16 = 0, LACT_PRODUCTS_SPLIT = 1 } lact_products;
+ * of bf16 values on the matrix cores).
+ * Muon maps every singular value of the gradient towards one, so it lifts the
+ * rounding of bf16 operands in the weak directions of short chunks (~7e-2 on
+ * 100-key chunks) and compounds it over a scan (~1.4x per chunk: 3e-3 after
+ * one 4096-key chunk, 0.25 after fourteen).  Under Muon, LACT_PRODUCTS_BF16
+ * is therefore accepted only for chunks of >= 1024 keys and runs of at most
+ * 4 chunks (one lact_update call counts as one chunk); otherwise the call
+ * returns LACT_ERR_UNSUPPORTED.  LACT_PRODUCTS_AUTO (the default) takes
+ * LACT_PRODUCTS_BF16 where it is accepted and LACT_PRODUCTS_SPLIT elsewhere.
+ * Callers that drive a long Muon scan through lact_update should ask for
+ * LACT_PRODUCTS_SPLIT themselves.  Ignored in fp32 I/O mode. */
+typedef enum { LACT_PRODUCTS_BF16 = 0, LACT_PRODUCTS_SPLIT = 1, LACT_PRODUCTS_AUTO = 2 } lact_products;
 
 /* Length of the updated rows (step (4)).  LACT_NORM_UNIT: every stored row r
  * of W1, W3 (length d) and W2 (length h) becomes r / max(||r||_2, norm_eps).
@@ -131,7 +144,7 @@ typedef struct {
 /* Defaults: opt GD, beta 0, ns_iters 5, (a,b,c) = (3.4445, -4.7750, 2.0315)
  * (the quintic published with the Muon optimizer; the pages only name
  * Newton-Schulz), ns_eps 1e-7, step 1, norm_eps 1e-12, io_dtype LACT_BF16,
- * products LACT_PRODUCTS_BF16, norm_mode LACT_NORM_UNIT, eta_mode LACT_ETA_SHARED.
+ * products LACT_PRODUCTS_AUTO, norm_mode LACT_NORM_UNIT, eta_mode LACT_ETA_SHARED.
  * B, H, d, h are set to 0 and must be filled in. */
 void lact_config_default(lact_config* cfg);
 

@@ -73,7 +73,7 @@ class Workload:
     ns_iters: int = 5
     io_dtype: str = "bf16"  # "fp32" | "bf16"
     seed: int = 0
-    products: str = "bf16"  # "bf16" | "split": precision of derived product operands
+    products: str = "auto"  # "auto" | "bf16" | "split": precision of derived product operands
     norm: str = "unit"      # "unit" | "keep": updated rows to unit length or kept at their length
     eta_per_matrix: bool = False  # rates [3,B,H,T_kv]: one per token and matrix (W1, W2, W3)
 
@@ -114,12 +114,12 @@ WORKLOADS = {
     # 16 chunks of 2048, apply-then-update, momentum 0.9.
     "lm": Workload("lm", B=8, H=8, d=128, h=256, T_kv=32768, T_q=32768,
                    chunk_kv=2048, chunk_q=2048, order="apply_then_update",
-                   opt="momentum", beta=0.9),
+                   opt="momentum", beta=0.9, products="bf16"),
     # posed-image set: 196,608 input tokens as one chunk, 12 heads d=64,
     # h=128, update-then-apply on 4096 query tokens, Muon 5.
     "posed": Workload("posed", B=1, H=12, d=64, h=128, T_kv=196608, T_q=4096,
                       chunk_kv=196608, chunk_q=4096, order="update_then_apply",
-                      opt="muon"),
+                      opt="muon", products="bf16"),
     # AR video: 14 chunks of 4096 tokens, 40 heads d=128, h=256,
     # apply-then-update, Muon 5.
     # (Muon over 14 chunks amplifies bf16 rounding of the gradient's operands
@@ -131,7 +131,7 @@ WORKLOADS = {
     # update-then-apply on 8040 query tokens, Muon 5.
     "million": Workload("million", B=1, H=12, d=64, h=128, T_kv=1029120, T_q=8040,
                         chunk_kv=1029120, chunk_q=8040, order="update_then_apply",
-                        opt="muon"),
+                        opt="muon", products="bf16"),
 }
 
 

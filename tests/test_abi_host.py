@@ -2,7 +2,13 @@
 
 * the library loads and exports every function include/lact.h declares;
 * workspace sizing;
-* argument validation returns the documented status before any HIP call.
+* argument validation returns the documented status before any HIP call;
+* the binding checks shapes and devices before calling the library.
+
+Several checks hand the library stand-in device addresses (256) with one bad
+argument.  Where no GPU is visible a validation regression then ends as a HIP
+error (no device); on a machine with a GPU it would launch kernels on those
+addresses, so the module runs only where no GPU is visible.
 """
 
 import ctypes
@@ -15,6 +21,17 @@ import chunk_test_amd as L
 from chunk_test_amd import lact as B
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0  # counts without initialising the runtime
+    except Exception:  # noqa: BLE001
+        return False
+
+
+pytestmark = pytest.mark.skipif(_gpu_visible(), reason="stand-in device addresses: CPU-only module")
 
 
 def header_functions():
@@ -163,3 +180,99 @@ def test_binding_checks_the_rate_shape():
         cfg = L.Config(1, 2, 64, 128, eta_per_matrix=per_matrix)
         with pytest.raises(ValueError, match="leading dims"):
             B._check_eta(cfg, torch.zeros(bad), K)
+
+
+def _forward_rc(cfg, T_kv, chunk_kv, T_q, chunk_q, order=0):
+    lib = L.load_library()
+    c = cfg.to_c()
+    s = B.LactState(256, 256, 256, 256, 256, 256)
+    rc = lib.lact_chunked_forward(ctypes.byref(c), ctypes.byref(s), 256, 256, 256, 256, 256, T_kv,
+                                  T_q, chunk_kv, chunk_q, order, 256, 1 << 40, None)
+    return rc, lib.lact_last_error().decode()
+
+
+def test_bf16_products_refused_where_muon_amplifies_rounding():
+    """bf16 operand products under Muon: refused on chunks of < 1024 keys and on
+    runs of more than 4 chunks (the video workload's 14 chunks of 4096); split
+    and the default (auto) pass validation there (no GPU here: the first launch
+    then fails with a HIP error)."""
+    video = dict(T_kv=14 * 4096, chunk_kv=4096, T_q=14 * 4096, chunk_q=4096)
+    tiny_chunks = dict(T_kv=300, chunk_kv=100, T_q=21, chunk_q=7)
+    for shape, d, h in ((video, 128, 256), (tiny_chunks, 64, 128)):
+        rc, msg = _forward_rc(L.Config(1, 2, d, h, opt="muon", products="bf16"), **shape)
+        assert rc == B.LACT_ERR_UNSUPPORTED and "1024 keys" in msg, (rc, msg)
+        for prod in ("auto", "split"):
+            rc, msg = _forward_rc(L.Config(1, 2, d, h, opt="muon", products=prod), **shape)
+            assert rc == B.LACT_ERR_HIP, (prod, rc, msg)
+    # accepted: one long chunk (posed), four chunks, and every optimizer other than Muon
+    for cfg, shape in ((L.Config(1, 2, 64, 128, opt="muon", products="bf16"),
+                        dict(T_kv=196608, chunk_kv=196608, T_q=4096, chunk_q=4096)),
+                       (L.Config(1, 2, 64, 128, opt="muon", products="bf16"),
+                        dict(T_kv=4 * 1024, chunk_kv=1024, T_q=4, chunk_q=1)),
+                       (L.Config(1, 2, 64, 128, opt="momentum", beta=0.9, products="bf16"), tiny_chunks),
+                       (L.Config(1, 2, 64, 128, opt="gd", products="bf16"), video)):
+        rc, msg = _forward_rc(cfg, **shape)
+        assert rc == B.LACT_ERR_HIP, (cfg, rc, msg)
+    # lact_update counts as one chunk: only the chunk length matters
+    cfg = L.Config(1, 1, 64, 128, opt="muon", products="bf16")
+    assert _call_update(cfg, n=100) == B.LACT_ERR_UNSUPPORTED
+    assert _call_update(cfg, n=1024) == B.LACT_ERR_HIP
+    assert _call_update(L.Config(1, 1, 64, 128, opt="muon"), n=100) == B.LACT_ERR_HIP
+    # the workspace covers either precision (auto decides per call)
+    auto = L.workspace_bytes(L.Config(1, 40, 128, 256, opt="muon"), 4096, 4096)
+    for prod in ("bf16", "split"):
+        assert auto >= L.workspace_bytes(L.Config(1, 40, 128, 256, opt="muon", products=prod), 4096, 4096)
+
+
+def _cpu_state(cfg, **override):
+    import torch
+    st = {}
+    for n in ("W1", "W2", "W3") + (("M1", "M2", "M3") if cfg.uses_momentum() else ()):
+        shape = (cfg.B, cfg.H, cfg.d, cfg.h) if n[1] == "2" else (cfg.B, cfg.H, cfg.h, cfg.d)
+        st[n] = torch.zeros(shape)
+    st.update(override)
+    return st
+
+
+def _binding_cases():
+    """(entry point, what is wrong) for the binding's shape checks."""
+    return ["K d", "V tokens", "eta tokens", "eta per-matrix block", "W2 transposed", "M1 shape",
+            "Q batch", "O tokens", "apply Q/O differ", "update K heads"]
+
+
+@pytest.mark.parametrize("case", _binding_cases())
+def test_binding_rejects_mismatched_shapes_before_the_library(case):
+    """Every mismatch is a ValueError raised before any library call (CPU
+    tensors: with the right shapes the next complaint is about the device)."""
+    import torch
+    cfg = L.Config(2, 3, 64, 128, opt="momentum", beta=0.9)
+    st = _cpu_state(cfg)
+    T_kv, T_q = 32, 8
+    Q = torch.zeros(2, 3, T_q, 64)
+    K = torch.zeros(2, 3, T_kv, 64)
+    V = torch.zeros(2, 3, T_kv, 64)
+    eta = torch.zeros(2, 3, T_kv)
+    O = torch.zeros(2, 3, T_q, 64)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    fwd = lambda **kw: L.lact_chunked_forward(
+        kw.get("cfg", cfg), kw.get("st", st), kw.get("Q", Q), kw.get("K", K), kw.get("V", V),
+        kw.get("eta", eta), kw.get("O", O), 16, 4, "apply_then_update", ws)
+    call = {
+        "K d": lambda: fwd(K=torch.zeros(2, 3, T_kv, 32)),
+        "V tokens": lambda: fwd(V=torch.zeros(2, 3, T_kv - 1, 64)),
+        "eta tokens": lambda: fwd(eta=torch.zeros(2, 3, T_kv + 1)),
+        "eta per-matrix block": lambda: fwd(cfg=L.Config(2, 3, 64, 128, opt="momentum", beta=0.9,
+                                                         eta_per_matrix=True)),
+        "W2 transposed": lambda: fwd(st=_cpu_state(cfg, W2=torch.zeros(2, 3, 128, 64))),
+        "M1 shape": lambda: fwd(st=_cpu_state(cfg, M1=torch.zeros(2, 3, 128, 32))),
+        "Q batch": lambda: fwd(Q=torch.zeros(1, 3, T_q, 64)),
+        "O tokens": lambda: fwd(O=torch.zeros(2, 3, T_q + 2, 64)),
+        "apply Q/O differ": lambda: L.lact_apply(cfg, st, Q, torch.zeros(2, 3, T_q, 64)[:, :, :4],
+                                                 m=4, q_stride_bh=T_q * 64),
+        "update K heads": lambda: L.lact_update(cfg, st, torch.zeros(2, 2, T_kv, 64), V, eta, ws),
+    }[case]
+    with pytest.raises(ValueError, match="shape|differ"):
+        call()
+    # the same call with matching shapes gets past the shape checks
+    with pytest.raises(ValueError, match="device tensor"):
+        fwd()

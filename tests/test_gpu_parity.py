@@ -38,13 +38,18 @@ SMALL_CASES = [
     small("posed", H=2, T_kv=16384, T_q=512, chunk_kv=16384, chunk_q=512),
     small("video", H=2, T_kv=3 * 4096, T_q=3 * 4096),
     small("million", H=2, T_kv=40000, T_q=1000, chunk_kv=40000, chunk_q=1000),
-    # bf16, chunks shorter than one LDS stage of the MFMA kernel, ragged.
-    # (Muon is not used here: on 100-token chunks Newton-Schulz lifts the
-    # near-null singular directions of the gradient, and bf16 operand
-    # rounding alone moves the result by ~7e-2; a CPU emulation of bf16
-    # operands shows the same.)
+    # bf16, chunks shorter than one LDS stage of the MFMA kernel, ragged
     small("posed", name="posed-tiny-chunks", H=3, T_kv=1000, T_q=70, chunk_kv=100, chunk_q=7,
           opt="momentum", beta=0.9),
+    # the same under Muon: on 100-key chunks Newton-Schulz lifts the weak
+    # directions of the gradient, where bf16 operand rounding alone moves the
+    # result by ~7e-2, so the default product precision (auto) keeps the derived
+    # operands split here
+    small("posed", name="posed-tiny-chunks-muon", H=3, T_kv=300, T_q=21, chunk_kv=100,
+          chunk_q=7, products="auto"),
+    # the video workload's shape and length under the default product precision
+    # (14 Muon chunks: split products)
+    small("video", name="video-auto", H=1, products="auto"),
     # bf16, two 128-unit hidden slices at d = 64; 1000 queries (two query-read
     # workgroups of several pipelined 128-query steps, the last one ragged)
     small("posed", name="posed-h256", H=2, h=256, T_kv=5000, T_q=1000, chunk_kv=5000, chunk_q=1000),
@@ -100,15 +105,14 @@ def test_small_parity(w):
 def random_case(seed):
     """A seeded draw over the supported shapes and options (sizes small enough for
     the oracle): head dim, hidden width, I/O type, optimizer, order, ragged chunk
-    sizes and the two variants.  bf16 Muon gets chunks of at least 1,000 keys
-    (shorter bf16 Muon chunks are ill-conditioned, see the tiny-chunk case)."""
+    sizes and the two variants, with the default product precision (auto)."""
     r = np.random.default_rng(1000 + seed)
     d = int(r.choice([32, 64, 128]))
     h = int(r.choice([32, 64, 96, 128, 160, 256, 384]))
     io = str(r.choice(["fp32", "bf16"]))
     opt = str(r.choice(["gd", "momentum", "muon"]))
     n_chunks = int(r.integers(1, 4))
-    chunk_kv = int(r.integers(1000 if (io == "bf16" and opt == "muon") else 40, 1600))
+    chunk_kv = int(r.integers(40, 1600))
     chunk_q = int(r.integers(1, 300))
     return TINY.replace(
         name=f"random-{seed}", B=int(r.integers(1, 3)), H=int(r.integers(1, 3)), d=d, h=h,
@@ -355,3 +359,70 @@ def test_invalid_arguments_raise_without_launching():
     with pytest.raises(L.LactError) as e:
         L.lact_apply(cfg, st, Q, torch.empty_like(Q))
     assert e.value.status == -2
+
+
+def test_offset_buffers_take_the_fp32_kernels_within_tolerance():
+    """The launch plan depends on buffer alignment: K, V, Q, O one element past
+    a 16-byte boundary run the fp32-arithmetic kernels instead of the matrix
+    cores.  Expected: both runs within the bf16 bar of the oracle (not the
+    same bits), and each run reproducible bit for bit."""
+    import torch
+    import chunk_test_amd as L
+    w = small("posed", name="offset", H=2, T_kv=4096, T_q=256, chunk_kv=4096, chunk_q=256)
+    st = S.gen_weights(w)
+    x = S.gen_inputs(w)
+    cfg = G.config_of(w)
+    O_ref, s_ref = G.run_oracle(w, x, st)
+    results = []
+    for off in (0, 1, 0, 1):
+        dst = G.device_state(w, st)
+        dev = {}
+        for n in ("Q", "K", "V"):
+            a = torch.from_numpy(np.ascontiguousarray(x[n])).to(torch.bfloat16)
+            buf = torch.zeros(a.numel() + 8, dtype=torch.bfloat16, device="cuda")
+            dev[n] = buf[off:off + a.numel()].view(a.shape)
+            dev[n].copy_(a)
+        obuf = torch.zeros(dev["Q"].numel() + 8, dtype=torch.bfloat16, device="cuda")
+        O = obuf[off:off + dev["Q"].numel()].view(dev["Q"].shape)
+        assert (dev["K"].data_ptr() % 16 == 0) == (off == 0)
+        eta = G.to_dev(x["eta"], w, io=False)
+        ws = L.alloc_workspace(cfg, w.chunk_kv, w.chunk_q)
+        L.lact_chunked_forward(cfg, dst, dev["Q"], dev["K"], dev["V"], eta, O, w.chunk_kv,
+                               w.chunk_q, w.order, ws)
+        torch.cuda.synchronize()
+        s_np = {n: t.cpu().numpy() for n, t in dst.items()}
+        O_np = O.float().cpu().numpy()
+        _, bad = G.compare(w, O_np, s_np, O_ref, s_ref)
+        assert not bad, (off, bad)
+        results.append((O_np, s_np))
+    for a, b in ((0, 2), (1, 3)):
+        assert np.array_equal(results[a][0], results[b][0])
+        for n in results[a][1]:
+            assert np.array_equal(results[a][1][n], results[b][1][n]), n
+    assert not np.array_equal(results[0][0], results[1][0])
+
+
+@pytest.mark.parametrize("where", ["eta", "K"])
+def test_nan_input_propagates_within_its_pair(where):
+    """A NaN in one token's rate (or key) of one pair: that pair's gradient,
+    update and weights become NaN and so does every output read after the
+    update; every other pair gives the same bits as without the NaN (pairs are
+    independent; nothing checks values on the device)."""
+    w = small("posed", name=f"nan-{where}", H=3, T_kv=8192, T_q=256, chunk_kv=4096, chunk_q=128)
+    st = S.gen_weights(w)
+    x = S.gen_inputs(w)
+    O0, s0 = G.run_gpu(w, x, st)
+    bad_pair = 1
+    if where == "eta":
+        x["eta"][0, bad_pair, 777] = np.nan
+    else:
+        x["K"][0, bad_pair, 777, 5] = np.nan
+    O1, s1 = G.run_gpu(w, x, st)
+    for n in ("W1", "W2", "W3"):
+        assert np.all(np.isnan(s1[n][0, bad_pair])), n
+        for p in (0, 2):
+            assert np.array_equal(s1[n][0, p], s0[n][0, p]), (n, p)
+    # update-then-apply: every query of the pair reads the poisoned weights
+    assert np.all(np.isnan(O1[0, bad_pair]))
+    for p in (0, 2):
+        assert np.array_equal(O1[0, p], O0[0, p]), p
