@@ -69,6 +69,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
                            "(or python chunk_test_amd/build.py)")
+    # One HIP runtime per process: PyTorch ships its own copy of the runtime
+    # under the same soname.  Loaded first, it is the one the library binds to;
+    # loaded after the library, it would start a second runtime beside the
+    # library's, and the library's kernel launches would then find no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER
     lib.lact_config_default.argtypes = [P(LactConfig)]

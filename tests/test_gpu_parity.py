@@ -354,8 +354,9 @@ def test_invalid_arguments_raise_without_launching():
     import dataclasses
     w = TINY
     cfg = dataclasses.replace(G.config_of(w), d=60)
-    st = G.device_state(w, S.gen_weights(w))
-    Q = torch.zeros(1, 1, 8, 64, device="cuda")
+    st = {n: torch.zeros((1, 1) + ((60, w.h) if n == "W2" else (w.h, 60)), device="cuda")
+          for n in ("W1", "W2", "W3")}
+    Q = torch.zeros(1, 1, 8, 60, device="cuda")
     with pytest.raises(L.LactError) as e:
         L.lact_apply(cfg, st, Q, torch.empty_like(Q))
     assert e.value.status == -2
