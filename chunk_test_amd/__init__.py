@@ -10,9 +10,11 @@ from .lact import (  # noqa: F401
     alloc_workspace,
     lact_apply,
     lact_chunked_forward,
+    lact_chunked_forward_noalloc,
     lact_update,
     load_library,
     mfma_path,
+    noalloc_scratch_bytes,
     profile_enable,
     profile_read,
     workspace_bytes,

@@ -506,6 +506,39 @@ int run_apply(const Plan& p, const lact_state* st, const void* Q, void* O, int64
   return LACT_OK;
 }
 
+// ------------------------------------------------- allocation-free entry point
+// Scratch of lact_chunked_forward_noalloc: a fixed array in the code object,
+// one copy per GPU the library runs on, held until the process ends.  Host
+// code must not use the array's name as an address (on the host it is only a
+// stand-in): each device's address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and only that pointer is passed on.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of the scratch array (looked up on the first call made
+// with the device current).
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(LACT_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr || reinterpret_cast<uintptr_t>(p) % kAlign != 0)
+      return fail(LACT_ERR_HIP, "scratch array at an unusable address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LACT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -627,6 +660,29 @@ int lact_chunked_forward(const lact_config* cfg, const lact_state* st, const voi
   }
   return LACT_OK;
 }
+
+int lact_chunked_forward_noalloc(const lact_config* cfg, const lact_state* st, const void* Q,
+                                 const void* K, const void* V, const float* eta, void* O, int64_t T_kv,
+                                 int64_t T_q, int64_t chunk_kv, int64_t chunk_q, int32_t order,
+                                 void* stream) {
+  g_last_error.clear();
+  Plan p;
+  int rc = check_config(cfg, &p);
+  if (rc) return rc;
+  if (chunk_kv < 1) return fail(LACT_ERR_INVALID_ARG, "chunk sizes must be >= 1");
+  const size_t need = lact_workspace_bytes(cfg, chunk_kv, chunk_q);
+  if (need > kNoallocScratchBytes)
+    return fail(LACT_ERR_WORKSPACE,
+                "chunks of %lld keys need %zu bytes of scratch, above the %zu bytes of the "
+                "allocation-free entry point (use lact_chunked_forward with a workspace)",
+                (long long)chunk_kv, need, kNoallocScratchBytes);
+  void* ws = nullptr;
+  if ((rc = noalloc_scratch(&ws))) return rc;
+  return lact_chunked_forward(cfg, st, Q, K, V, eta, O, T_kv, T_q, chunk_kv, chunk_q, order, ws,
+                              kNoallocScratchBytes, stream);
+}
+
+size_t lact_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
 
 const char* lact_status_string(int status) {
   switch (status) {

@@ -34,7 +34,8 @@ NORM_CODES = {"unit": 0, "keep": 1}
 EXPORTED = (
     "lact_config_default", "lact_workspace_bytes", "lact_update", "lact_apply",
     "lact_chunked_forward", "lact_status_string", "lact_last_error", "lact_mfma_path",
-    "lact_profile_enable", "lact_profile_read", "lact_version",
+    "lact_profile_enable", "lact_profile_read", "lact_version", "lact_chunked_forward_noalloc",
+    "lact_noalloc_scratch_bytes",
 )
 
 
@@ -93,6 +94,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          c_void_p, c_void_p, c_int64, c_int64, c_int64, c_int64,
                                          c_int32, c_void_p, c_size_t, c_void_p]
     lib.lact_chunked_forward.restype = c_int
+    lib.lact_chunked_forward_noalloc.argtypes = [P(LactConfig), P(LactState), c_void_p, c_void_p,
+                                                 c_void_p, c_void_p, c_void_p, c_int64, c_int64,
+                                                 c_int64, c_int64, c_int32, c_void_p]
+    lib.lact_chunked_forward_noalloc.restype = c_int
+    lib.lact_noalloc_scratch_bytes.argtypes = []
+    lib.lact_noalloc_scratch_bytes.restype = c_size_t
     lib.lact_status_string.argtypes = [c_int]
     lib.lact_status_string.restype = c_char_p
     lib.lact_last_error.argtypes = []
@@ -335,6 +342,33 @@ def lact_chunked_forward(cfg: Config, st: dict, Q, K, V, eta, O, chunk_kv: int, 
     _check(lib.lact_chunked_forward(ctypes.byref(c), ctypes.byref(s), _ptr(Q), _ptr(K), _ptr(V),
                                     _ptr(eta), _ptr(O), T_kv, T_q, chunk_kv, chunk_q,
                                     ORDER_CODES[order], _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def lact_chunked_forward_noalloc(cfg: Config, st: dict, Q, K, V, eta, O, chunk_kv: int,
+                                 chunk_q: int, order: str, stream=None):
+    """lact_chunked_forward without a workspace: the library's fixed scratch
+    array on the current device (no allocation; overlapping calls on one GPU
+    race)."""
+    lib = load_library()
+    _state_shapes(cfg, st)
+    T_kv = K.shape[2] if K is not None and K.dim() == 4 else -1
+    T_q = Q.shape[2] if Q is not None and Q.dim() == 4 else -1
+    for name, t, T in (("K", K, T_kv), ("V", V, T_kv), ("Q", Q, T_q), ("O", O, T_q)):
+        _check_shape(name, t, (cfg.B, cfg.H, T, cfg.d))
+    _check_shape("eta", eta, _eta_shape(cfg, T_kv))
+    sts = _check_state(cfg, st)
+    for name, t in (("Q", Q), ("K", K), ("V", V), ("O", O)):
+        _check_tensor(name, t, _io_dtype(cfg))
+    _check_eta(cfg, eta, K)
+    _same_device(sts + [Q, K, V, eta, O])
+    c, s = cfg.to_c(), _state(st)
+    _check(lib.lact_chunked_forward_noalloc(ctypes.byref(c), ctypes.byref(s), _ptr(Q), _ptr(K),
+                                            _ptr(V), _ptr(eta), _ptr(O), T_kv, T_q, chunk_kv,
+                                            chunk_q, ORDER_CODES[order], _stream(stream)))
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(load_library().lact_noalloc_scratch_bytes())
 
 
 def mfma_path(d: int, h: int, io_dtype: str = "bf16") -> int:

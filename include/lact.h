@@ -182,6 +182,25 @@ int lact_chunked_forward(const lact_config* cfg, const lact_state* st,
                          int64_t chunk_q, int32_t order, void* ws, size_t ws_bytes,
                          void* stream);
 
+/* lact_chunked_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace.  Its scratch is a
+ * fixed array of lact_noalloc_scratch_bytes() bytes (64 MiB) that the library
+ * holds on every GPU it runs on until the process ends; the call allocates
+ * nothing.  The device is the current one (the stream must belong to it).
+ * Chunks whose workspace (lact_workspace_bytes) exceeds the array are
+ * refused with LACT_ERR_WORKSPACE.  Every call on a GPU shares that GPU's
+ * array: calls that overlap on one GPU (several streams or threads) race,
+ * and must be ordered by the caller.  Nothing in the array needs clearing
+ * between calls.  Results are the same bits as lact_chunked_forward's. */
+int lact_chunked_forward_noalloc(const lact_config* cfg, const lact_state* st,
+                                 const void* Q, const void* K, const void* V, const float* eta,
+                                 void* O, int64_t T_kv, int64_t T_q, int64_t chunk_kv,
+                                 int64_t chunk_q, int32_t order, void* stream);
+
+/* Size of the allocation-free entry point's scratch array. */
+size_t lact_noalloc_scratch_bytes(void);
+
 /* Static text of a status code. */
 const char* lact_status_string(int status);
 
