@@ -166,7 +166,9 @@ def swiglu_grad(W1, W2, W3, K, V, eta, token_block=None):
 
 # --------------------------------------------------------------------------
 # linear fast net (review, "Large chunks alone do not explain the gains":
-# a linear state of the same size).  Used by the closed-form pins only.
+# the nonlinear fast net against a linear state).  The closed-form pins use
+# it without row normalisation; the GPU variant runs it with every
+# normalisation mode.
 # --------------------------------------------------------------------------
 
 def linear_forward(W, X):
@@ -400,26 +402,29 @@ def lact_chunked_forward(state, Q, K, V, eta, chunk_kv, chunk_q, order, hp: Hype
     other outputs stay zero and their state is copied unchanged); the pairs
     are independent, so this is how large configurations are sampled.
     ``eta`` is [B, H, T_kv], or [3, B, H, T_kv] for a rate per token and matrix.
+    With the linear fast net (``hp.net == "linear"``) the state holds one
+    matrix per pair, W1 [B, H, d, d] (and M1).
     """
     B, H = K.shape[:2]
+    wn = ("W1",) if hp.net == "linear" else ("W1", "W2", "W3")
+    mn = tuple("M" + n[1] for n in wn)
     new = {k: np.array(v, dtype=dtype, copy=True) for k, v in state.items()}
     if hp.uses_momentum():
-        for n in ("M1", "M2", "M3"):
+        for n in mn:
             new.setdefault(n, np.zeros_like(new["W" + n[1]]))
     O = np.zeros(Q.shape, dtype=dtype)
     todo = list(_pairs(B, H)) if pairs is None else list(pairs)
     for b, h in todo:
         # inputs are cast one pair at a time to bound host memory
         cast = lambda x: np.asarray(x[b, h], dtype=dtype)
-        W = tuple(new[n][b, h] for n in ("W1", "W2", "W3"))
-        M = (tuple(new[n][b, h] for n in ("M1", "M2", "M3"))
-             if hp.uses_momentum() else None)
+        W = tuple(new[n][b, h] for n in wn)
+        M = tuple(new[n][b, h] for n in mn) if hp.uses_momentum() else None
         O[b, h], W, M = chunked_forward_pair(W, M, cast(Q), cast(K), cast(V),
                                              _pair_eta(eta, b, h, dtype), chunk_kv, chunk_q,
                                              order, hp)
-        for n, x in zip(("W1", "W2", "W3"), W):
+        for n, x in zip(wn, W):
             new[n][b, h] = x
         if M is not None:
-            for n, x in zip(("M1", "M2", "M3"), M):
+            for n, x in zip(mn, M):
                 new[n][b, h] = x
     return O, new

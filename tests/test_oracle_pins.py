@@ -79,3 +79,29 @@ def test_float32_twin_close_to_float64():
     assert P.rel_err(O32, O64) < 1e-5
     for n in ("W1", "W2", "W3"):
         assert P.rel_err(W32[n], W64[n]) < 1e-5
+
+
+def test_batched_linear_net_matches_pairwise_and_closed_form():
+    """The batched entry point with the linear net (state W1 [B, H, d, d]) runs
+    each pair's scan; without normalisation it is the chunk-causal linear
+    attention closed form (both orders)."""
+    r = np.random.default_rng(31)
+    B, H, d, T, chunk = 2, 2, 8, 48, 8
+    W0 = r.normal(size=(B, H, d, d)) / np.sqrt(d)
+    Q, K, V = (r.normal(size=(B, H, T, d)) for _ in range(3))
+    eta = np.abs(r.normal(size=(B, H, T))) * 0.1
+    for order in ("apply_then_update", "update_then_apply"):
+        for opt, beta in (("gd", 0.0), ("momentum", 0.6), ("muon", 0.0)):
+            hp = oracle.Hyper(opt=opt, beta=beta, net="linear", normalize=opt == "muon")
+            O, new = oracle.lact_chunked_forward({"W1": W0}, Q, K, V, eta, chunk, chunk, order, hp)
+            assert set(new) == ({"W1", "M1"} if hp.uses_momentum() else {"W1"})
+            for b in range(B):
+                for h in range(H):
+                    M = (np.zeros((d, d)),) if hp.uses_momentum() else None
+                    Op, Wp, _ = oracle.chunked_forward_pair((W0[b, h],), M, Q[b, h], K[b, h], V[b, h],
+                                                            eta[b, h], chunk, chunk, order, hp)
+                    assert np.array_equal(O[b, h], Op) and np.array_equal(new["W1"][b, h], Wp[0])
+                    if opt != "muon":
+                        ref = P.linear_closed_form(W0[b, h], Q[b, h], K[b, h], V[b, h], eta[b, h],
+                                                   chunk, order, beta)
+                        assert P.rel_err(O[b, h], ref) < 1e-12
