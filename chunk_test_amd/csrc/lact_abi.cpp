@@ -86,6 +86,8 @@ struct Plan {
   bool momentum = false;
   bool muon = false;
   bool split = false;  // bf16 inputs, ~fp32 derived operands
+  bool linear = false; // linear fast net (one d x d matrix per pair)
+  int norm = 0;        // lact_norm_mode
 };
 
 // Token splits of one chunk's gradient.  Derived from the shapes only (not
@@ -125,6 +127,9 @@ Splits plan_splits(const SplitRule& r, int64_t n) {
 SplitRule generic_rule(const Plan& p) {
   return {static_cast<int64_t>(p.P) * (p.h / 32), 1024, 256, 128};
 }
+
+// Linear fast net: one workgroup per (split, pair), 64-token tiles.
+SplitRule linear_rule(const Plan& p) { return {static_cast<int64_t>(p.P), 1024, 256, 64}; }
 
 // Which chunk-gradient kernel runs.  The MFMA kernels read 16-byte rows with
 // 32-bit offsets inside a pair's rows: they need aligned K, V and strides and
@@ -169,7 +174,11 @@ int check_config(const lact_config* c, Plan* p) {
   if (c->B < 1 || c->H < 1) return fail(LACT_ERR_INVALID_ARG, "B=%d H=%d must be >= 1", c->B, c->H);
   if (static_cast<int64_t>(c->B) * c->H > 65535)
     return fail(LACT_ERR_UNSUPPORTED, "B*H=%lld above 65535", (long long)c->B * c->H);
-  if (c->d < 1 || c->h < 1) return fail(LACT_ERR_INVALID_ARG, "d=%d h=%d must be >= 1", c->d, c->h);
+  if (c->net != LACT_NET_SWIGLU && c->net != LACT_NET_LINEAR)
+    return fail(LACT_ERR_INVALID_ARG, "net %d unknown", c->net);
+  const bool linear = c->net == LACT_NET_LINEAR;
+  if (c->d < 1 || (!linear && c->h < 1))
+    return fail(LACT_ERR_INVALID_ARG, "d=%d h=%d must be >= 1", c->d, c->h);
   if (c->io_dtype != LACT_F32 && c->io_dtype != LACT_BF16)
     return fail(LACT_ERR_INVALID_ARG, "io_dtype %d unknown", c->io_dtype);
   if (c->opt != LACT_OPT_GD && c->opt != LACT_OPT_MOMENTUM && c->opt != LACT_OPT_MUON)
@@ -188,10 +197,27 @@ int check_config(const lact_config* c, Plan* p) {
     return fail(LACT_ERR_INVALID_ARG, "products %d unknown", c->products);
   if (!finite(c->norm_eps) || c->norm_eps <= 0.f)
     return fail(LACT_ERR_INVALID_ARG, "norm_eps %g must be finite and > 0", c->norm_eps);
-  if (c->norm_mode != LACT_NORM_UNIT && c->norm_mode != LACT_NORM_KEEP)
+  if (c->norm_mode != LACT_NORM_UNIT && c->norm_mode != LACT_NORM_KEEP && c->norm_mode != LACT_NORM_NONE)
     return fail(LACT_ERR_INVALID_ARG, "norm_mode %d unknown", c->norm_mode);
   if (c->eta_mode != LACT_ETA_SHARED && c->eta_mode != LACT_ETA_PER_MATRIX)
     return fail(LACT_ERR_INVALID_ARG, "eta_mode %d unknown", c->eta_mode);
+  if (linear) {
+    if (!lact::linear_shape_ok(c->d))
+      return fail(LACT_ERR_UNSUPPORTED, "linear fast net: d=%d not in {16, 32, 64, 128}", c->d);
+    if (c->eta_mode != LACT_ETA_SHARED)
+      return fail(LACT_ERR_UNSUPPORTED, "linear fast net: one rate per token (eta_mode 0)");
+    p->P = c->B * c->H;
+    p->d = c->d;
+    p->h = c->d;
+    p->bf16 = c->io_dtype == LACT_BF16;
+    p->momentum = c->opt == LACT_OPT_MOMENTUM || (c->opt == LACT_OPT_MUON && c->beta > 0.f);
+    p->muon = c->opt == LACT_OPT_MUON;
+    p->linear = true;
+    p->norm = c->norm_mode;
+    return LACT_OK;
+  }
+  if (c->norm_mode == LACT_NORM_NONE)
+    return fail(LACT_ERR_UNSUPPORTED, "norm_mode LACT_NORM_NONE is built for the linear fast net only");
   const int mf = lact_mfma_path(c->d, c->h, c->io_dtype);
   if (mf < 0)
     return fail(LACT_ERR_UNSUPPORTED,
@@ -205,6 +231,7 @@ int check_config(const lact_config* c, Plan* p) {
   p->momentum = c->opt == LACT_OPT_MOMENTUM || (c->opt == LACT_OPT_MUON && c->beta > 0.f);
   p->muon = c->opt == LACT_OPT_MUON;
   p->split = p->bf16 && c->products == LACT_PRODUCTS_SPLIT;
+  p->norm = c->norm_mode;
   return LACT_OK;
 }
 
@@ -221,7 +248,7 @@ constexpr int64_t kMuonBf16MaxChunks = 4;
 
 // Settles the product precision of a run of `chunks` chunks of `n` keys.
 int resolve_products(const lact_config* c, Plan* p, int64_t n, int64_t chunks) {
-  if (!p->bf16) {
+  if (!p->bf16 || p->linear) {
     p->split = false;
     return LACT_OK;
   }
@@ -244,6 +271,12 @@ int resolve_products(const lact_config* c, Plan* p, int64_t n, int64_t chunks) {
 
 int check_state(const Plan& p, const lact_state* st, bool need_m) {
   if (st == nullptr) return fail(LACT_ERR_INVALID_ARG, "state is NULL");
+  if (p.linear) {
+    if (!st->W1) return fail(LACT_ERR_INVALID_ARG, "linear fast net: W1 must be non-NULL");
+    if (need_m && p.momentum && !st->M1)
+      return fail(LACT_ERR_INVALID_ARG, "this optimizer keeps momentum: M1 must be non-NULL");
+    return LACT_OK;
+  }
   if (!st->W1 || !st->W2 || !st->W3) return fail(LACT_ERR_INVALID_ARG, "W1, W2, W3 must be non-NULL");
   if (need_m && p.momentum && (!st->M1 || !st->M2 || !st->M3))
     return fail(LACT_ERR_INVALID_ARG, "this optimizer keeps momentum: M1, M2, M3 must be non-NULL");
@@ -258,8 +291,23 @@ struct WsLayout {
 
 WsLayout ws_layout(const Plan& p, int64_t max_chunk_kv) {
   WsLayout w;
-  const size_t per = static_cast<size_t>(3) * p.h * p.d;
   const int64_t n = max_chunk_kv < 1 ? 1 : max_chunk_kv;
+  if (p.linear) {
+    // partials [P, S, d d] | dir [P, d d] | Newton-Schulz scratch [P, 4 d d]
+    const size_t dd = static_cast<size_t>(p.d) * p.d;
+    const int64_t S = split_bound(linear_rule(p), n);
+    size_t off = 0;
+    w.partials = off;
+    off += align_up(sizeof(float) * dd * p.P * static_cast<size_t>(S));
+    w.dir = off;
+    off += align_up(sizeof(float) * dd * p.P);
+    w.ns = off;
+    if (p.muon) off += align_up(sizeof(float) * 4 * dd * p.P);
+    w.wb = off;
+    w.total = off;
+    return w;
+  }
+  const size_t per = static_cast<size_t>(3) * p.h * p.d;
   // every kernel the update may pick for up to n tokens
   // (for either product precision: AUTO settles it per call)
   int64_t S = split_bound(generic_rule(p), n);
@@ -304,11 +352,63 @@ size_t io_bytes(const Plan& p) { return p.bf16 ? 2 : 4; }
 // One update on validated arguments (steps 2-4).  With wb non-NULL the
 // update tail also stores the new W1, W2, W3 as bf16 there (three arrays of
 // P h d values) where its kernels support it; *wb_written says whether it did.
+// One update of the linear fast net: split-K gradient, then reduction with
+// momentum, Newton-Schulz (Muon) and the step with the row rule.
+int run_update_linear(const lact_config* c, const Plan& p, const lact_state* st, const void* K,
+                      const void* V, const float* eta, int64_t n, int64_t kv_stride, int64_t eta_stride,
+                      char* ws, const WsLayout& L, hipStream_t s) {
+  const Splits sp = plan_splits(linear_rule(p), n);
+  float* partials = reinterpret_cast<float*>(ws + L.partials);
+  hipError_t e;
+  {
+    PhaseTimer t(0, s);
+    lact::LinGradArgs g{};
+    g.K = K;
+    g.V = V;
+    g.eta = eta;
+    g.n = n;
+    g.kv_stride = kv_stride;
+    g.eta_stride = eta_stride;
+    g.partials = partials;
+    g.P = p.P;
+    g.d = p.d;
+    g.S = sp.S;
+    g.tps = sp.tps;
+    g.bf16 = p.bf16;
+    e = lact::launch_lin_grad(g, s);
+    if (e != hipSuccess) return hip_fail(e, "linear gradient kernel");
+  }
+  PhaseTimer t(1, s);
+  lact::LinTailArgs a{};
+  a.partials = partials;
+  a.splits = sp.S;
+  a.dir = reinterpret_cast<float*>(ws + L.dir);
+  a.scratch = reinterpret_cast<float*>(ws + L.ns);
+  a.W = st->W1;
+  a.M = p.momentum ? st->M1 : nullptr;
+  a.beta = c->beta;
+  a.step = c->step;
+  a.norm_eps = c->norm_eps;
+  a.norm = p.norm;
+  a.muon = p.muon;
+  a.iters = c->ns_iters;
+  a.a = c->ns_a;
+  a.b = c->ns_b;
+  a.c = c->ns_c;
+  a.ns_eps = c->ns_eps;
+  a.P = p.P;
+  a.d = p.d;
+  e = lact::launch_lin_tail(a, s);
+  if (e != hipSuccess) return hip_fail(e, "linear update-tail kernels");
+  return LACT_OK;
+}
+
 int run_update(const lact_config* c, const Plan& p, const lact_state* st, const void* K,
                const void* V, const float* eta, int64_t n, int64_t kv_stride,
                int64_t eta_stride, char* ws, const WsLayout& L, hipStream_t s,
                uint16_t* wb = nullptr, bool* wb_written = nullptr) {
   if (wb_written != nullptr) *wb_written = false;
+  if (p.linear) return run_update_linear(c, p, st, K, V, eta, n, kv_stride, eta_stride, ws, L, s);
   const bool aligned = (reinterpret_cast<uintptr_t>(K) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(V) % 16 == 0) && (kv_stride % 8 == 0);
   const GradChoice gk = grad_choice(p, aligned, n);
@@ -478,6 +578,20 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
 int run_apply(const Plan& p, const lact_state* st, const void* Q, void* O, int64_t m,
               int64_t q_stride, hipStream_t s, const uint16_t* wb = nullptr) {
   PhaseTimer t(4, s);
+  if (p.linear) {
+    lact::LinApplyArgs a{};
+    a.Q = Q;
+    a.O = O;
+    a.m = m;
+    a.q_stride = q_stride;
+    a.W = st->W1;
+    a.P = p.P;
+    a.d = p.d;
+    a.bf16 = p.bf16;
+    hipError_t e = lact::launch_lin_apply(a, s);
+    if (e != hipSuccess) return hip_fail(e, "linear query-read kernel");
+    return LACT_OK;
+  }
   lact::ApplyArgs a{};
   a.Q = Q;
   a.O = O;
@@ -559,6 +673,7 @@ void lact_config_default(lact_config* c) {
   c->products = LACT_PRODUCTS_AUTO;
   c->norm_mode = LACT_NORM_UNIT;
   c->eta_mode = LACT_ETA_SHARED;
+  c->net = LACT_NET_SWIGLU;
 }
 
 int lact_mfma_path(int32_t d, int32_t h, int32_t io_dtype) {
@@ -723,6 +838,6 @@ int lact_profile_read(double* ms, int64_t* launches) {
   return rc;
 }
 
-int lact_version(void) { return 1; }
+int lact_version(void) { return 2; }
 
 }  // extern "C"

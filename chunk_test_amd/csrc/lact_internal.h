@@ -89,6 +89,43 @@ struct ApplyArgs {
   const uint16_t *Wb1, *Wb2, *Wb3;
 };
 
+// ---- linear fast net f_W(x) = W x, W [P, d, d] (fp32 arithmetic) ----
+struct LinGradArgs {
+  const void* K;
+  const void* V;
+  const float* eta;
+  int64_t n, kv_stride, eta_stride;
+  float* partials;  // [P, S, d d]
+  int P, d, S;
+  int64_t tps;
+  int bf16;
+};
+struct LinTailArgs {
+  const float* partials;  // [P, splits, d d]
+  int splits;
+  float* dir;             // [P, d d]
+  float* scratch;         // Newton-Schulz: 4 d d floats per pair
+  float* W;               // [P, d, d]
+  float* M;               // [P, d, d] or NULL
+  float beta, step, norm_eps;
+  int norm;               // 0 unit rows, 1 rows kept at their length, 2 no normalisation
+  int muon, iters;
+  float a, b, c, ns_eps;
+  int P, d;
+};
+struct LinApplyArgs {
+  const void* Q;
+  void* O;
+  int64_t m, q_stride;
+  const float* W;
+  int P, d;
+  int bf16;
+};
+bool linear_shape_ok(int d);
+hipError_t launch_lin_grad(const LinGradArgs& a, hipStream_t s);
+hipError_t launch_lin_tail(const LinTailArgs& a, hipStream_t s);  // reduce (+momentum), NS, step
+hipError_t launch_lin_apply(const LinApplyArgs& a, hipStream_t s);
+
 // ---- generic kernels (fp32 arithmetic; any supported d, h) ----
 hipError_t launch_grad_simple(const GradArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);

@@ -29,7 +29,8 @@ ORDER_CODES = {"apply_then_update": LACT_APPLY_THEN_UPDATE, "update_then_apply":
 OPT_CODES = {"gd": LACT_OPT_GD, "momentum": LACT_OPT_MOMENTUM, "muon": LACT_OPT_MUON}
 DTYPE_CODES = {"fp32": LACT_F32, "bf16": LACT_BF16}
 PRODUCT_CODES = {"bf16": 0, "split": 1, "auto": 2}
-NORM_CODES = {"unit": 0, "keep": 1}
+NORM_CODES = {"unit": 0, "keep": 1, "none": 2}
+NET_CODES = {"swiglu": 0, "linear": 1}
 
 EXPORTED = (
     "lact_config_default", "lact_workspace_bytes", "lact_update", "lact_apply",
@@ -45,7 +46,7 @@ class LactConfig(ctypes.Structure):
         ("io_dtype", c_int32), ("opt", c_int32), ("beta", c_float),
         ("ns_iters", c_int32), ("ns_a", c_float), ("ns_b", c_float), ("ns_c", c_float),
         ("ns_eps", c_float), ("step", c_float), ("norm_eps", c_float), ("products", c_int32),
-        ("norm_mode", c_int32), ("eta_mode", c_int32),
+        ("norm_mode", c_int32), ("eta_mode", c_int32), ("net", c_int32),
     ]
 
 
@@ -140,15 +141,16 @@ class Config:
     step: float = 1.0
     norm_eps: float = 1e-12
     products: str = "auto"  # "auto" | "bf16" | "split" (lact_products)
-    norm: str = "unit"  # "unit" | "keep": updated rows to unit length, or kept at their length
+    norm: str = "unit"  # "unit" | "keep" | "none" (linear net only): row rule after each update
     eta_per_matrix: bool = False  # rates [3,B,H,T]: one per token and matrix (W1, W2, W3)
+    net: str = "swiglu"  # "swiglu" | "linear" (state W1 [B,H,d,d] only)
 
     def to_c(self) -> LactConfig:
         return LactConfig(self.B, self.H, self.d, self.h, DTYPE_CODES[self.io_dtype],
                           OPT_CODES[self.opt], self.beta, self.ns_iters, self.ns_a, self.ns_b,
                           self.ns_c, self.ns_eps, self.step, self.norm_eps,
                           PRODUCT_CODES[self.products], NORM_CODES[self.norm],
-                          1 if self.eta_per_matrix else 0)
+                          1 if self.eta_per_matrix else 0, NET_CODES[self.net])
 
     def uses_momentum(self) -> bool:
         return self.opt == "momentum" or (self.opt == "muon" and self.beta > 0)
@@ -210,7 +212,12 @@ def _io_dtype(cfg: Config):
 
 
 def _state_shapes(cfg: Config, st):
-    """W1, W3 (M1, M3): [B,H,h,d]; W2 (M2): [B,H,d,h]."""
+    """W1, W3 (M1, M3): [B,H,h,d]; W2 (M2): [B,H,d,h].  Linear net: W1 (M1) [B,H,d,d]."""
+    if cfg.net == "linear":
+        names = ("W1",) + (("M1",) if cfg.uses_momentum() else ())
+        for n in names:
+            _check_shape(n, st.get(n), (cfg.B, cfg.H, cfg.d, cfg.d))
+        return names
     names = ("W1", "W2", "W3") + (("M1", "M2", "M3") if cfg.uses_momentum() else ())
     for n in names:
         want = (cfg.B, cfg.H, cfg.d, cfg.h) if n[1] == "2" else (cfg.B, cfg.H, cfg.h, cfg.d)

@@ -107,7 +107,20 @@ typedef enum { LACT_PRODUCTS_BF16 = 0, LACT_PRODUCTS_SPLIT = 1, LACT_PRODUCTS_AU
  * of Deep Neural Networks" is in the reference list of the "Test-Time
  * Training Done Right" arXiv page).  Identical to LACT_NORM_UNIT for rows of
  * unit length. */
-typedef enum { LACT_NORM_UNIT = 0, LACT_NORM_KEEP = 1 } lact_norm_mode;
+typedef enum { LACT_NORM_UNIT = 0, LACT_NORM_KEEP = 1, LACT_NORM_NONE = 2 } lact_norm_mode;
+/* (LACT_NORM_NONE: rows are left as the step leaves them; linear fast net
+ * only, where it gives the chunk-causal linear-attention closed form.) */
+
+/* The fast net.  LACT_NET_SWIGLU: the layer's f_W above.  LACT_NET_LINEAR:
+ * f_W(x) = W x with one matrix W [d x d] per pair, the linear state the
+ * pages compare the SwiGLU fast net against ("LaCT: Large Chunk Test-Time
+ * Training" review, section "Large chunks alone do not explain the gains"):
+ * the same scan, loss, update rules and row normalisation; the chunk
+ * gradient is dW = -sum_i eta_i v_i k_i^T.  The state is W1 = W
+ * [B, H, d, d] (M1 for momentum); W2, W3 (M2, M3) are not used and may be
+ * NULL; h is ignored; d in {16, 32, 64, 128}; one rate per token; fp32
+ * arithmetic throughout (bf16 inputs and outputs where io_dtype says so). */
+typedef enum { LACT_NET_SWIGLU = 0, LACT_NET_LINEAR = 1 } lact_net;
 
 /* Learning rates.  LACT_ETA_SHARED: one rate eta_i per token, shared by W1,
  * W2 and W3 (the loss of step (2)).  LACT_ETA_PER_MATRIX: three rates per
@@ -134,6 +147,7 @@ typedef struct {
   int32_t products;  /* lact_products: how bf16-mode products treat derived operands      */
   int32_t norm_mode; /* lact_norm_mode: rows to unit length, or kept at their length      */
   int32_t eta_mode;  /* lact_eta_mode: one rate per token, or one per token and matrix    */
+  int32_t net;       /* lact_net: SwiGLU fast weights (the layer) or a linear one         */
 } lact_config;
 
 typedef struct {
@@ -144,7 +158,8 @@ typedef struct {
 /* Defaults: opt GD, beta 0, ns_iters 5, (a,b,c) = (3.4445, -4.7750, 2.0315)
  * (the quintic published with the Muon optimizer; the pages only name
  * Newton-Schulz), ns_eps 1e-7, step 1, norm_eps 1e-12, io_dtype LACT_BF16,
- * products LACT_PRODUCTS_AUTO, norm_mode LACT_NORM_UNIT, eta_mode LACT_ETA_SHARED.
+ * products LACT_PRODUCTS_AUTO, norm_mode LACT_NORM_UNIT, eta_mode LACT_ETA_SHARED,
+ * net LACT_NET_SWIGLU.
  * B, H, d, h are set to 0 and must be filled in. */
 void lact_config_default(lact_config* cfg);
 

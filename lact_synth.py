@@ -76,6 +76,7 @@ class Workload:
     products: str = "auto"  # "auto" | "bf16" | "split": precision of derived product operands
     norm: str = "unit"      # "unit" | "keep": updated rows to unit length or kept at their length
     eta_per_matrix: bool = False  # rates [3,B,H,T_kv]: one per token and matrix (W1, W2, W3)
+    net: str = "swiglu"     # "swiglu" | "linear": f_W(x) = W x with W [d x d] (state W1)
 
     @property
     def n_chunks(self) -> int:
@@ -94,6 +95,12 @@ class Workload:
         pair and update, s = min(d, h), l = max(d, h).
         """
         n, m, d, h = self.chunk_kv, self.chunk_q, self.d, self.h
+        if self.net == "linear":
+            # dW = U^T K (2 n d^2), O = Q W^T (2 m d^2), Newton-Schulz on d x d
+            f = self.pairs * self.n_chunks * (2.0 * n * d * d + 2.0 * m * d * d)
+            if self.opt == "muon":
+                f += self.pairs * self.n_chunks * 3 * self.ns_iters * 6.0 * d ** 3
+            return f
         per_chunk = 12.0 * n * d * h + 6.0 * m * d * h
         f = self.pairs * self.n_chunks * per_chunk
         if self.opt == "muon":
@@ -136,7 +143,14 @@ WORKLOADS = {
 
 
 def gen_weights(w: Workload):
-    """Initial fast weights, [B,H,h,d] / [B,H,d,h] float32 (drawn per head)."""
+    """Initial fast weights, [B,H,h,d] / [B,H,d,h] float32 (drawn per head);
+    the linear net's W1 [B,H,d,d] ~ N(0, 1/sqrt(d))."""
+    bc = lambda x: np.ascontiguousarray(np.broadcast_to(x[None], (w.B,) + x.shape))
+    if w.net == "linear":
+        W = np.empty((w.H, w.d, w.d), np.float32)
+        for hh in range(w.H):
+            W[hh] = block_rng(w.seed, "W1", 0, hh).normal(0.0, 1.0 / np.sqrt(w.d), (w.d, w.d))
+        return {"W1": bc(W)}
     W1 = np.empty((w.H, w.h, w.d), np.float32)
     W3 = np.empty((w.H, w.h, w.d), np.float32)
     W2 = np.empty((w.H, w.d, w.h), np.float32)
@@ -144,7 +158,6 @@ def gen_weights(w: Workload):
         W1[hh] = block_rng(w.seed, "W1", 0, hh).normal(0.0, 1.0 / np.sqrt(w.d), (w.h, w.d))
         W3[hh] = block_rng(w.seed, "W3", 0, hh).normal(0.0, 1.0 / np.sqrt(w.d), (w.h, w.d))
         W2[hh] = block_rng(w.seed, "W2", 0, hh).normal(0.0, 1.0 / np.sqrt(w.h), (w.d, w.h))
-    bc = lambda x: np.ascontiguousarray(np.broadcast_to(x[None], (w.B,) + x.shape))
     return {"W1": bc(W1), "W2": bc(W2), "W3": bc(W3)}
 
 

@@ -34,7 +34,7 @@ def config_of(w: S.Workload):
     from chunk_test_amd import Config
     return Config(B=w.B, H=w.H, d=w.d, h=w.h, io_dtype=w.io_dtype, opt=w.opt, beta=w.beta,
                   ns_iters=w.ns_iters, products=w.products, norm=w.norm,
-                  eta_per_matrix=w.eta_per_matrix)
+                  eta_per_matrix=w.eta_per_matrix, net=w.net)
 
 
 def to_dev(x, w: S.Workload, io=True):
@@ -48,9 +48,10 @@ def to_dev(x, w: S.Workload, io=True):
 def device_state(w: S.Workload, st_np):
     import torch
     cfg = config_of(w)
-    st = {n: to_dev(st_np[n], w, io=False) for n in ("W1", "W2", "W3")}
+    wn = ("W1",) if w.net == "linear" else ("W1", "W2", "W3")
+    st = {n: to_dev(st_np[n], w, io=False) for n in wn}
     if cfg.uses_momentum():
-        for n in ("M1", "M2", "M3"):
+        for n in tuple("M" + x[1] for x in wn):
             src = st_np.get(n)
             st[n] = (to_dev(src, w, io=False) if src is not None
                      else torch.zeros_like(st["W" + n[1]]))
@@ -77,7 +78,7 @@ def run_gpu(w: S.Workload, x, st_np, ws=None):
 def run_oracle(w: S.Workload, x, st_np, pairs=None, token_block=65536):
     import oracle
     hp = oracle.Hyper(opt=w.opt, beta=w.beta, ns_iters=w.ns_iters, token_block=token_block,
-                      norm_keep=w.norm == "keep")
+                      norm_keep=w.norm == "keep", net=w.net, normalize=w.norm != "none")
     return oracle.lact_chunked_forward(st_np, x["Q"], x["K"], x["V"], x["eta"], w.chunk_kv,
                                        w.chunk_q, w.order, hp, pairs=pairs)
 

@@ -276,3 +276,40 @@ def test_binding_rejects_mismatched_shapes_before_the_library(case):
     # the same call with matching shapes gets past the shape checks
     with pytest.raises(ValueError, match="device tensor"):
         fwd()
+
+
+def test_linear_net_validation():
+    lib = L.load_library()
+    ok = L.Config(1, 2, 64, 0, net="linear", norm="none", opt="muon")
+    assert L.workspace_bytes(ok, 1000, 100) > 0
+    for bad, status, text in ((L.Config(1, 2, 48, 0, net="linear"), B.LACT_ERR_UNSUPPORTED, "d=48"),
+                              (L.Config(1, 2, 64, 0, net="linear", eta_per_matrix=True),
+                               B.LACT_ERR_UNSUPPORTED, "one rate"),
+                              (L.Config(1, 2, 64, 128, norm="none"), B.LACT_ERR_UNSUPPORTED, "linear")):
+        c = bad.to_c()
+        assert lib.lact_workspace_bytes(ctypes.byref(c), 128, 128) == 0
+        s = B.LactState(256, 256, 256, None, None, None)
+        assert lib.lact_update(ctypes.byref(c), ctypes.byref(s), 256, 256, 256, 16, 16 * c.d, 16, 256,
+                               1 << 30, None) == status
+        assert text in lib.lact_last_error().decode()
+    c = L.Config(1, 2, 64, 0, net="linear").to_c()
+    c.net = 5
+    assert lib.lact_workspace_bytes(ctypes.byref(c), 128, 128) == 0
+    # the linear state is W1 (and M1) only: W2 / W3 may be NULL
+    c = L.Config(1, 2, 64, 0, net="linear", opt="momentum", beta=0.9).to_c()
+    assert _call_update(L.Config(1, 2, 64, 0, net="linear", opt="momentum", beta=0.9),
+                        st=B.LactState(256, None, None, 256, None, None)) == B.LACT_ERR_HIP
+    assert _call_update(L.Config(1, 2, 64, 0, net="linear", opt="momentum", beta=0.9),
+                        st=B.LactState(256, None, None, None, None, None)) == B.LACT_ERR_INVALID_ARG
+
+
+def test_binding_linear_state_shapes():
+    import torch
+    cfg = L.Config(1, 2, 32, 0, net="linear")
+    K = torch.zeros(1, 2, 16, 32)
+    eta = torch.zeros(1, 2, 16)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="W1 has shape"):
+        L.lact_update(cfg, {"W1": torch.zeros(1, 2, 32, 16)}, K, K, eta, ws)
+    with pytest.raises(ValueError, match="device tensor"):
+        L.lact_update(cfg, {"W1": torch.zeros(1, 2, 32, 32)}, K, K, eta, ws)
