@@ -8,7 +8,9 @@ from .lact import (  # noqa: F401
     Config,
     LactError,
     alloc_workspace,
+    backward_workspace_bytes,
     lact_apply,
+    lact_chunked_backward,
     lact_chunked_forward,
     lact_chunked_forward_noalloc,
     lact_update,

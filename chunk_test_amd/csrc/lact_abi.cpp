@@ -352,6 +352,46 @@ size_t io_bytes(const Plan& p) { return p.bf16 ? 2 : 4; }
 // One update on validated arguments (steps 2-4).  With wb non-NULL the
 // update tail also stores the new W1, W2, W3 as bf16 there (three arrays of
 // P h d values) where its kernels support it; *wb_written says whether it did.
+// The chunk gradient's split partials (the kernel chosen by shape, alignment
+// and product precision); *sp receives the split plan.
+int launch_gradient(const lact_config* c, const Plan& p, const lact_state* st, const void* K, const void* V,
+                    const float* eta, int64_t n, int64_t kv_stride, int64_t eta_stride, float* partials,
+                    hipStream_t s, Splits* sp_out) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(K) % 16 == 0) &&
+                       (reinterpret_cast<uintptr_t>(V) % 16 == 0) && (kv_stride % 8 == 0);
+  const GradChoice gk = grad_choice(p, aligned, n);
+  const Splits sp = plan_splits(gk.kind == GradKind::Generic ? generic_rule(p) : mfma_rule(p, gk), n);
+  *sp_out = sp;
+  PhaseTimer t(0, s);
+  lact::GradArgs g{};
+  g.K = K;
+  g.V = V;
+  g.eta = eta;
+  g.n = n;
+  g.kv_stride = kv_stride;
+  g.eta_stride = eta_stride;
+  // per-matrix rates: three blocks of P pairs each
+  g.eta_mat = c->eta_mode == LACT_ETA_PER_MATRIX ? static_cast<int64_t>(p.P) * eta_stride : 0;
+  g.W1 = st->W1;
+  g.W2 = st->W2;
+  g.W3 = st->W3;
+  g.partials = partials;
+  g.P = p.P;
+  g.d = p.d;
+  g.h = p.h;
+  g.S = sp.S;
+  g.tps = sp.tps;
+  g.bf16 = p.bf16;
+  hipError_t e;
+  switch (gk.kind) {
+    case GradKind::D64: e = lact::launch_grad_d64(g, s); break;
+    case GradKind::D128: e = lact::launch_grad_d128(g, p.split, s); break;
+    default: e = lact::launch_grad_simple(g, s); break;
+  }
+  if (e != hipSuccess) return hip_fail(e, "gradient kernel");
+  return LACT_OK;
+}
+
 // One update of the linear fast net: split-K gradient, then reduction with
 // momentum, Newton-Schulz (Muon) and the step with the row rule.
 int run_update_linear(const lact_config* c, const Plan& p, const lact_state* st, const void* K,
@@ -409,41 +449,12 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
                uint16_t* wb = nullptr, bool* wb_written = nullptr) {
   if (wb_written != nullptr) *wb_written = false;
   if (p.linear) return run_update_linear(c, p, st, K, V, eta, n, kv_stride, eta_stride, ws, L, s);
-  const bool aligned = (reinterpret_cast<uintptr_t>(K) % 16 == 0) &&
-                       (reinterpret_cast<uintptr_t>(V) % 16 == 0) && (kv_stride % 8 == 0);
-  const GradChoice gk = grad_choice(p, aligned, n);
-  const Splits sp = plan_splits(gk.kind == GradKind::Generic ? generic_rule(p) : mfma_rule(p, gk), n);
   float* partials = reinterpret_cast<float*>(ws + L.partials);
   float* dir = reinterpret_cast<float*>(ws + L.dir);
+  Splits sp;
+  int rc = launch_gradient(c, p, st, K, V, eta, n, kv_stride, eta_stride, partials, s, &sp);
+  if (rc) return rc;
   hipError_t e;
-  {
-    PhaseTimer t(0, s);
-    lact::GradArgs g{};
-    g.K = K;
-    g.V = V;
-    g.eta = eta;
-    g.n = n;
-    g.kv_stride = kv_stride;
-    g.eta_stride = eta_stride;
-    // per-matrix rates: three blocks of P pairs each
-    g.eta_mat = c->eta_mode == LACT_ETA_PER_MATRIX ? static_cast<int64_t>(p.P) * eta_stride : 0;
-    g.W1 = st->W1;
-    g.W2 = st->W2;
-    g.W3 = st->W3;
-    g.partials = partials;
-    g.P = p.P;
-    g.d = p.d;
-    g.h = p.h;
-    g.S = sp.S;
-    g.tps = sp.tps;
-    g.bf16 = p.bf16;
-    switch (gk.kind) {
-      case GradKind::D64: e = lact::launch_grad_d64(g, s); break;
-      case GradKind::D128: e = lact::launch_grad_d128(g, p.split, s); break;
-      default: e = lact::launch_grad_simple(g, s); break;
-    }
-    if (e != hipSuccess) return hip_fail(e, "gradient kernel");
-  }
   lact::TailArgs ta{};
   ta.partials = partials;
   ta.splits = sp.S;
@@ -617,6 +628,298 @@ int run_apply(const Plan& p, const lact_state* st, const void* Q, void* O, int64
   }
   hipError_t e = use_mfma ? lact::launch_apply_mfma(a, s) : lact::launch_apply_simple(a, s);
   if (e != hipSuccess) return hip_fail(e, "query-read kernel");
+  return LACT_OK;
+}
+
+// ------------------------------------------------------------------ backward
+// Workspace of the backward pass (bytes, 256-byte aligned sections).
+struct BwLayout {
+  WsLayout fwd;           // the forward update's own workspace, at offset 0
+  size_t ckW = 0, ckM = 0;  // N + 1 slots of W1 | W2 | W3 (and of M1 | M2 | M3)
+  size_t cot = 0, dM = 0, g = 0, dir = 0, ddir = 0, pc = 0, t = 0;  // [P, 3hd] each
+  size_t X = 0;           // three [P, max(chunk_kv, chunk_q), h] factor arrays
+  size_t part = 0;        // contraction partials [P, S, 3hd]
+  size_t ns = 0;          // Newton-Schulz VJP scratch
+  size_t total = 0;
+  int64_t rows = 0;       // max(chunk_kv, chunk_q)
+  int S = 1;
+};
+
+SplitRule backward_rule(const Plan& p) { return {static_cast<int64_t>(p.P) * (p.h / 32), 1024, 256, 32}; }
+
+BwLayout bw_layout(const lact_config* c, const Plan& p, int64_t N, int64_t chunk_kv, int64_t chunk_q) {
+  BwLayout b;
+  b.fwd = ws_layout(p, chunk_kv);
+  const size_t per = static_cast<size_t>(3) * p.h * p.d * p.P;  // floats of one state
+  b.rows = chunk_kv > chunk_q ? chunk_kv : chunk_q;
+  b.S = static_cast<int>(split_bound(backward_rule(p), b.rows));
+  size_t off = b.fwd.total;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  b.ckW = take(sizeof(float) * per * static_cast<size_t>(N + 1));
+  b.ckM = take(p.momentum ? sizeof(float) * per * static_cast<size_t>(N + 1) : 0);
+  b.cot = take(sizeof(float) * per);
+  b.dM = take(sizeof(float) * per);
+  b.g = take(sizeof(float) * per);
+  b.dir = take(sizeof(float) * per);
+  b.ddir = take(sizeof(float) * per);
+  b.pc = take(sizeof(float) * per);
+  b.t = take(sizeof(float) * per);
+  b.X = take(sizeof(float) * 3 * static_cast<size_t>(p.P) * static_cast<size_t>(b.rows) * p.h);
+  b.part = take(sizeof(float) * per * static_cast<size_t>(b.S));
+  b.ns = take(p.muon ? sizeof(float) * 3 * static_cast<size_t>(p.P) *
+                           static_cast<size_t>(lact::bw_ns_floats_per_matrix(p.d, p.h, c->ns_iters))
+                     : 0);
+  b.total = off;
+  return b;
+}
+
+int check_backward(const lact_config* c, const Plan& p) {
+  if (p.linear) return fail(LACT_ERR_UNSUPPORTED, "backward: SwiGLU fast net only");
+  if (p.norm != LACT_NORM_UNIT) return fail(LACT_ERR_UNSUPPORTED, "backward: unit rows (norm_mode 0) only");
+  if (c->eta_mode != LACT_ETA_SHARED) return fail(LACT_ERR_UNSUPPORTED, "backward: one rate per token only");
+  if (!lact::backward_shape_ok(p.d, p.h))
+    return fail(LACT_ERR_UNSUPPORTED, "backward: (d, h) = (%d, %d): d in {32, 64, 128}, h a multiple of 32",
+                p.d, p.h);
+  return LACT_OK;
+}
+
+// The backward pass on validated arguments (see include/lact.h).
+int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, const char* Q, const char* K,
+                 const char* V, const float* eta, const char* dO, const lact_state* dWf, const lact_grads* out,
+                 int64_t T_kv, int64_t T_q, int64_t chunk_kv, int64_t chunk_q, int32_t order, char* ws,
+                 const BwLayout& L, hipStream_t s) {
+  using lact::MatRef;
+  const int64_t N = T_kv / chunk_kv;
+  const int64_t hd = static_cast<int64_t>(p.h) * p.d;
+  const int64_t per = 3 * hd * p.P;  // floats of one state
+  const size_t eb = io_bytes(p);
+  float* ckW = reinterpret_cast<float*>(ws + L.ckW);
+  float* ckM = reinterpret_cast<float*>(ws + L.ckM);
+  float* cot = reinterpret_cast<float*>(ws + L.cot);
+  float* dM = reinterpret_cast<float*>(ws + L.dM);
+  float* gb = reinterpret_cast<float*>(ws + L.g);
+  float* dirb = reinterpret_cast<float*>(ws + L.dir);
+  float* ddir = reinterpret_cast<float*>(ws + L.ddir);
+  float* pc = reinterpret_cast<float*>(ws + L.pc);
+  float* tb = reinterpret_cast<float*>(ws + L.t);
+  float* X = reinterpret_cast<float*>(ws + L.X);
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  const int64_t xs = L.rows * p.h;  // pair stride of a factor array
+  hipError_t e;
+  // slot c of the checkpoints as a state: W1 | W2 | W3, each [P, ...]
+  auto slot = [&](int64_t cidx) {
+    lact_state x{};
+    x.W1 = ckW + cidx * per;
+    x.W2 = x.W1 + hd * p.P;
+    x.W3 = x.W2 + hd * p.P;
+    if (p.momentum) {
+      x.M1 = ckM + cidx * per;
+      x.M2 = x.M1 + hd * p.P;
+      x.M3 = x.M2 + hd * p.P;
+    }
+    return x;
+  };
+  auto refs = [&](float* a, float* b, float* d3, int64_t stride, MatRef* r) {
+    r[0] = {a, stride};
+    r[1] = {b, stride};
+    r[2] = {d3, stride};
+  };
+  const size_t state_bytes = sizeof(float) * hd * p.P;
+  // ---- forward: the weights (and momentum) entering every chunk
+  {
+    lact_state s0 = slot(0);
+    if ((e = hipMemcpyAsync(s0.W1, st0->W1, state_bytes, hipMemcpyDeviceToDevice, s)) != hipSuccess ||
+        (e = hipMemcpyAsync(s0.W2, st0->W2, state_bytes, hipMemcpyDeviceToDevice, s)) != hipSuccess ||
+        (e = hipMemcpyAsync(s0.W3, st0->W3, state_bytes, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return hip_fail(e, "initial weights copy");
+    if (p.momentum) {
+      MatRef z{nullptr, 0};
+      if ((e = lact::launch_bw_copy(s0.M1, z, z, z, p.P, p.d, p.h, true, s)) != hipSuccess)
+        return hip_fail(e, "momentum zero");
+    }
+  }
+  for (int64_t cidx = 0; cidx < N; ++cidx) {
+    const size_t bytes = sizeof(float) * per * (p.momentum ? 1 : 1);
+    if ((e = hipMemcpyAsync(ckW + (cidx + 1) * per, ckW + cidx * per, bytes, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return hip_fail(e, "checkpoint copy");
+    if (p.momentum &&
+        (e = hipMemcpyAsync(ckM + (cidx + 1) * per, ckM + cidx * per, bytes, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+      return hip_fail(e, "checkpoint copy");
+    lact_state sn = slot(cidx + 1);
+    const char* Kp = K + static_cast<size_t>(cidx * chunk_kv * p.d) * eb;
+    const char* Vp = V + static_cast<size_t>(cidx * chunk_kv * p.d) * eb;
+    int rc = run_update(c, p, &sn, Kp, Vp, eta + cidx * chunk_kv, chunk_kv, T_kv * p.d, T_kv, ws, L.fwd, s);
+    if (rc) return rc;
+  }
+  // ---- cotangents of the final state and of the momentum
+  {
+    MatRef f1{dWf ? dWf->W1 : nullptr, hd}, f2{dWf ? dWf->W2 : nullptr, hd}, f3{dWf ? dWf->W3 : nullptr, hd};
+    MatRef z{nullptr, 0};
+    if ((e = lact::launch_bw_copy(cot, f1, f2, f3, p.P, p.d, p.h, true, s)) != hipSuccess ||
+        (e = lact::launch_bw_copy(dM, z, z, z, p.P, p.d, p.h, true, s)) != hipSuccess)
+      return hip_fail(e, "cotangent init");
+  }
+  // token-local VJP + weight contraction, added into cot
+  auto tok_and_contract = [&](bool apply, const lact_state& W, const char* A, const char* B, const float* et,
+                              int64_t n, int64_t in_stride, char* dA, char* dB, float* de) -> int {
+    lact::BwTokArgs a{};
+    a.A = A;
+    a.B = B;
+    a.eta = et;
+    a.n = n;
+    a.in_stride = in_stride;
+    a.eta_stride = T_kv;
+    a.W1 = {W.W1, hd};
+    a.W2 = {W.W2, hd};
+    a.W3 = {W.W3, hd};
+    a.P1 = {pc, 3 * hd};
+    a.P2 = {pc + hd, 3 * hd};
+    a.P3 = {pc + 2 * hd, 3 * hd};
+    a.X1 = X;
+    a.X2 = X + xs * p.P;
+    a.X3 = X + 2 * xs * p.P;
+    a.x_stride = xs;
+    a.dA = dA;
+    a.dB = dB;
+    a.out_stride = in_stride;
+    a.deta = de;
+    a.deta_stride = T_kv;
+    a.P = p.P;
+    a.d = p.d;
+    a.h = p.h;
+    a.bf16 = p.bf16;
+    hipError_t err = lact::launch_bw_tok(a, apply, s);
+    if (err != hipSuccess) return hip_fail(err, "backward token kernel");
+    const Splits sp = plan_splits(backward_rule(p), n);
+    lact::BwContractArgs b{};
+    b.A = A;
+    b.B = B;
+    b.eta = apply ? nullptr : et;
+    b.n = n;
+    b.in_stride = in_stride;
+    b.eta_stride = T_kv;
+    b.X1 = a.X1;
+    b.X2 = a.X2;
+    b.X3 = a.X3;
+    b.x_stride = xs;
+    b.partials = part;
+    b.P = p.P;
+    b.d = p.d;
+    b.h = p.h;
+    b.S = sp.S;
+    b.tps = sp.tps;
+    b.bf16 = p.bf16;
+    if ((err = lact::launch_bw_contract(b, s)) != hipSuccess) return hip_fail(err, "backward contraction kernel");
+    if ((err = lact::launch_bw_reduce_add(cot, part, sp.S, 3 * hd, p.P, s)) != hipSuccess)
+      return hip_fail(err, "backward reduction kernel");
+    return LACT_OK;
+  };
+  char* dQ = static_cast<char*>(out->dQ);
+  char* dK = static_cast<char*>(out->dK);
+  char* dV = static_cast<char*>(out->dV);
+  // ---- chunks in reverse order
+  for (int64_t cidx = N - 1; cidx >= 0; --cidx) {
+    const lact_state Win = slot(cidx), Wout = slot(cidx + 1);
+    const size_t ko = static_cast<size_t>(cidx * chunk_kv * p.d) * eb;
+    const size_t qo = static_cast<size_t>(cidx * chunk_q * p.d) * eb;
+    const float* ec = eta + cidx * chunk_kv;
+    int rc;
+    if (order == LACT_UPDATE_THEN_APPLY &&
+        (rc = tok_and_contract(true, Wout, Q + qo, dO + qo, nullptr, chunk_q, T_q * p.d, dQ + qo, nullptr, nullptr)))
+      return rc;
+    // the update's direction, recomputed: g (GD, Muon without momentum) or
+    // the new momentum M_{c+1}; through Newton-Schulz for Muon
+    if (p.momentum) {
+      MatRef m1{Wout.M1, hd}, m2{Wout.M2, hd}, m3{Wout.M3, hd};
+      if ((e = lact::launch_bw_copy(gb, m1, m2, m3, p.P, p.d, p.h, true, s)) != hipSuccess)
+        return hip_fail(e, "momentum gather");
+    } else {
+      Splits sp;
+      if ((rc = launch_gradient(c, p, &Win, K + ko, V + ko, ec, chunk_kv, T_kv * p.d, T_kv,
+                                reinterpret_cast<float*>(ws + L.fwd.partials), s, &sp)))
+        return rc;
+      lact::ReduceArgs r{};
+      r.partials = reinterpret_cast<float*>(ws + L.fwd.partials);
+      r.dir = gb;
+      r.P = p.P;
+      r.d = p.d;
+      r.h = p.h;
+      r.S = sp.S;
+      if ((e = lact::launch_reduce(r, s)) != hipSuccess) return hip_fail(e, "gradient reduction");
+    }
+    const float* direction = gb;
+    if (p.muon) {
+      if ((e = hipMemcpyAsync(dirb, gb, sizeof(float) * per, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+        return hip_fail(e, "direction copy");
+      lact::NSArgs a{};
+      a.dir = dirb;
+      a.scratch = reinterpret_cast<float*>(ws + L.fwd.ns);
+      a.P = p.P;
+      a.d = p.d;
+      a.h = p.h;
+      a.iters = c->ns_iters;
+      a.a = c->ns_a;
+      a.b = c->ns_b;
+      a.c = c->ns_c;
+      a.eps = c->ns_eps;
+      if ((e = lact::launch_ns_simple(a, s)) != hipSuccess) return hip_fail(e, "Newton-Schulz kernel");
+      direction = dirb;
+    }
+    // through the step and the row normalisation
+    lact::BwStepArgs sa{};
+    refs(Win.W1, Win.W2, Win.W3, hd, sa.W_in);
+    refs(Wout.W1, Wout.W2, Wout.W3, hd, sa.W_out);
+    sa.dir = direction;
+    sa.cot = cot;
+    sa.ddir = ddir;
+    sa.step = c->step;
+    sa.norm_eps = c->norm_eps;
+    sa.P = p.P;
+    sa.d = p.d;
+    sa.h = p.h;
+    if ((e = lact::launch_bw_step(sa, s)) != hipSuccess) return hip_fail(e, "backward step kernel");
+    // through the optimizer: the cotangent of the chunk gradient into pc
+    const float* t_in = ddir;
+    if (p.muon) {
+      lact::BwNSArgs na{};
+      na.g = gb;
+      na.dx = ddir;
+      na.out = p.momentum ? tb : pc;
+      na.scratch = reinterpret_cast<float*>(ws + L.ns);
+      na.per_mat = lact::bw_ns_floats_per_matrix(p.d, p.h, c->ns_iters);
+      na.P = p.P;
+      na.d = p.d;
+      na.h = p.h;
+      na.iters = c->ns_iters;
+      na.a = c->ns_a;
+      na.b = c->ns_b;
+      na.c = c->ns_c;
+      na.eps = c->ns_eps;
+      if ((e = lact::launch_bw_ns(na, s)) != hipSuccess) return hip_fail(e, "Newton-Schulz VJP kernel");
+      t_in = tb;
+    }
+    if (p.momentum) {
+      if ((e = lact::launch_bw_momentum(t_in, dM, pc, c->beta, per, s)) != hipSuccess)
+        return hip_fail(e, "momentum VJP kernel");
+    } else if (!p.muon) {
+      if ((e = hipMemcpyAsync(pc, ddir, sizeof(float) * per, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+        return hip_fail(e, "cotangent copy");
+    }
+    // through the chunk gradient
+    if ((rc = tok_and_contract(false, Win, K + ko, V + ko, ec, chunk_kv, T_kv * p.d, dK + ko, dV + ko,
+                               out->deta + cidx * chunk_kv)))
+      return rc;
+    if (order == LACT_APPLY_THEN_UPDATE &&
+        (rc = tok_and_contract(true, Win, Q + qo, dO + qo, nullptr, chunk_q, T_q * p.d, dQ + qo, nullptr, nullptr)))
+      return rc;
+  }
+  MatRef o1{out->dW1, hd}, o2{out->dW2, hd}, o3{out->dW3, hd};
+  if ((e = lact::launch_bw_copy(cot, o1, o2, o3, p.P, p.d, p.h, false, s)) != hipSuccess)
+    return hip_fail(e, "cotangent store");
   return LACT_OK;
 }
 
@@ -798,6 +1101,52 @@ int lact_chunked_forward_noalloc(const lact_config* cfg, const lact_state* st, c
 }
 
 size_t lact_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+size_t lact_backward_workspace_bytes(const lact_config* cfg, int64_t T_kv, int64_t chunk_kv, int64_t chunk_q) {
+  Plan p;
+  if (check_config(cfg, &p) != LACT_OK || check_backward(cfg, p) != LACT_OK) return 0;
+  if (T_kv < 1 || chunk_kv < 1 || chunk_q < 1 || T_kv % chunk_kv) return 0;
+  return bw_layout(cfg, p, T_kv / chunk_kv, chunk_kv, chunk_q).total;
+}
+
+int lact_chunked_backward(const lact_config* cfg, const lact_state* st, const void* Q, const void* K,
+                          const void* V, const float* eta, const void* dO, const lact_state* dW_final,
+                          const lact_grads* out, int64_t T_kv, int64_t T_q, int64_t chunk_kv, int64_t chunk_q,
+                          int32_t order, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  Plan p;
+  int rc = check_config(cfg, &p);
+  if (rc) return rc;
+  if ((rc = check_backward(cfg, p))) return rc;
+  if (st == nullptr || !st->W1 || !st->W2 || !st->W3)
+    return fail(LACT_ERR_INVALID_ARG, "initial W1, W2, W3 must be non-NULL");
+  if (dW_final != nullptr && (!dW_final->W1 || !dW_final->W2 || !dW_final->W3))
+    return fail(LACT_ERR_INVALID_ARG, "dW_final: W1, W2, W3 must be non-NULL");
+  if (!Q || !K || !V || !eta || !dO || out == nullptr)
+    return fail(LACT_ERR_INVALID_ARG, "Q, K, V, eta, dO, out must be non-NULL");
+  if (!out->dQ || !out->dK || !out->dV || !out->deta || !out->dW1 || !out->dW2 || !out->dW3)
+    return fail(LACT_ERR_INVALID_ARG, "every output of lact_grads must be non-NULL");
+  if (T_kv < 1 || T_q < 1 || chunk_kv < 1 || chunk_q < 1)
+    return fail(LACT_ERR_INVALID_ARG, "sequence lengths and chunk sizes must be >= 1");
+  if (T_kv % chunk_kv || T_q % chunk_q)
+    return fail(LACT_ERR_INVALID_ARG, "chunk sizes (%lld, %lld) must divide T_kv=%lld and T_q=%lld",
+                (long long)chunk_kv, (long long)chunk_q, (long long)T_kv, (long long)T_q);
+  const int64_t N = T_kv / chunk_kv;
+  if (T_q / chunk_q != N)
+    return fail(LACT_ERR_INVALID_ARG, "key chunks (%lld) and query chunks (%lld) differ", (long long)N,
+                (long long)(T_q / chunk_q));
+  if (order != LACT_APPLY_THEN_UPDATE && order != LACT_UPDATE_THEN_APPLY)
+    return fail(LACT_ERR_INVALID_ARG, "order %d unknown", order);
+  if ((rc = resolve_products(cfg, &p, chunk_kv, N))) return rc;
+  const BwLayout L = bw_layout(cfg, p, N, chunk_kv, chunk_q);
+  if (ws_bytes < L.total)
+    return fail(LACT_ERR_WORKSPACE, "workspace of %zu bytes is below the %zu bytes needed", ws_bytes, L.total);
+  if (ws == nullptr || reinterpret_cast<uintptr_t>(ws) % kAlign != 0)
+    return fail(LACT_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
+  return run_backward(cfg, p, st, static_cast<const char*>(Q), static_cast<const char*>(K),
+                      static_cast<const char*>(V), eta, static_cast<const char*>(dO), dW_final, out, T_kv, T_q,
+                      chunk_kv, chunk_q, order, static_cast<char*>(ws), L, static_cast<hipStream_t>(stream));
+}
 
 const char* lact_status_string(int status) {
   switch (status) {

@@ -126,6 +126,68 @@ hipError_t launch_lin_grad(const LinGradArgs& a, hipStream_t s);
 hipError_t launch_lin_tail(const LinTailArgs& a, hipStream_t s);  // reduce (+momentum), NS, step
 hipError_t launch_lin_apply(const LinApplyArgs& a, hipStream_t s);
 
+// ---- backward pass (fp32 arithmetic) ----
+struct MatRef {  // one matrix per pair: element e of pair p at p * pair_stride + e
+  float* p;
+  int64_t pair_stride;
+};
+struct BwTokArgs {  // token-local VJPs (chunk gradient: A = K, B = V; query read: A = Q, B = dO)
+  const void* A;
+  const void* B;
+  const float* eta;  // chunk gradient only
+  int64_t n, in_stride, eta_stride;
+  MatRef W1, W2, W3;  // fast weights of the step
+  MatRef P1, P2, P3;  // cotangents of the chunk gradient (chunk gradient only)
+  float *X1, *X2, *X3;  // [P, n, h] factors of the weight cotangents
+  int64_t x_stride;
+  void* dA;
+  void* dB;  // chunk gradient only
+  int64_t out_stride;
+  float* deta;  // chunk gradient only
+  int64_t deta_stride;
+  int P, d, h;
+  int bf16;
+};
+struct BwContractArgs {  // X1^T A, (b B)^T X2, X3^T A over tokens, b = -eta or 1
+  const void* A;
+  const void* B;
+  const float* eta;  // NULL: b = 1
+  int64_t n, in_stride, eta_stride;
+  const float *X1, *X2, *X3;
+  int64_t x_stride;
+  float* partials;  // [P, S, 3hd]
+  int P, d, h, S;
+  int64_t tps;
+  int bf16;
+};
+struct BwStepArgs {
+  MatRef W_in[3], W_out[3];  // W1, W2, W3 before and after the update
+  const float* dir;          // [P, 3hd] direction of the update
+  float* cot;                // [P, 3hd] cotangent of W_out in, of W_in (direct path) out
+  float* ddir;               // [P, 3hd] cotangent of the direction
+  float step, norm_eps;
+  int P, d, h;
+};
+struct BwNSArgs {
+  const float* g;   // [P, 3hd] Newton-Schulz input
+  const float* dx;  // [P, 3hd] cotangent of its output
+  float* out;       // [P, 3hd] cotangent of its input
+  float* scratch;   // 3P * per_mat floats
+  int64_t per_mat;
+  int P, d, h, iters;
+  float a, b, c, eps;
+};
+bool backward_shape_ok(int d, int h);
+hipError_t launch_bw_tok(const BwTokArgs& a, bool apply, hipStream_t s);
+hipError_t launch_bw_contract(const BwContractArgs& a, hipStream_t s);
+hipError_t launch_bw_reduce_add(float* dst, const float* partials, int S, int64_t per, int P, hipStream_t s);
+hipError_t launch_bw_step(const BwStepArgs& a, hipStream_t s);
+hipError_t launch_bw_momentum(const float* t, float* dM, float* Pout, float beta, int64_t total, hipStream_t s);
+int64_t bw_ns_floats_per_matrix(int d, int h, int iters);
+hipError_t launch_bw_ns(const BwNSArgs& a, hipStream_t s);
+hipError_t launch_bw_copy(float* blocks, const MatRef& m1, const MatRef& m2, const MatRef& m3, int P, int d, int h,
+                          bool to_blocks, hipStream_t s);
+
 // ---- generic kernels (fp32 arithmetic; any supported d, h) ----
 hipError_t launch_grad_simple(const GradArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);

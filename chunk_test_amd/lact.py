@@ -36,7 +36,7 @@ EXPORTED = (
     "lact_config_default", "lact_workspace_bytes", "lact_update", "lact_apply",
     "lact_chunked_forward", "lact_status_string", "lact_last_error", "lact_mfma_path",
     "lact_profile_enable", "lact_profile_read", "lact_version", "lact_chunked_forward_noalloc",
-    "lact_noalloc_scratch_bytes",
+    "lact_noalloc_scratch_bytes", "lact_backward_workspace_bytes", "lact_chunked_backward",
 )
 
 
@@ -52,6 +52,10 @@ class LactConfig(ctypes.Structure):
 
 class LactState(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in ("W1", "W2", "W3", "M1", "M2", "M3")]
+
+
+class LactGrads(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in ("dQ", "dK", "dV", "deta", "dW1", "dW2", "dW3")]
 
 
 class LactError(RuntimeError):
@@ -101,6 +105,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lact_chunked_forward_noalloc.restype = c_int
     lib.lact_noalloc_scratch_bytes.argtypes = []
     lib.lact_noalloc_scratch_bytes.restype = c_size_t
+    lib.lact_backward_workspace_bytes.argtypes = [P(LactConfig), c_int64, c_int64, c_int64]
+    lib.lact_backward_workspace_bytes.restype = c_size_t
+    lib.lact_chunked_backward.argtypes = [P(LactConfig), P(LactState), c_void_p, c_void_p, c_void_p,
+                                          c_void_p, c_void_p, c_void_p, P(LactGrads), c_int64, c_int64,
+                                          c_int64, c_int64, c_int32, c_void_p, c_size_t, c_void_p]
+    lib.lact_chunked_backward.restype = c_int
     lib.lact_status_string.argtypes = [c_int]
     lib.lact_status_string.restype = c_char_p
     lib.lact_last_error.argtypes = []
@@ -372,6 +382,57 @@ def lact_chunked_forward_noalloc(cfg: Config, st: dict, Q, K, V, eta, O, chunk_k
     _check(lib.lact_chunked_forward_noalloc(ctypes.byref(c), ctypes.byref(s), _ptr(Q), _ptr(K),
                                             _ptr(V), _ptr(eta), _ptr(O), T_kv, T_q, chunk_kv,
                                             chunk_q, ORDER_CODES[order], _stream(stream)))
+
+
+def backward_workspace_bytes(cfg: Config, T_kv: int, chunk_kv: int, chunk_q: int) -> int:
+    lib = load_library()
+    c = cfg.to_c()
+    n = lib.lact_backward_workspace_bytes(ctypes.byref(c), T_kv, chunk_kv, chunk_q)
+    if n == 0:
+        raise LactError(LACT_ERR_UNSUPPORTED, f"no backward workspace size for {cfg}")
+    return n
+
+
+def lact_chunked_backward(cfg: Config, st: dict, Q, K, V, eta, dO, chunk_kv: int, chunk_q: int,
+                          order: str, ws=None, dW_final: dict | None = None, stream=None):
+    """Cotangents of lact_chunked_forward's inputs given dO (like Q) and,
+    optionally, dW_final (cotangents of the final W1, W2, W3).  ``st`` holds
+    the initial W1, W2, W3 (not modified).  Returns a dict with dQ, dK, dV
+    (like Q, K, V), deta and dW1, dW2, dW3 (new tensors)."""
+    import torch
+    lib = load_library()
+    if cfg.net != "swiglu":
+        raise ValueError("backward: SwiGLU fast net only")
+    wcfg = dataclasses.replace(cfg, opt="gd", beta=0.0)  # the initial state has no momentum
+    _state_shapes(wcfg, st)
+    T_kv = K.shape[2] if K is not None and K.dim() == 4 else -1
+    T_q = Q.shape[2] if Q is not None and Q.dim() == 4 else -1
+    for name, t, T in (("K", K, T_kv), ("V", V, T_kv), ("Q", Q, T_q), ("dO", dO, T_q)):
+        _check_shape(name, t, (cfg.B, cfg.H, T, cfg.d))
+    _check_shape("eta", eta, _eta_shape(cfg, T_kv))
+    if dW_final is not None:
+        _state_shapes(wcfg, dW_final)
+    sts = _check_state(wcfg, st)
+    for name, t in (("Q", Q), ("K", K), ("V", V), ("dO", dO)):
+        _check_tensor(name, t, _io_dtype(cfg))
+    _check_eta(cfg, eta, K)
+    fin = _check_state(wcfg, dW_final) if dW_final is not None else []
+    if ws is None:
+        ws = torch.empty(backward_workspace_bytes(cfg, T_kv, chunk_kv, chunk_q), dtype=torch.uint8,
+                         device=K.device)
+    _same_device(sts + fin + [Q, K, V, eta, dO, ws])
+    out = {"dQ": torch.empty_like(Q), "dK": torch.empty_like(K), "dV": torch.empty_like(V),
+           "deta": torch.empty_like(eta)}
+    for n in ("W1", "W2", "W3"):
+        out["d" + n] = torch.empty_like(st[n])
+    g = LactGrads(*[_ptr(out[n]) for n in ("dQ", "dK", "dV", "deta", "dW1", "dW2", "dW3")])
+    c, s = cfg.to_c(), _state(st)
+    fs = _state(dW_final) if dW_final is not None else None
+    _check(lib.lact_chunked_backward(ctypes.byref(c), ctypes.byref(s), _ptr(Q), _ptr(K), _ptr(V),
+                                     _ptr(eta), _ptr(dO), ctypes.byref(fs) if fs is not None else None,
+                                     ctypes.byref(g), T_kv, T_q, chunk_kv, chunk_q, ORDER_CODES[order],
+                                     _ptr(ws), ws.numel(), _stream(stream)))
+    return out
 
 
 def noalloc_scratch_bytes() -> int:

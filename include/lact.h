@@ -216,6 +216,49 @@ int lact_chunked_forward_noalloc(const lact_config* cfg, const lact_state* st,
 /* Size of the allocation-free entry point's scratch array. */
 size_t lact_noalloc_scratch_bytes(void);
 
+/* ------------------------------------------------------------------ backward
+ * Training through the layer: the pages' throughput figures are training
+ * throughput ("LaCT: Large Chunk Test-Time Training" review, section
+ * "Language modelling: quality and throughput differ").  Given the cotangent
+ * dO of lact_chunked_forward's outputs (and, optionally, of the final fast
+ * weights), lact_chunked_backward returns the cotangents of its inputs: dQ,
+ * dK, dV, deta and the initial fast weights dW1, dW2, dW3.  It first reruns
+ * the forward updates from the initial weights (with zero momentum), keeping
+ * the weights entering every chunk in the workspace, then takes every chunk
+ * back in reverse order: the query read, the step and row normalisation,
+ * the optimizer (momentum's buffer cotangent carried back over the chunks,
+ * Newton-Schulz differentiated through every iteration and its pre-scaling)
+ * and the chunk gradient itself (a gradient: its VJP carries the second
+ * derivative of silu).  The forward updates run on the same kernels as
+ * lact_chunked_forward; every VJP runs fp32 arithmetic.
+ * Scope: the SwiGLU fast net with unit rows (norm_mode LACT_NORM_UNIT), one
+ * rate per token, d in {32, 64, 128}, h a multiple of 32 up to 1024; any
+ * order and optimizer.  Others return LACT_ERR_UNSUPPORTED. */
+typedef struct {
+  void *dQ, *dK, *dV;      /* like Q, K, V (io_dtype), written                         */
+  float* deta;             /* [B, H, T_kv], written                                     */
+  float *dW1, *dW2, *dW3;  /* like W1, W2, W3: cotangents of the initial weights, written */
+} lact_grads;
+
+/* Scratch for lact_chunked_backward on sequences of T_kv keys in chunks of
+ * chunk_kv keys and chunk_q queries: the forward's workspace, N + 1 copies
+ * of the fast weights (and momentum), per-token factors of the weight
+ * cotangents (3 h floats per token and pair) and small per-pair buffers.
+ * 0 for an invalid or unsupported configuration. */
+size_t lact_backward_workspace_bytes(const lact_config* cfg, int64_t T_kv, int64_t chunk_kv,
+                                     int64_t chunk_q);
+
+/* st: the initial fast weights (read only; M is taken as zero).  Q, K, V,
+ * eta, T_kv, T_q, chunk sizes and order as for lact_chunked_forward.  dO:
+ * cotangent of O, like Q.  dW_final: NULL, or a state whose W1, W2, W3 hold
+ * the cotangents of the final fast weights (its M fields are ignored).
+ * Every output of `out` is written (not accumulated). */
+int lact_chunked_backward(const lact_config* cfg, const lact_state* st, const void* Q,
+                          const void* K, const void* V, const float* eta, const void* dO,
+                          const lact_state* dW_final, const lact_grads* out, int64_t T_kv,
+                          int64_t T_q, int64_t chunk_kv, int64_t chunk_q, int32_t order,
+                          void* ws, size_t ws_bytes, void* stream);
+
 /* Static text of a status code. */
 const char* lact_status_string(int status);
 
