@@ -7,3 +7,5 @@ from .lact_oracle import *  # noqa: F401,F403
 from .lact_oracle import Hyper, MUON_COEFFS  # noqa: F401
 from . import lact_backward  # noqa: F401,E402
 from .lact_backward import lact_chunked_backward, chunked_backward_pair  # noqa: F401,E402
+from . import lact_block  # noqa: F401,E402
+from .lact_block import window_attention, block_forward  # noqa: F401,E402
