@@ -11,9 +11,11 @@ from .lact import (  # noqa: F401
     backward_workspace_bytes,
     lact_apply,
     lact_chunked_backward,
+    lact_block_forward,
     lact_chunked_forward,
     lact_chunked_forward_noalloc,
     lact_update,
+    lact_window_attention,
     load_library,
     mfma_path,
     noalloc_scratch_bytes,

@@ -1102,6 +1102,53 @@ int lact_chunked_forward_noalloc(const lact_config* cfg, const lact_state* st, c
 
 size_t lact_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
 
+int lact_window_attention(const lact_config* cfg, const void* Q, const void* K, const void* V, void* O, int64_t T,
+                          int64_t window, float scale, int32_t accumulate, void* stream) {
+  g_last_error.clear();
+  if (cfg == nullptr) return fail(LACT_ERR_INVALID_ARG, "config is NULL");
+  if (cfg->B < 1 || cfg->H < 1) return fail(LACT_ERR_INVALID_ARG, "B=%d H=%d must be >= 1", cfg->B, cfg->H);
+  if (static_cast<int64_t>(cfg->B) * cfg->H > 65535)
+    return fail(LACT_ERR_UNSUPPORTED, "B*H=%lld above 65535", (long long)cfg->B * cfg->H);
+  if (cfg->io_dtype != LACT_F32 && cfg->io_dtype != LACT_BF16)
+    return fail(LACT_ERR_INVALID_ARG, "io_dtype %d unknown", cfg->io_dtype);
+  if (!lact::window_shape_ok(cfg->d))
+    return fail(LACT_ERR_UNSUPPORTED, "window attention: d=%d not in {32, 64, 128}", cfg->d);
+  if (!Q || !K || !V || !O) return fail(LACT_ERR_INVALID_ARG, "Q, K, V, O must be non-NULL");
+  if (T < 1 || window < 1) return fail(LACT_ERR_INVALID_ARG, "T and window must be >= 1");
+  if (!finite(scale)) return fail(LACT_ERR_INVALID_ARG, "scale must be finite");
+  if (accumulate != 0 && accumulate != 1) return fail(LACT_ERR_INVALID_ARG, "accumulate must be 0 or 1");
+  lact::WindowArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.T = T;
+  a.stride = T * cfg->d;
+  a.window = window;
+  a.scale = scale > 0.f ? scale : 1.f / std::sqrt(static_cast<float>(cfg->d));
+  a.accumulate = accumulate;
+  a.P = cfg->B * cfg->H;
+  a.d = cfg->d;
+  a.bf16 = cfg->io_dtype == LACT_BF16;
+  hipError_t e = lact::launch_window_attn(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "window-attention kernel");
+  return LACT_OK;
+}
+
+int lact_block_forward(const lact_config* cfg, const lact_state* st, const void* Q, const void* K, const void* V,
+                       const float* eta, void* O, int64_t T, int64_t chunk, int64_t window, float scale,
+                       int32_t order, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (cfg == nullptr) return fail(LACT_ERR_INVALID_ARG, "config is NULL");
+  if (!lact::window_shape_ok(cfg->d))
+    return fail(LACT_ERR_UNSUPPORTED, "window attention: d=%d not in {32, 64, 128}", cfg->d);
+  if (window < 1) return fail(LACT_ERR_INVALID_ARG, "window must be >= 1");
+  if (!finite(scale)) return fail(LACT_ERR_INVALID_ARG, "scale must be finite");
+  int rc = lact_chunked_forward(cfg, st, Q, K, V, eta, O, T, T, chunk, chunk, order, ws, ws_bytes, stream);
+  if (rc) return rc;
+  return lact_window_attention(cfg, Q, K, V, O, T, window, scale, 1, stream);
+}
+
 size_t lact_backward_workspace_bytes(const lact_config* cfg, int64_t T_kv, int64_t chunk_kv, int64_t chunk_q) {
   Plan p;
   if (check_config(cfg, &p) != LACT_OK || check_backward(cfg, p) != LACT_OK) return 0;

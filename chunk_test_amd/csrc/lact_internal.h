@@ -188,6 +188,21 @@ hipError_t launch_bw_ns(const BwNSArgs& a, hipStream_t s);
 hipError_t launch_bw_copy(float* blocks, const MatRef& m1, const MatRef& m2, const MatRef& m3, int P, int d, int h,
                           bool to_blocks, hipStream_t s);
 
+// ---- causal sliding-window attention (the LaCT block's local half) ----
+struct WindowArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  int64_t T, stride, window;  // stride: elements between pairs
+  float scale;
+  int accumulate;  // O += attention (else O = attention)
+  int P, d;
+  int bf16;
+};
+bool window_shape_ok(int d);
+hipError_t launch_window_attn(const WindowArgs& a, hipStream_t s);
+
 // ---- generic kernels (fp32 arithmetic; any supported d, h) ----
 hipError_t launch_grad_simple(const GradArgs& a, hipStream_t s);
 hipError_t launch_reduce(const ReduceArgs& a, hipStream_t s);

@@ -37,6 +37,7 @@ EXPORTED = (
     "lact_chunked_forward", "lact_status_string", "lact_last_error", "lact_mfma_path",
     "lact_profile_enable", "lact_profile_read", "lact_version", "lact_chunked_forward_noalloc",
     "lact_noalloc_scratch_bytes", "lact_backward_workspace_bytes", "lact_chunked_backward",
+    "lact_window_attention", "lact_block_forward",
 )
 
 
@@ -111,6 +112,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                           c_void_p, c_void_p, c_void_p, P(LactGrads), c_int64, c_int64,
                                           c_int64, c_int64, c_int32, c_void_p, c_size_t, c_void_p]
     lib.lact_chunked_backward.restype = c_int
+    lib.lact_window_attention.argtypes = [P(LactConfig), c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_int64, c_int64, c_float, c_int32, c_void_p]
+    lib.lact_window_attention.restype = c_int
+    lib.lact_block_forward.argtypes = [P(LactConfig), P(LactState), c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_int64, c_int64, c_int64, c_float, c_int32,
+                                       c_void_p, c_size_t, c_void_p]
+    lib.lact_block_forward.restype = c_int
     lib.lact_status_string.argtypes = [c_int]
     lib.lact_status_string.restype = c_char_p
     lib.lact_last_error.argtypes = []
@@ -433,6 +441,43 @@ def lact_chunked_backward(cfg: Config, st: dict, Q, K, V, eta, dO, chunk_kv: int
                                      ctypes.byref(g), T_kv, T_q, chunk_kv, chunk_q, ORDER_CODES[order],
                                      _ptr(ws), ws.numel(), _stream(stream)))
     return out
+
+
+def lact_window_attention(cfg: Config, Q, K, V, O, window: int, scale: float = 0.0,
+                          accumulate: bool = False, stream=None):
+    """O = (or, with accumulate, O +=) causal sliding-window attention of
+    Q, K, V [B,H,T,d]; scale <= 0 means 1/sqrt(d)."""
+    lib = load_library()
+    T = Q.shape[2] if Q is not None and Q.dim() == 4 else -1
+    for name, t in (("Q", Q), ("K", K), ("V", V), ("O", O)):
+        _check_shape(name, t, (cfg.B, cfg.H, T, cfg.d))
+    for name, t in (("Q", Q), ("K", K), ("V", V), ("O", O)):
+        _check_tensor(name, t, _io_dtype(cfg))
+    _same_device([Q, K, V, O])
+    c = cfg.to_c()
+    _check(lib.lact_window_attention(ctypes.byref(c), _ptr(Q), _ptr(K), _ptr(V), _ptr(O), T, window,
+                                     scale, 1 if accumulate else 0, _stream(stream)))
+
+
+def lact_block_forward(cfg: Config, st: dict, Q, K, V, eta, O, chunk: int, window: int, ws,
+                       order: str = "apply_then_update", scale: float = 0.0, stream=None):
+    """The LaCT block on shared Q, K, V [B,H,T,d]: O = window attention + the
+    TTT layer (chunks of `chunk` keys and queries; state updated in place)."""
+    lib = load_library()
+    _state_shapes(cfg, st)
+    T = K.shape[2] if K is not None and K.dim() == 4 else -1
+    for name, t in (("K", K), ("V", V), ("Q", Q), ("O", O)):
+        _check_shape(name, t, (cfg.B, cfg.H, T, cfg.d))
+    _check_shape("eta", eta, _eta_shape(cfg, T))
+    sts = _check_state(cfg, st)
+    for name, t in (("Q", Q), ("K", K), ("V", V), ("O", O)):
+        _check_tensor(name, t, _io_dtype(cfg))
+    _check_eta(cfg, eta, K)
+    _same_device(sts + [Q, K, V, eta, O, ws])
+    c, s = cfg.to_c(), _state(st)
+    _check(lib.lact_block_forward(ctypes.byref(c), ctypes.byref(s), _ptr(Q), _ptr(K), _ptr(V),
+                                  _ptr(eta), _ptr(O), T, chunk, window, scale, ORDER_CODES[order],
+                                  _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def noalloc_scratch_bytes() -> int:

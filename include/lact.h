@@ -216,6 +216,33 @@ int lact_chunked_forward_noalloc(const lact_config* cfg, const lact_state* st,
 /* Size of the allocation-free entry point's scratch array. */
 size_t lact_noalloc_scratch_bytes(void);
 
+/* ---------------------------------------------------------------- the block
+ * The LaCT block ("LaCT: Large Chunk Test-Time Training" review, section
+ * "Local attention and nonlinear memory work together"; project page,
+ * Figure 2): causal sliding-window attention handles the structure inside a
+ * chunk, the TTT layer the history across chunks; the language and video
+ * variants share Q, K, V between the two and add their outputs.
+ *
+ * lact_window_attention: O = attention(Q, K, V) (accumulate = 0) or
+ * O += attention(Q, K, V) (accumulate = 1) for Q, K, V, O [B, H, T, d] of
+ * cfg's io_dtype (pairs T d elements apart), where query t attends the
+ * keys s with t - window < s <= t:
+ *   o_t = sum_s softmax_s(scale q_t . k_s) v_s,  scale <= 0 means 1/sqrt(d).
+ * d in {32, 64, 128}; window >= 1; fp32 arithmetic.  Only B, H, d and
+ * io_dtype of cfg are used.
+ *
+ * lact_block_forward: O = attention(Q, K, V) + TTT(Q, K, V) with one shared
+ * Q, K, V [B, H, T, d]: lact_chunked_forward with T_q = T_kv = T and
+ * chunk_q = chunk_kv = chunk (state updated in place, workspace as for it),
+ * then the window attention added into O, on one stream. */
+int lact_window_attention(const lact_config* cfg, const void* Q, const void* K, const void* V,
+                          void* O, int64_t T, int64_t window, float scale, int32_t accumulate,
+                          void* stream);
+int lact_block_forward(const lact_config* cfg, const lact_state* st, const void* Q, const void* K,
+                       const void* V, const float* eta, void* O, int64_t T, int64_t chunk,
+                       int64_t window, float scale, int32_t order, void* ws, size_t ws_bytes,
+                       void* stream);
+
 /* ------------------------------------------------------------------ backward
  * Training through the layer: the pages' throughput figures are training
  * throughput ("LaCT: Large Chunk Test-Time Training" review, section
