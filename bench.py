@@ -77,16 +77,104 @@ def cpu_baseline(w: S.Workload, x, st, budget_s: float = 15.0):
         if t_used > budget_s:
             break
     tflops = done * per_pair / t_used / 1e12
+    # the float64 parity oracle on one pair of the same workload, for context
+    hp64 = oracle.Hyper(opt=w.opt, beta=w.beta, ns_iters=w.ns_iters, token_block=65536,
+                        norm_keep=w.norm == "keep")
+    t1 = time.perf_counter()
+    oracle.lact_chunked_forward(st, x["Q"], x["K"], x["V"], x["eta"], w.chunk_kv, w.chunk_q,
+                                w.order, hp64, dtype=np.float64, pairs=[pairs[0]])
+    t64 = time.perf_counter() - t1
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round(tflops, 6), "unit": "TFLOP/s", "cores": min(cores, threads), "kind": "oracle",
         "sample": f"{done} of {w.pairs} (batch, head) pairs of the {w.name} workload, full length, "
                   f"float32 NumPy oracle, {t_used:.1f} s",
+        "cpu_model": model,
+        "fp64_oracle": {"value": round(per_pair / t64 / 1e12, 6), "unit": "TFLOP/s",
+                        "sample": f"1 pair, float64 parity oracle, {t64:.1f} s"},
     }
+
+
+def other_mode(args, w, cfg, dev, Q, K, V, eta, O, ws):
+    """--mode backward / block: the step is lact_chunked_backward (given dO and the
+    cotangents of the final weights) or lact_block_forward (shared Q, K, V); one
+    JSON line with tokens/s (no flop count is claimed for these)."""
+    import torch
+    import chunk_test_amd as L
+    if args.mode == "backward":
+        g = torch.Generator(device="cuda").manual_seed(1)
+        dO = torch.randn(Q.shape, generator=g, device="cuda").to(Q.dtype)
+        dWf = {n: 0.1 * torch.randn(dev[n].shape, generator=g, device="cuda") for n in ("W1", "W2", "W3")}
+        st0 = {n: dev[n] for n in ("W1", "W2", "W3")}
+        bws = torch.empty(L.backward_workspace_bytes(cfg, w.T_kv, w.chunk_kv, w.chunk_q), dtype=torch.uint8,
+                          device="cuda")
+
+        def step():
+            L.lact_chunked_backward(cfg, st0, Q, K, V, eta, dO, w.chunk_kv, w.chunk_q, w.order, ws=bws,
+                                    dW_final=dWf)
+        metric = "LaCT layer backward tokens/s"
+    else:
+        if w.T_q != w.T_kv:
+            raise SystemExit("--mode block needs T_q == T_kv (shared Q, K, V)")
+        init = {n: t.clone() for n, t in dev.items()}
+
+        def step():
+            for n, t in dev.items():
+                t.copy_(init[n])
+            L.lact_block_forward(cfg, dev, K, K, V, eta, O, w.chunk_kv, args.window, ws, order=w.order)
+        metric = "LaCT block (window attention + layer) tokens/s"
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    attn = None
+    if args.mode == "block":
+        # the window attention alone: algorithmic flops 4 d per (query, visible key)
+        vis = sum(min(t + 1, args.window) for t in range(w.T_kv))
+        a_flops = 4.0 * w.d * vis * w.pairs
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        for _ in range(args.steps):
+            L.lact_window_attention(cfg, K, K, V, O, args.window)
+        a1.record()
+        torch.cuda.synchronize()
+        a_ms = a0.elapsed_time(a1) / args.steps
+        attn = {"ms": round(a_ms, 5), "flop": a_flops, "tflops": round(a_flops / (a_ms * 1e-3) / 1e12, 3),
+                "peak_frac": round(a_flops / (a_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    line = {
+        "metric": metric, "value": round(w.B * w.T_kv / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.io_dtype == "bf16" else "fp32", "data": "synthetic",
+        "config": {"workload": w.name, "mode": args.mode, "B": w.B, "H": w.H, "d": w.d, "h": w.h,
+                   "T_kv": w.T_kv, "T_q": w.T_q, "chunk_kv": w.chunk_kv, "chunk_q": w.chunk_q,
+                   "order": w.order, "opt": w.opt, "beta": w.beta, "products": w.products,
+                   "window": args.window if args.mode == "block" else None},
+        "wall_s_timed": round(wall, 4), "roofline": None, "cpu_baseline": None,
+        "window_attention": attn,
+    }
+    print(json.dumps(line), flush=True)
 
 
 def main():
@@ -99,6 +187,10 @@ def main():
                     help="variant: updated rows to unit length (default) or kept at their length")
     ap.add_argument("--eta-per-matrix", action="store_true",
                     help="variant: a learning rate per token and matrix (W1, W2, W3)")
+    ap.add_argument("--mode", default="forward", choices=("forward", "backward", "block"),
+                    help="forward: the layer (default); backward: lact_chunked_backward on the "
+                         "same workload; block: window attention + the layer on shared Q, K, V")
+    ap.add_argument("--window", type=int, default=2048, help="attention window of --mode block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -141,6 +233,9 @@ def main():
     def step():
         L.lact_chunked_forward(cfg, dev, Q, K, V, eta, O, w.chunk_kv, w.chunk_q, w.order, ws)
 
+    if args.mode != "forward":
+        return other_mode(args, w, cfg, dev, Q, K, V, eta, O, ws)
+
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -148,29 +243,43 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # every step starts from the initial state: W (and M) are restored before
+    # each step, outside its timed span (the kernels' time depends on the data)
+    init = {n: t.clone() for n, t in dev.items()}
+
+    def reset():
+        for n, t in dev.items():
+            t.copy_(init[n])
+
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
+        reset()
         step()
     torch.cuda.synchronize()
 
     log(f"[bench] timing {args.steps} steps")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        reset()
+        starts[i].record()
         step()
-    e1.record()
+        ends[i].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = e0.elapsed_time(e1) / args.steps
+    step_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    ms = sum(step_ms) / args.steps
 
     # per-phase kernel durations: HIP events recorded by the library on the
-    # launch stream around each phase, over the same number of steps
+    # launch stream around each phase, over as many steps again, right after
+    # the timed ones (the same sustained-load clock regime)
     log("[bench] per-phase event timing")
     L.profile_enable(True)
     L.profile_read()
     for _ in range(args.steps):
+        reset()
         step()
     torch.cuda.synchronize()
     phases = L.profile_read()
@@ -214,6 +323,8 @@ def main():
         "phase_ms_per_step": {k: round(v[0] / args.steps, 5) for k, v in phases.items()},
         "phase_launches_per_step": {k: v[1] / args.steps for k, v in phases.items()},
         "wall_s_timed": round(wall, 4),
+        "ms_per_step_min": round(min(step_ms), 5),
+        "ms_per_step_median": round(sorted(step_ms)[len(step_ms) // 2], 5),
         "roofline": roof,
         "cpu_baseline": None,
     }

@@ -6,7 +6,9 @@
 // t - window < s <= t:
 //   o_t = sum_s softmax_s(scale q_t . k_s) v_s.
 //
-// One workgroup per (64 queries, pair); four threads per query, each owning
+// bf16 at d = 128 runs on the matrix cores (k_window_attn_mfma below); the
+// general kernel (fp32 arithmetic, any supported d and I/O type): one
+// workgroup per (64 queries, pair); four threads per query, each owning
 // d/4 features of q and of the output.  Key/value tiles of 64 tokens go
 // through LDS; per tile the 64 scores of a query are formed first (partial
 // dots reduced over the query's four lanes), then the running maximum and
@@ -99,6 +101,228 @@ __global__ __launch_bounds__(kThreads) void k_window_attn(WindowArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 matrix-core variant for d = 128.  A workgroup of four wavefronts owns
+// 128 consecutive queries of a pair, 32 per wavefront; keys and values of
+// 64-token stages move from HBM straight into double-buffered LDS tiles
+// (global_load_lds, rows of 256 bytes with their 16-byte chunks XOR-swizzled
+// per row).  Per wavefront and 32-key sub-tile, on 32x32x16 MFMAs:
+//   S^T = K Q^T   (A = key rows from LDS, B = the wave's queries, held in
+//                  registers): lane = query, 16 registers = 16 keys;
+//   online softmax in that layout: the running maximum of a query is shared
+//   with the lane holding its other 16 keys (lane ^ 32); p = 2^(s c - m),
+//   c = scale log2(e); the output is rescaled only when some maximum grew;
+//   O^T += V^T P^T  (A = value columns from LDS transpose reads, B = p as
+//                  bf16 in the same key order): lane = query, registers =
+//                  features, so the rescale is per lane.
+// Masks are applied only on sub-tiles that cross the diagonal or the
+// window's lower edge; sub-tiles outside every query's window are skipped.
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_t;
+
+namespace mf {
+constexpr int D = 128;
+constexpr int KS = D / 16;   // k-steps of S^T = K Q^T
+constexpr int NT = D / 32;   // 32-feature tiles of the output
+constexpr int ROW = 2 * D;   // bytes per token row
+constexpr int TT = 64;       // keys per stage
+constexpr int TILE = TT * ROW;
+constexpr int QW = 128;      // queries per workgroup
+
+// XOR swizzle of the sixteen 16-byte chunks of row r (r_i: bit i of r):
+// conflict-free 16-byte row reads over 16 consecutive rows and 8-byte
+// transpose reads over four rows 4m .. 4m + 3 (see the d = 128 chunk-gradient
+// kernel, which uses the same tile layout).
+__device__ __forceinline__ int swz(int r) {
+  return 8 * ((r >> 1) & 1) + 4 * ((r ^ (r >> 3)) & 1) + 2 * (r & 1) + ((r >> 2) & 1);
+}
+}  // namespace mf
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_window_attn_mfma(WindowArgs a) {
+  using namespace mf;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[4 * TILE];  // K[2], V[2]
+  const int pair = blockIdx.y;
+  const int64_t q0 = static_cast<int64_t>(blockIdx.x) * QW;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int g = lane >> 5;
+  const int ln = lane & 31;
+  const int64_t base = static_cast<int64_t>(pair) * a.stride;
+  const uint16_t* Qg = static_cast<const uint16_t*>(a.Q) + base;
+  const uint16_t* Kg = static_cast<const uint16_t*>(a.K) + base;
+  const uint16_t* Vg = static_cast<const uint16_t*>(a.V) + base;
+  const int T = static_cast<int>(a.T);
+  const int W = static_cast<int>(a.window < a.T ? a.window : a.T);
+  const int qw0 = static_cast<int>(q0) + 32 * wv;  // this wave's first query
+  const int myq = qw0 + ln;
+  const float c = a.scale * 1.4426950408889634f;   // scores to base-2 exponents
+
+  // this wave's queries as B operands: lane holds query qw0 + ln, features
+  // 16 ks + 8 g .. +7 (queries past the end re-read the last one)
+  bf16x8_t qb[KS];
+  {
+    const int qr = myq < T ? myq : T - 1;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qb[ks] = *reinterpret_cast<const bf16x8_t*>(Qg + static_cast<int64_t>(qr) * D + 16 * ks + 8 * g);
+  }
+
+  f32x16_t o[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+
+  // stage range: keys any query of the workgroup can see
+  const int q_hi = static_cast<int>(q0) + QW - 1 < T - 1 ? static_cast<int>(q0) + QW - 1 : T - 1;
+  int k_begin = static_cast<int>(q0) - W + 1;
+  if (k_begin < 0) k_begin = 0;
+  k_begin = (k_begin / TT) * TT;
+  const int k_end = q_hi + 1;  // exclusive
+
+  auto dma_stage = [&](int k0, int b) {
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+#pragma unroll
+    for (int k = 0; k < TT / 16; ++k) {
+      const int piece = 4 * k + wv;
+      const int r = 4 * piece + (lane >> 4);
+      const int cl = (lane & 15) ^ swz(r);
+      const int tok = k0 + r < T ? k0 + r : T - 1;
+      const unsigned off = static_cast<unsigned>(tok) * D + 8 * cl;
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Kg + off), (lds_ptr_t)(lds + b * TILE + 1024 * piece), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Vg + off), (lds_ptr_t)(lds + (2 + b) * TILE + 1024 * piece), 16, 0,
+                                       0);
+    }
+  };
+
+  // operand addresses (lane constants plus immediates)
+  int ak_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) ak_off[ks] = ln * ROW + 16 * ((2 * ks + g) ^ swz(ln));
+  const int tq = lane >> 4, tk = (lane >> 2) & 3, ta = lane & 3;
+  int tr_off[2][2];
+  {
+    const int tl = 4 * (tq >> 1) + tk;
+    const int r0 = tl & 1, r1 = (tl >> 1) & 1, r2 = (tl >> 2) & 1;
+    const int low = (2 * (tq & 1) + (ta >> 1)) ^ (2 * r0 + r2);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+#pragma unroll
+      for (int n1 = 0; n1 < 2; ++n1)
+        tr_off[x][n1] = tl * ROW + 16 * (8 * (n1 ^ r1) + 4 * (x ^ r0) + low) + 8 * (ta & 1);
+    }
+  }
+
+  if (k_begin < k_end) dma_stage(k_begin, 0);
+  int b = 0;
+  for (int k0 = k_begin; k0 < k_end; k0 += TT, b ^= 1) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this stage has landed
+    __syncthreads();
+    if (k0 + TT < k_end) dma_stage(k0 + TT, b ^ 1);
+    const unsigned char* kb = lds + b * TILE;
+    const unsigned char* vb = lds + (2 + b) * TILE;
+#pragma unroll 1
+    for (int st = 0; st < TT / 32; ++st) {
+      const int kb0 = k0 + 32 * st;  // first key of the sub-tile
+      // skipped when outside every window of this wave's queries
+      if (kb0 > qw0 + 31 || kb0 + 31 < qw0 - W + 1 || kb0 >= T) continue;
+      f32x16_t s;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+      bf16x8_t ak[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ak[ks] = *reinterpret_cast<const bf16x8_t*>(kb + ak_off[ks] + 8192 * st);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], qb[ks], s, 0, 0, 0);
+      // value operands of this sub-tile (read while the scores complete)
+      bf16x8_t vt[2][NT];
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          s16x4_t t2[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int off = tr_off[(nt & 1) ^ hh][nt >> 1] + 8192 * st + 4096 * hs + 2048 * hh;
+            t2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(vb + off));
+          }
+          vt[hs][nt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t2[0], t2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      }
+      // register r holds key kb0 + 8 (r / 4) + 4 g + r % 4 of query myq
+      const bool edge = (kb0 + 31 > qw0) || (kb0 < qw0 + 31 - W + 1);
+      if (edge) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (!(key <= myq && key > myq - W)) s[r] = -INFINITY;
+        }
+      }
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m, mx * c);  // running maximum, base-2 units (-inf: nothing seen yet)
+      if (__any(mn != m)) {
+        const float corr = (mn == m) ? 1.f : exp2f(m - mn);  // 0 on the first visible sub-tile
+        l *= corr;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[t][r] *= corr;
+        }
+        m = mn;
+      }
+      bf16x8_t p[2];
+      const float mm = (m == -INFINITY) ? 0.f : m;  // (then every score of the lane is -inf: p = 0)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[r], c, -mm));
+        l += e;
+        p[r >> 3][r & 7] = static_cast<__bf16>(e);
+      }
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[hs][nt], p[hs], o[nt], 0, 0, 0);
+      }
+    }
+  }
+  l += __shfl_xor(l, 32, 64);
+  if (myq >= T) return;
+  const float inv = 1.f / l;
+  uint16_t* Og = static_cast<uint16_t*>(a.O) + base + static_cast<int64_t>(myq) * D;
+  // register r of tile nt: feature 32 nt + 8 (r / 4) + 4 g + r % 4 (four consecutive per group)
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int f = 32 * nt + 8 * rg + 4 * g;
+      bf16x4_t v4;
+      if (a.accumulate) v4 = *reinterpret_cast<const bf16x4_t*>(Og + f);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = o[nt][4 * rg + i] * inv;
+        if (a.accumulate) v += static_cast<float>(v4[i]);
+        v4[i] = static_cast<__bf16>(v);
+      }
+      *reinterpret_cast<bf16x4_t*>(Og + f) = v4;
+    }
+  }
+}
+
 template <int D>
 hipError_t launch_d(const WindowArgs& a, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((a.T + kQ - 1) / kQ), a.P);
@@ -115,6 +339,13 @@ hipError_t launch_d(const WindowArgs& a, hipStream_t s) {
 bool window_shape_ok(int d) { return d == 32 || d == 64 || d == 128; }
 
 hipError_t launch_window_attn(const WindowArgs& a, hipStream_t s) {
+  const bool aligned = ((reinterpret_cast<uintptr_t>(a.Q) | reinterpret_cast<uintptr_t>(a.K) |
+                         reinterpret_cast<uintptr_t>(a.V) | reinterpret_cast<uintptr_t>(a.O)) & 15) == 0;
+  if (a.bf16 && a.d == mf::D && aligned && a.T * a.d < (int64_t(1) << 31)) {
+    const dim3 grid(static_cast<unsigned>((a.T + mf::QW - 1) / mf::QW), a.P);
+    hipLaunchKernelGGL(k_window_attn_mfma, grid, dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+  }
   switch (a.d) {
     case 32: return launch_d<32>(a, s);
     case 64: return launch_d<64>(a, s);

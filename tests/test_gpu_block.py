@@ -26,6 +26,12 @@ def attention_case(B, H, T, d, io, seed):
     (1, 2, 200, 128, "fp32", 1000, 0.0),   # window longer than the sequence: causal attention
     (1, 2, 3000, 128, "bf16", 2048, 0.0),  # the 760M language model's window
     (1, 3, 1100, 64, "bf16", 129, 2.0),
+    # the matrix-core kernel (bf16, d = 128): ragged lengths, windows shorter than a
+    # 32-key sub-tile, the identity window, a window longer than the sequence
+    (1, 2, 1000, 128, "bf16", 1, 0.0),
+    (1, 2, 777, 128, "bf16", 33, 0.5),
+    (2, 1, 300, 128, "bf16", 100000, 0.0),
+    (1, 1, 4100, 128, "bf16", 4096, 0.0),
 ])
 def test_window_attention_parity(B, H, T, d, io, window, scale):
     import torch
