@@ -628,6 +628,7 @@ hipError_t launch_bw_tok(const BwTokArgs& a, bool apply, hipStream_t s) {
 }
 
 hipError_t launch_bw_contract(const BwContractArgs& a, hipStream_t s) {
+  if (bw_contract_mfma_ok(a)) return launch_bw_contract_mfma(a, s);
   switch (a.d) {
     case 32: return launch_contract_d<32>(a, s);
     case 64: return launch_contract_d<64>(a, s);

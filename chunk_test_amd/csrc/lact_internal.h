@@ -180,6 +180,9 @@ struct BwNSArgs {
 bool backward_shape_ok(int d, int h);
 hipError_t launch_bw_tok(const BwTokArgs& a, bool apply, hipStream_t s);
 hipError_t launch_bw_contract(const BwContractArgs& a, hipStream_t s);
+// the bf16 matrix-core contraction (d = 128, h a multiple of 128, 16-byte aligned inputs)
+bool bw_contract_mfma_ok(const BwContractArgs& a);
+hipError_t launch_bw_contract_mfma(const BwContractArgs& a, hipStream_t s);
 hipError_t launch_bw_reduce_add(float* dst, const float* partials, int S, int64_t per, int P, hipStream_t s);
 hipError_t launch_bw_step(const BwStepArgs& a, hipStream_t s);
 hipError_t launch_bw_momentum(const float* t, float* dM, float* Pout, float beta, int64_t total, hipStream_t s);

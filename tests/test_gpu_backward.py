@@ -74,6 +74,10 @@ CASES += [
                               chunk_q=1024),
     S.WORKLOADS["video"].replace(name="bw-video-split", H=1, T_kv=3 * 1024, chunk_kv=1024,
                                  T_q=3 * 1024, chunk_q=1024),
+    # bf16 at d = 128 with chunks that are no multiple of the 32-token stages
+    # (ragged last stage and split in the matrix-core contractions)
+    S.WORKLOADS["lm"].replace(name="bw-lm-bf16-ragged", B=1, H=2, T_kv=3 * 1000, chunk_kv=1000,
+                              T_q=3 * 200, chunk_q=200, order="update_then_apply"),
 ]
 
 
