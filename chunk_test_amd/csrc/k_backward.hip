@@ -619,6 +619,7 @@ hipError_t launch_contract_d(const BwContractArgs& a, hipStream_t s) {
 bool backward_shape_ok(int d, int h) { return (d == 32 || d == 64 || d == 128) && h % kHS == 0 && h >= kHS && h <= 1024; }
 
 hipError_t launch_bw_tok(const BwTokArgs& a, bool apply, hipStream_t s) {
+  if (bw_tok_mfma_ok(a, apply)) return launch_bw_tok_mfma(a, apply, s);
   switch (a.d) {
     case 32: return launch_tok_d<32>(a, apply, s);
     case 64: return launch_tok_d<64>(a, apply, s);

@@ -18,6 +18,14 @@
 // tokens (A, B, the rates and the three factor rows of the slice) moves from
 // HBM into double-buffered LDS with global_load_lds one stage ahead; A and B
 // enter the products through LDS transpose reads (tokens as the k index).
+//
+// The query read's token-local VJP runs here too (k_bw_apply_mfma): per query
+// q and hidden unit j, with h1 = W1 q, h3 = W3 q, ob = (dO W2)_j,
+//   X1 = ob h3 silu'(h1),  X2 = silu(h1) h3,  X3 = ob silu(h1),
+//   dq = W1^T X1 + W3^T X3,
+// the three projections and dq as split-operand MFMAs (the weights enter as
+// bf16 hi + lo operands prepared once per call by k_bw_ops, the queries and
+// output cotangents exactly), the element math in fp32.
 #include "lact_device.h"
 #include "lact_internal.h"
 
@@ -28,6 +36,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_t;
@@ -252,6 +261,422 @@ void k_bw_contract_mfma(BwContractArgs a, int hsl, int nbase) {
   }
 }
 
+
+// Operands of the token kernels: every matrix as bf16 hi and lo parts in
+// [hidden unit][feature] order (W2 and P2, stored [feature][hidden unit], are
+// transposed): op[pair][m][hl][j][e], m over W1, W3, W2 (and P1, P3, P2).
+__global__ __launch_bounds__(kThreads) void k_bw_ops(BwOpsArgs a) {
+  const int64_t hd = static_cast<int64_t>(a.h) * D;
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t total = static_cast<int64_t>(a.P) * a.nm * hd;
+  if (idx >= total) return;
+  const int64_t pm = idx / hd, e_idx = idx % hd;
+  const int pair = static_cast<int>(pm / a.nm), m = static_cast<int>(pm % a.nm);
+  const int j = static_cast<int>(e_idx / D), e = static_cast<int>(e_idx % D);
+  const MatRef& r = a.m[m];
+  const bool tr = (m % 3) == 2;  // W2, P2: stored [D][h]
+  const float x = r.p[pair * r.pair_stride + (tr ? static_cast<int64_t>(e) * a.h + j : e_idx)];
+  const __bf16 hi = static_cast<__bf16>(x);
+  const __bf16 lo = static_cast<__bf16>(x - static_cast<float>(hi));
+  __bf16* o = reinterpret_cast<__bf16*>(a.op) + pair * a.op_stride + static_cast<int64_t>(m) * 2 * hd;
+  o[e_idx] = hi;
+  o[hd + e_idx] = lo;
+}
+
+constexpr int KS = D / 16;           // k-steps over the features
+constexpr int QWG = 128;             // queries per workgroup (32 per wave)
+constexpr int JT = 32;               // hidden units per weight tile
+constexpr int WHALF = JT * ROW;      // one matrix part (hi or lo) of a tile: 8 KiB
+constexpr int WTILE3 = 6 * WHALF;    // W1, W3, W2^T, hi and lo
+
+__device__ __forceinline__ float sigmoid_fast(float z) {
+  return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_bw_apply_mfma(BwTokArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * WTILE3];
+  const int pair = blockIdx.y;
+  const int64_t tb = static_cast<int64_t>(blockIdx.x) * QWG;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int g = lane >> 5;
+  const int ln = lane & 31;
+  const int h = a.h;
+  const int ntile = h / JT;
+  const int64_t hd = static_cast<int64_t>(h) * D;
+  const uint16_t* opg = a.op + pair * a.op_stride;
+
+  // this lane's query (past the end: the last one, outputs dropped) as the
+  // B operand of the projections: features 16 ks + 8 g .. +7
+  const int64_t t = tb + 32 * wave + ln;
+  const int64_t tcl = t < a.n ? t : a.n - 1;
+  bf16x8_t qop[KS], oop[KS];
+  {
+    const uint16_t* Qg = static_cast<const uint16_t*>(a.A) + pair * a.in_stride + tcl * D;
+    const uint16_t* Og = static_cast<const uint16_t*>(a.B) + pair * a.in_stride + tcl * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qop[ks] = *reinterpret_cast<const bf16x8_t*>(Qg + 16 * ks + 8 * g);
+      oop[ks] = *reinterpret_cast<const bf16x8_t*>(Og + 16 * ks + 8 * g);
+    }
+  }
+
+  // DMA of weight tile jt (rows 32 jt .. +31 of the six parts) into buffer b:
+  // 48 pieces of 1 KiB (four rows), lane l landing at byte 16 l (row
+  // 4 (piece % 8) + l / 16, physical chunk l % 16 holding chunk (l % 16) ^ swz(row))
+  auto dma_w = [&](int jt, int b) {
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+#pragma unroll
+    for (int k = 0; k < 12; ++k) {
+      const int piece = 4 * k + wv;
+      const int part = piece >> 3;
+      const int r = 4 * (piece & 7) + (lane >> 4);
+      const int cl = (lane & 15) ^ swz(r);
+      const uint16_t* src = opg + part * hd + static_cast<int64_t>(JT * jt + r) * D + 8 * cl;
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(lds + b * WTILE3 + part * WHALF + 1024 * (piece & 7)),
+                                       16, 0, 0);
+    }
+  };
+
+  // row reads of a part (lane = hidden unit ln of the tile, features
+  // 16 ks + 8 g .. +7) and transpose reads (lane = feature 32 nt + ln, slot i
+  // = hidden unit 16 s + 8 (i / 4) + 4 g + i % 4 of the tile)
+  int ak_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) ak_off[ks] = ln * ROW + 16 * ((2 * ks + g) ^ swz(ln));
+  const int tq = lane >> 4, tk = (lane >> 2) & 3, ta = lane & 3;
+  int tr_off[2][2];
+  {
+    const int tl = 4 * (tq >> 1) + tk;
+    const int r0 = tl & 1, r1 = (tl >> 1) & 1, r2 = (tl >> 2) & 1;
+    const int low = (2 * (tq & 1) + (ta >> 1)) ^ (2 * r0 + r2);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+#pragma unroll
+      for (int n1 = 0; n1 < 2; ++n1)
+        tr_off[x][n1] = tl * ROW + 16 * (8 * (n1 ^ r1) + 4 * (x ^ r0) + low) + 8 * (ta & 1);
+    }
+  }
+  auto tr_read = [&](const unsigned char* base, int nt, int s) {
+    s16x4_t t2[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      t2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t)(base + tr_off[(nt & 1) ^ hh][nt >> 1] + 4096 * s + 2048 * hh));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t2[0], t2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  f32x16_t dq[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[nt][r] = 0.f;
+  }
+  float* X1 = a.X1 + pair * a.x_stride + t * h;
+  float* X2 = a.X2 + pair * a.x_stride + t * h;
+  float* X3 = a.X3 + pair * a.x_stride + t * h;
+  const bool live = t < a.n;
+
+  dma_w(0, 0);
+  for (int jt = 0; jt < ntile; ++jt) {
+    const int b = jt & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile jt has landed
+    __syncthreads();
+    if (jt + 1 < ntile) dma_w(jt + 1, b ^ 1);
+    const unsigned char* w1h = lds + b * WTILE3;
+    const unsigned char* w1l = w1h + WHALF;
+    const unsigned char* w3h = w1h + 2 * WHALF;
+    const unsigned char* w3l = w1h + 3 * WHALF;
+    const unsigned char* w2h = w1h + 4 * WHALF;
+    const unsigned char* w2l = w1h + 5 * WHALF;
+    // projections, transposed: c[j][query] (lane = query, register r =
+    // hidden unit 8 (r / 4) + 4 g + r % 4 of the tile)
+    f32x16_t c1, c3, cb;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c1[r] = c3[r] = cb[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(w1h + ak_off[ks]);
+      const bf16x8_t l1 = *reinterpret_cast<const bf16x8_t*>(w1l + ak_off[ks]);
+      const bf16x8_t a3 = *reinterpret_cast<const bf16x8_t*>(w3h + ak_off[ks]);
+      const bf16x8_t l3 = *reinterpret_cast<const bf16x8_t*>(w3l + ak_off[ks]);
+      const bf16x8_t a2 = *reinterpret_cast<const bf16x8_t*>(w2h + ak_off[ks]);
+      const bf16x8_t l2 = *reinterpret_cast<const bf16x8_t*>(w2l + ak_off[ks]);
+      c1 = mfma32(a1, qop[ks], c1);
+      c3 = mfma32(a3, qop[ks], c3);
+      cb = mfma32(a2, oop[ks], cb);
+      c1 = mfma32(l1, qop[ks], c1);
+      c3 = mfma32(l3, qop[ks], c3);
+      cb = mfma32(l2, oop[ks], cb);
+    }
+    // element math; x1 = X1, x3 = X3 (the operands of dq), G
+    float x1[16], x3[16], gg[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float h1 = c1[r], h3 = c3[r], ob = cb[r];
+      const float sg = sigmoid_fast(h1);
+      const float act = h1 * sg;
+      x3[r] = ob * act;
+      x1[r] = ob * h3 * (sg * (1.f + h1 * (1.f - sg)));
+      gg[r] = act * h3;
+    }
+    if (live) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int j = JT * jt + 8 * rg + 4 * g;
+        *reinterpret_cast<f32x4_t*>(X1 + j) = f32x4_t{x1[4 * rg], x1[4 * rg + 1], x1[4 * rg + 2], x1[4 * rg + 3]};
+        *reinterpret_cast<f32x4_t*>(X2 + j) = f32x4_t{gg[4 * rg], gg[4 * rg + 1], gg[4 * rg + 2], gg[4 * rg + 3]};
+        *reinterpret_cast<f32x4_t*>(X3 + j) = f32x4_t{x3[4 * rg], x3[4 * rg + 1], x3[4 * rg + 2], x3[4 * rg + 3]};
+      }
+    }
+    // dq[e][query] += sum over the tile's hidden units of W1[j][e] X1 + W3[j][e] X3
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8_t b1h, b1l, b3h, b3l;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        b1h[i] = static_cast<__bf16>(x1[8 * s + i]);
+        b1l[i] = static_cast<__bf16>(x1[8 * s + i] - static_cast<float>(b1h[i]));
+        b3h[i] = static_cast<__bf16>(x3[8 * s + i]);
+        b3l[i] = static_cast<__bf16>(x3[8 * s + i] - static_cast<float>(b3h[i]));
+      }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const bf16x8_t o1h = tr_read(w1h, nt, s), o1l = tr_read(w1l, nt, s);
+        const bf16x8_t o3h = tr_read(w3h, nt, s), o3l = tr_read(w3l, nt, s);
+        dq[nt] = mfma32(o1h, b1h, dq[nt]);
+        dq[nt] = mfma32(o3h, b3h, dq[nt]);
+        dq[nt] = mfma32(o1h, b1l, dq[nt]);
+        dq[nt] = mfma32(o3h, b3l, dq[nt]);
+        dq[nt] = mfma32(o1l, b1h, dq[nt]);
+        dq[nt] = mfma32(o3l, b3h, dq[nt]);
+      }
+    }
+  }
+  // dq (lane = query, register r = feature 32 nt + 8 (r / 4) + 4 g + r % 4)
+  if (live) {
+    uint16_t* dQ = static_cast<uint16_t*>(a.dA) + pair * a.out_stride + t * D;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        bf16x4_t v4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v4[i] = static_cast<__bf16>(dq[nt][4 * rg + i]);
+        *reinterpret_cast<bf16x4_t*>(dQ + 32 * nt + 8 * rg + 4 * g) = v4;
+      }
+    }
+  }
+}
+
+constexpr int WTILE6 = 12 * WHALF;  // W1, W3, W2^T, P1, P3, P2^T, hi and lo: 96 KiB
+
+// Token-local VJP of the chunk gradient on MFMA: per key k (value v, rate
+// eta) and hidden unit j, with u = -eta v,
+//   h1 = W1 k, h3 = W3 k, dg = (u W2)_j, p1 = P1 k, p3 = P3 k, gb = (u P2)_j
+// (P: the cotangents reaching the chunk gradient), the factors
+//   X2 = p3 a + p1 h3 s1,  X3 = p1 dg s1 + gb a,
+//   X1 = p1 dg h3 s2 + (p3 dg + gb h3) s1
+// (a = silu(h1), s1 = silu'(h1), s2 = silu''(h1)) and the per-token sums
+//   ubar = P2 G + W2 X2  (G = a h3),
+//   kbar = P1^T dH1 + P3^T dH3 + W1^T X1 + W3^T X3  (dH1 = dg h3 s1, dH3 = dg a),
+// giving dk = kbar, dv = -eta ubar, deta = -ubar . v.  Six projections and
+// six token-side products per weight tile, all split-operand MFMAs; the
+// weight tile (twelve bf16 parts) is one LDS buffer, refilled after every
+// wave has finished with it.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_bw_grad_mfma(BwTokArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[WTILE6];
+  const int pair = blockIdx.y;
+  const int64_t tb = static_cast<int64_t>(blockIdx.x) * QWG;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int g = lane >> 5;
+  const int ln = lane & 31;
+  const int h = a.h;
+  const int ntile = h / JT;
+  const int64_t hd = static_cast<int64_t>(h) * D;
+  const uint16_t* opg = a.op + pair * a.op_stride;
+
+  const int64_t t = tb + 32 * wave + ln;
+  const bool live = t < a.n;
+  const int64_t tcl = live ? t : a.n - 1;
+  const uint16_t* Kg = static_cast<const uint16_t*>(a.A) + pair * a.in_stride + tcl * D;
+  const uint16_t* Vg = static_cast<const uint16_t*>(a.B) + pair * a.in_stride + tcl * D;
+  bf16x8_t kop[KS], vop[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    kop[ks] = *reinterpret_cast<const bf16x8_t*>(Kg + 16 * ks + 8 * g);
+    vop[ks] = *reinterpret_cast<const bf16x8_t*>(Vg + 16 * ks + 8 * g);
+  }
+  const float ne = live ? -a.eta[pair * a.eta_stride + t] : 0.f;
+
+  auto dma_w = [&](int jt) {
+    int lane = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane));
+#pragma unroll
+    for (int k = 0; k < 24; ++k) {
+      const int piece = 4 * k + wv;
+      const int part = piece >> 3;
+      const int r = 4 * (piece & 7) + (lane >> 4);
+      const int cl = (lane & 15) ^ swz(r);
+      const uint16_t* src = opg + part * hd + static_cast<int64_t>(JT * jt + r) * D + 8 * cl;
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(lds + part * WHALF + 1024 * (piece & 7)), 16, 0, 0);
+    }
+  };
+
+  int ak_off[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) ak_off[ks] = ln * ROW + 16 * ((2 * ks + g) ^ swz(ln));
+  const int tq = lane >> 4, tk = (lane >> 2) & 3, ta = lane & 3;
+  int tr_off[2][2];
+  {
+    const int tl = 4 * (tq >> 1) + tk;
+    const int r0 = tl & 1, r1 = (tl >> 1) & 1, r2 = (tl >> 2) & 1;
+    const int low = (2 * (tq & 1) + (ta >> 1)) ^ (2 * r0 + r2);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+#pragma unroll
+      for (int n1 = 0; n1 < 2; ++n1)
+        tr_off[x][n1] = tl * ROW + 16 * (8 * (n1 ^ r1) + 4 * (x ^ r0) + low) + 8 * (ta & 1);
+    }
+  }
+  auto tr_read = [&](const unsigned char* base, int nt, int s) {
+    s16x4_t t2[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      t2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_s16x4_t)(base + tr_off[(nt & 1) ^ hh][nt >> 1] + 4096 * s + 2048 * hh));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t2[0], t2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto part = [&](int m, int hl) { return static_cast<const unsigned char*>(lds + (2 * m + hl) * WHALF); };
+
+  f32x16_t ub[NT], kb[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ub[nt][r] = kb[nt][r] = 0.f;
+  }
+  float* X1 = a.X1 + pair * a.x_stride + t * h;
+  float* X2 = a.X2 + pair * a.x_stride + t * h;
+  float* X3 = a.X3 + pair * a.x_stride + t * h;
+
+  dma_w(0);
+  for (int jt = 0; jt < ntile; ++jt) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile jt has landed
+    __syncthreads();
+    // the six projections, transposed (lane = key, register r = hidden unit
+    // 8 (r / 4) + 4 g + r % 4 of the tile); m: W1, W3, W2^T, P1, P3, P2^T
+    f32x16_t c[6];
+#pragma unroll
+    for (int m = 0; m < 6; ++m) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) c[m][r] = 0.f;
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int m = 0; m < 6; ++m) {
+        const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(part(m, 0) + ak_off[ks]);
+        const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(part(m, 1) + ak_off[ks]);
+        const bf16x8_t bo = (m == 2 || m == 5) ? vop[ks] : kop[ks];
+        c[m] = mfma32(ah, bo, c[m]);
+        c[m] = mfma32(al, bo, c[m]);
+      }
+    }
+    // element math (fp32)
+    float x1[16], x2[16], x3[16], dh1[16], dh3[16], gg[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float h1 = c[0][r], h3 = c[1][r], dg = ne * c[2][r];
+      const float p1 = c[3][r], p3 = c[4][r], gb = ne * c[5][r];
+      const float sg = sigmoid_fast(h1);
+      const float act = h1 * sg;
+      const float s1 = sg * (1.f + h1 * (1.f - sg));
+      const float s2 = sg * (1.f - sg) * (2.f + h1 * (1.f - 2.f * sg));
+      x2[r] = p3 * act + p1 * h3 * s1;
+      const float ab = p3 * dg + gb * h3;
+      x3[r] = p1 * dg * s1 + gb * act;
+      x1[r] = p1 * dg * h3 * s2 + ab * s1;
+      dh1[r] = dg * h3 * s1;
+      dh3[r] = dg * act;
+      gg[r] = act * h3;
+    }
+    if (live) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int j = JT * jt + 8 * rg + 4 * g;
+        *reinterpret_cast<f32x4_t*>(X1 + j) = f32x4_t{x1[4 * rg], x1[4 * rg + 1], x1[4 * rg + 2], x1[4 * rg + 3]};
+        *reinterpret_cast<f32x4_t*>(X2 + j) = f32x4_t{x2[4 * rg], x2[4 * rg + 1], x2[4 * rg + 2], x2[4 * rg + 3]};
+        *reinterpret_cast<f32x4_t*>(X3 + j) = f32x4_t{x3[4 * rg], x3[4 * rg + 1], x3[4 * rg + 2], x3[4 * rg + 3]};
+      }
+    }
+    // token-side sums over the tile's hidden units
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      // B operands (lane = key, slot i = hidden unit 16 s + 8 (i / 4) + 4 g + i % 4)
+      bf16x8_t bh[6], bl[6];  // G, X2 (for ubar); dH1, dH3, X1, X3 (for kbar)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float v6[6] = {gg[8 * s + i], x2[8 * s + i], dh1[8 * s + i], dh3[8 * s + i], x1[8 * s + i], x3[8 * s + i]};
+#pragma unroll
+        for (int q = 0; q < 6; ++q) {
+          bh[q][i] = static_cast<__bf16>(v6[q]);
+          bl[q][i] = static_cast<__bf16>(v6[q] - static_cast<float>(bh[q][i]));
+        }
+      }
+      // matrix of each B operand: P2^T, W2^T (ubar); P1, P3, W1, W3 (kbar)
+      constexpr int mat[6] = {5, 2, 3, 4, 0, 1};
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int q = 0; q < 6; ++q) {
+          const bf16x8_t oh = tr_read(part(mat[q], 0), nt, s), ol = tr_read(part(mat[q], 1), nt, s);
+          f32x16_t& acc = q < 2 ? ub[nt] : kb[nt];
+          acc = mfma32(oh, bh[q], acc);
+          acc = mfma32(oh, bl[q], acc);
+          acc = mfma32(ol, bh[q], acc);
+        }
+      }
+    }
+    __syncthreads();  // every wave is done with tile jt
+    if (jt + 1 < ntile) dma_w(jt + 1);
+  }
+  // outputs (lane = key, register r = feature 32 nt + 8 (r / 4) + 4 g + r % 4)
+  if (live) {
+    uint16_t* dK = static_cast<uint16_t*>(a.dA) + pair * a.out_stride + t * D;
+    uint16_t* dV = static_cast<uint16_t*>(a.dB) + pair * a.out_stride + t * D;
+    const uint16_t* Vr = static_cast<const uint16_t*>(a.B) + pair * a.in_stride + t * D;
+    float de = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int f = 32 * nt + 8 * rg + 4 * g;
+        const bf16x4_t v4 = *reinterpret_cast<const bf16x4_t*>(Vr + f);
+        bf16x4_t k4, w4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float u = ub[nt][4 * rg + i];
+          k4[i] = static_cast<__bf16>(kb[nt][4 * rg + i]);
+          w4[i] = static_cast<__bf16>(ne * u);
+          de -= u * static_cast<float>(v4[i]);
+        }
+        *reinterpret_cast<bf16x4_t*>(dK + f) = k4;
+        *reinterpret_cast<bf16x4_t*>(dV + f) = w4;
+      }
+    }
+    de += __shfl_xor(de, 32, 64);
+    if (g == 0) a.deta[pair * a.deta_stride + t] = de;  // (both halves of a key are live or not)
+  }
+}
+
 }  // namespace
 
 bool bw_contract_mfma_ok(const BwContractArgs& a) {
@@ -267,6 +692,37 @@ hipError_t launch_bw_contract_mfma(const BwContractArgs& a, hipStream_t s) {
   const int nbase = a.S * a.P;
   const int blocks = ((nbase + 7) / 8) * 8 * hsl;
   hipLaunchKernelGGL(k_bw_contract_mfma, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  return hipGetLastError();
+}
+
+}  // namespace lact
+
+namespace lact {
+
+bool bw_tok_mfma_ok(const BwTokArgs& a, bool apply) {
+  const uintptr_t al = reinterpret_cast<uintptr_t>(a.A) | reinterpret_cast<uintptr_t>(a.B) |
+                       reinterpret_cast<uintptr_t>(a.X1) | reinterpret_cast<uintptr_t>(a.X2) |
+                       reinterpret_cast<uintptr_t>(a.X3) | reinterpret_cast<uintptr_t>(a.dA) |
+                       reinterpret_cast<uintptr_t>(a.op);
+  const uintptr_t al2 = apply ? 0 : reinterpret_cast<uintptr_t>(a.dB);
+  return a.op != nullptr && a.bf16 && a.d == D && a.h % JT == 0 && ((al | al2) & 15) == 0 && (a.in_stride % 8) == 0 &&
+         (a.out_stride % 8) == 0 && (a.x_stride % 4) == 0 && (apply || a.eta != nullptr);
+}
+
+hipError_t launch_bw_ops(const BwOpsArgs& a, hipStream_t s) {
+  if (a.d != D || a.nm < 1 || a.nm > 6 || a.op_stride < static_cast<int64_t>(2) * a.nm * a.h * D) return hipErrorInvalidValue;
+  const int64_t total = static_cast<int64_t>(a.P) * a.nm * a.h * D;
+  hipLaunchKernelGGL(k_bw_ops, dim3(static_cast<unsigned>((total + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_tok_mfma(const BwTokArgs& a, bool apply, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((a.n + QWG - 1) / QWG), a.P);
+  if (apply) {
+    hipLaunchKernelGGL(k_bw_apply_mfma, grid, dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(k_bw_grad_mfma, grid, dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -640,6 +640,7 @@ struct BwLayout {
   size_t X = 0;           // three [P, max(chunk_kv, chunk_q), h] factor arrays
   size_t part = 0;        // contraction partials [P, S, 3hd]
   size_t ns = 0;          // Newton-Schulz VJP scratch
+  size_t op = 0;          // bf16 hi | lo operands of the matrix-core token kernels [P][6][2][h][d]
   size_t total = 0;
   int64_t rows = 0;       // max(chunk_kv, chunk_q)
   int S = 1;
@@ -670,6 +671,7 @@ BwLayout bw_layout(const lact_config* c, const Plan& p, int64_t N, int64_t chunk
   b.t = take(sizeof(float) * per);
   b.X = take(sizeof(float) * 3 * static_cast<size_t>(p.P) * static_cast<size_t>(b.rows) * p.h);
   b.part = take(sizeof(float) * per * static_cast<size_t>(b.S));
+  b.op = take(p.bf16 && p.d == 128 ? sizeof(uint16_t) * 4 * per : 0);
   b.ns = take(p.muon ? sizeof(float) * 3 * static_cast<size_t>(p.P) *
                            static_cast<size_t>(lact::bw_ns_floats_per_matrix(p.d, p.h, c->ns_iters))
                      : 0);
@@ -792,7 +794,28 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
     a.d = p.d;
     a.h = p.h;
     a.bf16 = p.bf16;
-    hipError_t err = lact::launch_bw_tok(a, apply, s);
+    hipError_t err;
+    if (p.bf16 && p.d == 128) {  // (the operand region exists exactly then)
+      // operands of the matrix-core token kernels as bf16 hi | lo: W1, W3, W2^T
+      // (and for the chunk gradient's VJP P1, P3, P2^T)
+      lact::BwOpsArgs o{};
+      o.m[0] = a.W1;
+      o.m[1] = a.W3;
+      o.m[2] = a.W2;
+      o.m[3] = a.P1;
+      o.m[4] = a.P3;
+      o.m[5] = a.P2;
+      o.nm = apply ? 3 : 6;
+      o.op = reinterpret_cast<uint16_t*>(ws + L.op);
+      o.op_stride = 12 * hd;
+      o.P = p.P;
+      o.d = p.d;
+      o.h = p.h;
+      if ((err = lact::launch_bw_ops(o, s)) != hipSuccess) return hip_fail(err, "backward operand kernel");
+      a.op = o.op;
+      a.op_stride = o.op_stride;
+    }
+    err = lact::launch_bw_tok(a, apply, s);
     if (err != hipSuccess) return hip_fail(err, "backward token kernel");
     const Splits sp = plan_splits(backward_rule(p), n);
     lact::BwContractArgs b{};

@@ -147,6 +147,15 @@ struct BwTokArgs {  // token-local VJPs (chunk gradient: A = K, B = V; query rea
   int64_t deta_stride;
   int P, d, h;
   int bf16;
+  const uint16_t* op;  // bf16 hi | lo operands of W1, W3, W2^T ([P][3][2][h][d]) or NULL
+  int64_t op_stride;   // elements per pair of op
+};
+struct BwOpsArgs {  // matrices as bf16 hi | lo parts in [hidden][feature] order
+  MatRef m[6];      // W1, W3, W2 (then P1, P3, P2): m[2], m[5] stored [d][h]
+  int nm;           // 3 or 6
+  uint16_t* op;     // [P][nm][2][h][d]
+  int64_t op_stride;
+  int P, d, h;  // d must be 128
 };
 struct BwContractArgs {  // X1^T A, (b B)^T X2, X3^T A over tokens, b = -eta or 1
   const void* A;
@@ -179,6 +188,11 @@ struct BwNSArgs {
 };
 bool backward_shape_ok(int d, int h);
 hipError_t launch_bw_tok(const BwTokArgs& a, bool apply, hipStream_t s);
+// matrix-core token kernel of the query read (bf16, d = 128, h a multiple of 32,
+// operands from launch_bw_ops)
+bool bw_tok_mfma_ok(const BwTokArgs& a, bool apply);
+hipError_t launch_bw_tok_mfma(const BwTokArgs& a, bool apply, hipStream_t s);
+hipError_t launch_bw_ops(const BwOpsArgs& a, hipStream_t s);
 hipError_t launch_bw_contract(const BwContractArgs& a, hipStream_t s);
 // the bf16 matrix-core contraction (d = 128, h a multiple of 128, 16-byte aligned inputs)
 bool bw_contract_mfma_ok(const BwContractArgs& a);
