@@ -67,15 +67,15 @@ __device__ __forceinline__ float bf16_half(unsigned w, int k) {
 // Split-operand products of NQ 32 x 32 tiles, all over the same KSTEPS
 // k-steps: for tile q, hh[q] += P_hi Q_hi^T and cross[q] += P_hi Q_lo^T +
 // P_lo Q_hi^T, with P rows at pa[q] and Q rows at pb[q] (row-major bf16 in
-// LDS, 16-byte operand slices at +32 ks; the lo block `half` bytes after the
-// hi block).  With PRE every operand of the phase is read before the first
+// LDS, the 16-byte operand slice of k-step ks at byte koff[ks] of the row;
+// the lo block `half` bytes after the hi block).  With PRE every operand of the phase is read before the first
 // product (one wave per SIMD has no other wave to hide the read latency);
 // otherwise the k loop is unrolled and the tiles interleaved inside it, so
 // the reads of one k-step overlap the products of the previous ones.
 template <int NQ, int KSTEPS, bool PRE>
 __device__ __forceinline__ void split_tiles(const unsigned char* const (&pa)[NQ],
-                                            const unsigned char* const (&pb)[NQ], int half,
-                                            f32x16_t (&hh)[NQ], f32x16_t (&cross)[NQ]) {
+                                            const unsigned char* const (&pb)[NQ], const int (&koff)[KSTEPS],
+                                            int half, f32x16_t (&hh)[NQ], f32x16_t (&cross)[NQ]) {
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
 #pragma unroll
@@ -90,10 +90,10 @@ __device__ __forceinline__ void split_tiles(const unsigned char* const (&pa)[NQ]
     for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        ah[ks][q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + 32 * ks);
-        bh[ks][q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + 32 * ks);
-        al[ks][q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + half + 32 * ks);
-        bl[ks][q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + half + 32 * ks);
+        ah[ks][q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + koff[ks]);
+        bh[ks][q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + koff[ks]);
+        al[ks][q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + half + koff[ks]);
+        bl[ks][q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + half + koff[ks]);
       }
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
@@ -112,10 +112,10 @@ __device__ __forceinline__ void split_tiles(const unsigned char* const (&pa)[NQ]
       bf16x8_t ah[NQ], al[NQ], bh[NQ], bl[NQ];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        ah[q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + 32 * ks);
-        al[q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + half + 32 * ks);
-        bh[q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + 32 * ks);
-        bl[q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + half + 32 * ks);
+        ah[q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + koff[ks]);
+        al[q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + half + koff[ks]);
+        bh[q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + koff[ks]);
+        bl[q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + half + koff[ks]);
       }
       // the two cross products of a tile are NQ products apart
 #pragma unroll
@@ -126,6 +126,38 @@ __device__ __forceinline__ void split_tiles(const unsigned char* const (&pa)[NQ]
       for (int q = 0; q < NQ; ++q) cross[q] = mfma(al[q], bh[q], cross[q]);
     }
   }
+}
+
+// Row-major X in LDS: 16-byte chunk c of row r sits at chunk c ^ xsw(r),
+// xsw(r) = 4 (r % 4) + (r / 4) % 4.  The operand reads of X X^T (16 rows in a
+// row, one chunk: xsw is one-to-one on r % 16) and the 8-byte stores of
+// quad_tr's output (rows 4m .. 4m + 3, eight 8-byte column groups: the rows
+// differ in bits 2, 3 of xsw, the groups in bits 0, 1 and in the half
+// chunk) are both free of bank conflicts.
+__device__ __forceinline__ int xsw(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+
+__device__ __forceinline__ unsigned dpp_u32_xor1(unsigned v) {
+  return static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ unsigned dpp_u32_xor2(unsigned v) {
+  return static_cast<unsigned>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), 0x4E, 0xF, 0xF, false));
+}
+
+// 4 x 4 transpose of bf16 values across the four lanes of a quad: on entry
+// lane p holds column p, rows 0-3 as w0 = (row 0, row 1), w1 = (row 2, row 3)
+// (element 0 in the low half); on exit it holds row p, columns 0-3 as
+// w0 = (column 0, column 1), w1 = (column 2, column 3).  Two butterfly
+// exchanges: 16-bit halves with lane p ^ 1, then words with lane p ^ 2.
+__device__ __forceinline__ void quad_tr(unsigned& w0, unsigned& w1, int p) {
+  const unsigned r0 = dpp_u32_xor1(w0), r1 = dpp_u32_xor1(w1);
+  // even lanes: (own low, partner's low); odd lanes: (partner's high, own high)
+  const unsigned sel = (p & 1) ? 0x03020706u : 0x05040100u;
+  const unsigned n0 = __builtin_amdgcn_perm(r0, w0, sel);
+  const unsigned n1 = __builtin_amdgcn_perm(r1, w1, sel);
+  const unsigned send = (p & 2) ? n0 : n1;
+  const unsigned recv = dpp_u32_xor2(send);
+  w0 = (p & 2) ? recv : n0;
+  w1 = (p & 2) ? n1 : recv;
 }
 
 // Column order of the stored s x s matrices A and B: inside every 16 columns
@@ -143,11 +175,13 @@ struct NSGeo {
   static constexpr int NW = L / 32;          // waves
   static constexpr int CT = L / (32 * NW);   // 32-column tiles of X per wave (1)
   static constexpr int MT = S / 32;          // 32-row tiles of X (and of A)
-  static constexpr int XRS = 2 * L + 16;     // bytes per row of X (bf16, padded)
+  static constexpr int XRS = 2 * L;          // bytes per row of X (bf16; 16-byte chunks swizzled, see xsw)
   static constexpr int X_HALF = S * XRS;     // hi block, then lo block
   static constexpr int ARS = 2 * S + 16;     // bytes per row of A / B
   static constexpr int A_HALF = S * ARS;
-  static constexpr int REGION = (2 * X_HALF > 2 * A_HALF) ? 2 * X_HALF : 2 * A_HALF;
+  static constexpr int XFS = 4 * L + 4;      // bytes per row of the fp32 staging of X (odd word count)
+  static constexpr int R1 = (2 * X_HALF > 2 * A_HALF) ? 2 * X_HALF : 2 * A_HALF;
+  static constexpr int REGION = (R1 > S * XFS) ? R1 : S * XFS;  // the fp32 staging shares the region
   static constexpr int ATILES = MT * MT;
   static constexpr int ATW = (ATILES + NW - 1) / NW;  // A tiles per wave
   // one wave per SIMD with registers to spare: read each phase's operands
@@ -184,7 +218,7 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
   // (an odd number of words per row: when X is G^T, a wavefront's staging
   // stores and final reads walk down a column, rows 4 apart, and an odd
   // stride spreads them over 16 banks instead of 1)
-  constexpr int XFS = 4 * L + 4;
+  constexpr int XFS = G::XFS;
   constexpr int NV = S * L / 4;  // float4 groups per matrix
   constexpr int GPT = NV / (2 * L);
   float4* W4 = reinterpret_cast<float4*>(Wm);
@@ -309,19 +343,29 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
       }
     }
     __syncthreads();
+    // row-major stores: every group of four rows of a lane quad is
+    // transposed across the quad (lane p then holds row 4 m' + p, four
+    // consecutive columns) and stored as 8 bytes
+    {
+      const int p = ln & 3;
 #pragma unroll
-    for (int ct = 0; ct < G::CT; ++ct) {
+      for (int ct = 0; ct < G::CT; ++ct) {
+        // logical chunk and half of the quad's four columns
+        const int lc = 4 * (G::NW * ct + w) + (ln >> 3), hf = (ln >> 2) & 1;
 #pragma unroll
-      for (int mt = 0; mt < G::MT; ++mt) {
-        // one base per 32-row tile keeps every store offset an immediate
-        unsigned char* xb = xhi + (32 * mt + 4 * g) * G::XRS + 2 * colof(ct);
+        for (int mt = 0; mt < G::MT; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ro = (8 * (r >> 2) + (r & 3)) * G::XRS;
-          const int ks = 2 * mt + (r >> 3), j = (r & 7) >> 1, k = r & 1;
-          const unsigned wh = xh[ct][ks][j], wl = xl[ct][ks][j];
-          *reinterpret_cast<uint16_t*>(xb + ro) = static_cast<uint16_t>(k ? (wh >> 16) : wh);
-          *reinterpret_cast<uint16_t*>(xb + G::X_HALF + ro) = static_cast<uint16_t>(k ? (wl >> 16) : wl);
+          for (int rg = 0; rg < 4; ++rg) {
+            const int ks = 2 * mt + (rg >> 1), j = 2 * (rg & 1);
+            unsigned h0 = xh[ct][ks][j], h1 = xh[ct][ks][j + 1];
+            unsigned l0 = xl[ct][ks][j], l1 = xl[ct][ks][j + 1];
+            quad_tr(h0, h1, p);
+            quad_tr(l0, l1, p);
+            const int row = 32 * mt + 8 * rg + 4 * g + p;
+            const int off = row * G::XRS + 16 * (lc ^ (4 * p + ((2 * rg + g) & 3))) + 8 * hf;
+            *reinterpret_cast<uint2*>(xhi + off) = make_uint2(h0, h1);
+            *reinterpret_cast<uint2*>(xhi + G::X_HALF + off) = make_uint2(l0, l1);
+          }
         }
       }
     }
@@ -330,17 +374,24 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
     // ---- A = X X^T: this wave's tiles (ti, tj) = (t / MT, t % MT),
     // t = w + NW q; K = l
     f32x16_t at[G::ATW];
+    // chunk 2 ks + g of row 32 t + ln, swizzled (xsw depends on ln % 16 only)
+    int xko[L / 16];
+#pragma unroll
+    for (int ks = 0; ks < L / 16; ++ks) {
+      const int c = 2 * ks + g;
+      xko[ks] = 16 * ((c & 15) ^ xsw(ln)) + 256 * (c >> 4);
+    }
     if constexpr (G::ATILES % G::NW == 0) {
       const unsigned char* pa[G::ATW];
       const unsigned char* pb[G::ATW];
 #pragma unroll
       for (int q = 0; q < G::ATW; ++q) {
         const int t = w + G::NW * q;
-        pa[q] = xhi + (32 * (t / G::MT) + ln) * G::XRS + 16 * g;
-        pb[q] = xhi + (32 * (t % G::MT) + ln) * G::XRS + 16 * g;
+        pa[q] = xhi + (32 * (t / G::MT) + ln) * G::XRS;
+        pb[q] = xhi + (32 * (t % G::MT) + ln) * G::XRS;
       }
       f32x16_t a2[G::ATW];
-      split_tiles<G::ATW, L / 16, G::PRE>(pa, pb, G::X_HALF, at, a2);
+      split_tiles<G::ATW, L / 16, G::PRE>(pa, pb, xko, G::X_HALF, at, a2);
 #pragma unroll
       for (int q = 0; q < G::ATW; ++q) {
 #pragma unroll
@@ -353,10 +404,10 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) at[q][r] = 0.f;
         if (t < G::ATILES) {
-          const unsigned char* pa[1] = {xhi + (32 * (t / G::MT) + ln) * G::XRS + 16 * g};
-          const unsigned char* pb[1] = {xhi + (32 * (t % G::MT) + ln) * G::XRS + 16 * g};
+          const unsigned char* pa[1] = {xhi + (32 * (t / G::MT) + ln) * G::XRS};
+          const unsigned char* pb[1] = {xhi + (32 * (t % G::MT) + ln) * G::XRS};
           f32x16_t hh[1], a2[1];
-          split_tiles<1, L / 16, false>(pa, pb, G::X_HALF, hh, a2);
+          split_tiles<1, L / 16, false>(pa, pb, xko, G::X_HALF, hh, a2);
 #pragma unroll
           for (int r = 0; r < 16; ++r) at[q][r] = hh[0][r] + a2[0][r];
         }
@@ -391,17 +442,20 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
     __syncthreads();
 
     // ---- B = b A + c A A on the same tiles (A symmetric: both operands are rows of A)
+    int ako[S / 16];
+#pragma unroll
+    for (int ks = 0; ks < S / 16; ++ks) ako[ks] = 16 * g + 32 * ks;
     if constexpr (G::ATILES % G::NW == 0) {
       const unsigned char* pa[G::ATW];
       const unsigned char* pb[G::ATW];
 #pragma unroll
       for (int q = 0; q < G::ATW; ++q) {
         const int t = w + G::NW * q;
-        pa[q] = ahi + (32 * (t / G::MT) + ln) * G::ARS + 16 * g;
-        pb[q] = ahi + (32 * (t % G::MT) + ln) * G::ARS + 16 * g;
+        pa[q] = ahi + (32 * (t / G::MT) + ln) * G::ARS;
+        pb[q] = ahi + (32 * (t % G::MT) + ln) * G::ARS;
       }
       f32x16_t acc[G::ATW], a2[G::ATW];
-      split_tiles<G::ATW, S / 16, G::PRE>(pa, pb, G::A_HALF, acc, a2);
+      split_tiles<G::ATW, S / 16, G::PRE>(pa, pb, ako, G::A_HALF, acc, a2);
 #pragma unroll
       for (int q = 0; q < G::ATW; ++q) {
 #pragma unroll
@@ -412,10 +466,10 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
       for (int q = 0; q < G::ATW; ++q) {
         const int t = w + G::NW * q;
         if (t < G::ATILES) {
-          const unsigned char* pa[1] = {ahi + (32 * (t / G::MT) + ln) * G::ARS + 16 * g};
-          const unsigned char* pb[1] = {ahi + (32 * (t % G::MT) + ln) * G::ARS + 16 * g};
+          const unsigned char* pa[1] = {ahi + (32 * (t / G::MT) + ln) * G::ARS};
+          const unsigned char* pb[1] = {ahi + (32 * (t % G::MT) + ln) * G::ARS};
           f32x16_t acc[1], a2[1];
-          split_tiles<1, S / 16, false>(pa, pb, G::A_HALF, acc, a2);
+          split_tiles<1, S / 16, false>(pa, pb, ako, G::A_HALF, acc, a2);
 #pragma unroll
           for (int r = 0; r < 16; ++r) at[q][r] = a.b * at[q][r] + a.c * (acc[0][r] + a2[0][r]);  // now B
         }
