@@ -67,15 +67,19 @@ __device__ __forceinline__ float bf16_half(unsigned w, int k) {
 // Split-operand products of NQ 32 x 32 tiles, all over the same KSTEPS
 // k-steps: for tile q, hh[q] += P_hi Q_hi^T and cross[q] += P_hi Q_lo^T +
 // P_lo Q_hi^T, with P rows at pa[q] and Q rows at pb[q] (row-major bf16 in
-// LDS, the 16-byte operand slice of k-step ks at byte koff[ks] of the row;
+// LDS, the 16-byte operand slice of k-step ks at byte koff(ks) of the row;
 // the lo block `half` bytes after the hi block).  With PRE every operand of the phase is read before the first
 // product (one wave per SIMD has no other wave to hide the read latency);
 // otherwise the k loop is unrolled and the tiles interleaved inside it, so
 // the reads of one k-step overlap the products of the previous ones.
-template <int NQ, int KSTEPS, bool PRE>
+template <int NQ, int KSTEPS, bool PRE, bool SWZ>
 __device__ __forceinline__ void split_tiles(const unsigned char* const (&pa)[NQ],
-                                            const unsigned char* const (&pb)[NQ], const int (&koff)[KSTEPS],
-                                            int half, f32x16_t (&hh)[NQ], f32x16_t (&cross)[NQ]) {
+                                            const unsigned char* const (&pb)[NQ], int yx, int half,
+                                            f32x16_t (&hh)[NQ], f32x16_t (&cross)[NQ]) {
+  // byte offset of k-step ks in a row: 16-byte chunk 2 ks + g, in swizzled
+  // rows chunk (2 ks + g) ^ xsw(row) with yx = 16 (g ^ xsw(row)) (xsw < 16
+  // leaves bit 4 of the chunk index, 256-byte steps, alone); otherwise yx = 16 g
+  auto koff = [&](int ks) { return SWZ ? (((32 * ks) & 255) ^ yx) + 256 * (ks >> 3) : yx + 32 * ks; };
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
 #pragma unroll
@@ -90,10 +94,10 @@ __device__ __forceinline__ void split_tiles(const unsigned char* const (&pa)[NQ]
     for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        ah[ks][q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + koff[ks]);
-        bh[ks][q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + koff[ks]);
-        al[ks][q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + half + koff[ks]);
-        bl[ks][q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + half + koff[ks]);
+        ah[ks][q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + koff(ks));
+        bh[ks][q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + koff(ks));
+        al[ks][q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + half + koff(ks));
+        bl[ks][q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + half + koff(ks));
       }
     }
     __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
@@ -112,10 +116,10 @@ __device__ __forceinline__ void split_tiles(const unsigned char* const (&pa)[NQ]
       bf16x8_t ah[NQ], al[NQ], bh[NQ], bl[NQ];
 #pragma unroll
       for (int q = 0; q < NQ; ++q) {
-        ah[q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + koff[ks]);
-        al[q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + half + koff[ks]);
-        bh[q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + koff[ks]);
-        bl[q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + half + koff[ks]);
+        ah[q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + koff(ks));
+        al[q] = *reinterpret_cast<const bf16x8_t*>(pa[q] + half + koff(ks));
+        bh[q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + koff(ks));
+        bl[q] = *reinterpret_cast<const bf16x8_t*>(pb[q] + half + koff(ks));
       }
       // the two cross products of a tile are NQ products apart
 #pragma unroll
@@ -179,9 +183,14 @@ struct NSGeo {
   static constexpr int X_HALF = S * XRS;     // hi block, then lo block
   static constexpr int ARS = 2 * S + 16;     // bytes per row of A / B
   static constexpr int A_HALF = S * ARS;
-  static constexpr int XFS = 4 * L + 4;      // bytes per row of the fp32 staging of X (odd word count)
+  // fp32 staging of G and of the final X in the stored matrix's own
+  // orientation: rows of rowlen floats (S for the tall W1, W3, L for W2)
+  // padded by 16 bytes
+  static constexpr int STG_TALL = L * (4 * S + 16);
+  static constexpr int STG_WIDE = S * (4 * L + 16);
+  static constexpr int STG = STG_TALL > STG_WIDE ? STG_TALL : STG_WIDE;
   static constexpr int R1 = (2 * X_HALF > 2 * A_HALF) ? 2 * X_HALF : 2 * A_HALF;
-  static constexpr int REGION = (R1 > S * XFS) ? R1 : S * XFS;  // the fp32 staging shares the region
+  static constexpr int REGION = (R1 > STG) ? R1 : STG;  // the staging shares the region
   static constexpr int ATILES = MT * MT;
   static constexpr int ATW = (ATILES + NW - 1) / NW;  // A tiles per wave
   // one wave per SIMD with registers to spare: read each phase's operands
@@ -189,17 +198,15 @@ struct NSGeo {
   static constexpr bool PRE = (S == 64 && L == 128);
 };
 
-template <int S, int L>
-__global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
+// The tail of one matrix; TR: G is tall (stored l x s), X = G^T.  (One body
+// per orientation, so that each is straight-line code for the register
+// allocator.)
+template <int S, int L, bool TR>
+__device__ __forceinline__ void muon_tail_body(const TailArgs& a, unsigned char* lds, float* red, int pair,
+                                               int which) {
   using G = NSGeo<S, L>;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[G::REGION];
-  __shared__ float red[G::NW];
-
-  const int mat = blockIdx.x;
-  const int pair = mat / 3, which = mat % 3;  // 0: W1 (h x d), 1: W2 (d x h), 2: W3 (h x d)
   const int64_t hd = static_cast<int64_t>(a.h) * a.d;
-  const int cols = (which == 1) ? a.h : a.d;
-  const bool tr = ((which == 1) ? a.d : a.h) > cols;  // X = G^T when G is tall
+  constexpr bool tr = TR;
   float* Wm = (which == 0 ? a.W1 : which == 1 ? a.W2 : a.W3) + pair * hd;
   float* Mm = (a.M1 == nullptr) ? nullptr : (which == 0 ? a.M1 : which == 1 ? a.M2 : a.M3) + pair * hd;
   uint16_t* Wbm = (a.Wb1 == nullptr) ? nullptr : (which == 0 ? a.Wb1 : which == 1 ? a.Wb2 : a.Wb3) + pair * hd;
@@ -211,14 +218,17 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
   auto colof = [&](int ct) { return 32 * (G::NW * ct + w) + ln; };
 
   // ---- G = sum of the split partials in fixed order (then the momentum
-  // update M <- beta M + G, G <- M), staged through LDS as fp32 X (row stride
-  // XFS) so the global reads stay coalesced and the register reads below use
-  // immediate offsets.  X0 = G / (||G||_F + eps) in registers, MFMA output
-  // layout: x[ct][mt][r] = X[32 mt + 8 (r/4) + 4 g + r%4][colof(ct)].
-  // (an odd number of words per row: when X is G^T, a wavefront's staging
-  // stores and final reads walk down a column, rows 4 apart, and an odd
-  // stride spreads them over 16 banks instead of 1)
-  constexpr int XFS = G::XFS;
+  // update M <- beta M + G, G <- M), staged through LDS in G's own row-major
+  // order (rows of rowlen floats, padded to grs bytes) so the global reads
+  // and the staging stores move 16-byte groups.  X0 = G / (||G||_F + eps) in
+  // registers, MFMA output layout:
+  // x[ct][mt][r] = X[32 mt + 8 (r/4) + 4 g + r%4][colof(ct)].  When G is tall
+  // (X = G^T), the four X rows of a register group are four consecutive
+  // floats of one staged row (one 16-byte read); otherwise they are four
+  // staged rows (lanes read consecutive words of each).
+  const int rowlen = tr ? S : L;  // (S and L are powers of two)
+  const int lg_rowlen = tr ? __builtin_ctz(S) : __builtin_ctz(L);
+  const int grs = 4 * rowlen + 16;
   constexpr int NV = S * L / 4;  // float4 groups per matrix
   constexpr int GPT = NV / (2 * L);
   float4* W4 = reinterpret_cast<float4*>(Wm);
@@ -283,17 +293,9 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
-    const int c = tid + 2 * L * k;
-    const float g4[4] = {acc[k].x, acc[k].y, acc[k].z, acc[k].w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = 4 * c + q;
-      const float v = g4[q];
-      ss += v * v;
-      const int i = tr ? (e % S) : (e / L);  // row of X
-      const int j = tr ? (e / S) : (e % L);  // column of X
-      *reinterpret_cast<float*>(lds + i * XFS + 4 * j) = v;
-    }
+    const int e = 4 * (tid + 2 * L * k);
+    ss += acc[k].x * acc[k].x + acc[k].y * acc[k].y + acc[k].z * acc[k].z + acc[k].w * acc[k].w;
+    *reinterpret_cast<float4*>(lds + (e >> lg_rowlen) * grs + 4 * (e & (rowlen - 1))) = acc[k];
   }
   {
     float t[1] = {ss};
@@ -311,10 +313,21 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
   for (int ct = 0; ct < G::CT; ++ct) {
 #pragma unroll
     for (int mt = 0; mt < G::MT; ++mt) {
-      const unsigned char* xb = lds + (32 * mt + 4 * g) * XFS + 4 * colof(ct);
+      if (tr) {
+        const unsigned char* xb = lds + colof(ct) * grs + 4 * (32 * mt + 4 * g);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        x[ct][mt][r] = *reinterpret_cast<const float*>(xb + (8 * (r >> 2) + (r & 3)) * XFS) * inv_denom;
+        for (int rg = 0; rg < 4; ++rg) {
+          const float4 v = *reinterpret_cast<const float4*>(xb + 32 * rg);
+          x[ct][mt][4 * rg] = v.x * inv_denom;
+          x[ct][mt][4 * rg + 1] = v.y * inv_denom;
+          x[ct][mt][4 * rg + 2] = v.z * inv_denom;
+          x[ct][mt][4 * rg + 3] = v.w * inv_denom;
+        }
+      } else {
+        const unsigned char* xb = lds + (32 * mt + 4 * g) * grs + 4 * colof(ct);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          x[ct][mt][r] = *reinterpret_cast<const float*>(xb + (8 * (r >> 2) + (r & 3)) * grs) * inv_denom;
       }
     }
   }
@@ -375,12 +388,7 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
     // t = w + NW q; K = l
     f32x16_t at[G::ATW];
     // chunk 2 ks + g of row 32 t + ln, swizzled (xsw depends on ln % 16 only)
-    int xko[L / 16];
-#pragma unroll
-    for (int ks = 0; ks < L / 16; ++ks) {
-      const int c = 2 * ks + g;
-      xko[ks] = 16 * ((c & 15) ^ xsw(ln)) + 256 * (c >> 4);
-    }
+    const int yx = 16 * (g ^ xsw(ln));
     if constexpr (G::ATILES % G::NW == 0) {
       const unsigned char* pa[G::ATW];
       const unsigned char* pb[G::ATW];
@@ -391,7 +399,7 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
         pb[q] = xhi + (32 * (t % G::MT) + ln) * G::XRS;
       }
       f32x16_t a2[G::ATW];
-      split_tiles<G::ATW, L / 16, G::PRE>(pa, pb, xko, G::X_HALF, at, a2);
+      split_tiles<G::ATW, L / 16, G::PRE, true>(pa, pb, yx, G::X_HALF, at, a2);
 #pragma unroll
       for (int q = 0; q < G::ATW; ++q) {
 #pragma unroll
@@ -407,7 +415,7 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
           const unsigned char* pa[1] = {xhi + (32 * (t / G::MT) + ln) * G::XRS};
           const unsigned char* pb[1] = {xhi + (32 * (t % G::MT) + ln) * G::XRS};
           f32x16_t hh[1], a2[1];
-          split_tiles<1, L / 16, false>(pa, pb, xko, G::X_HALF, hh, a2);
+          split_tiles<1, L / 16, false, true>(pa, pb, yx, G::X_HALF, hh, a2);
 #pragma unroll
           for (int r = 0; r < 16; ++r) at[q][r] = hh[0][r] + a2[0][r];
         }
@@ -442,9 +450,6 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
     __syncthreads();
 
     // ---- B = b A + c A A on the same tiles (A symmetric: both operands are rows of A)
-    int ako[S / 16];
-#pragma unroll
-    for (int ks = 0; ks < S / 16; ++ks) ako[ks] = 16 * g + 32 * ks;
     if constexpr (G::ATILES % G::NW == 0) {
       const unsigned char* pa[G::ATW];
       const unsigned char* pb[G::ATW];
@@ -455,7 +460,7 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
         pb[q] = ahi + (32 * (t % G::MT) + ln) * G::ARS;
       }
       f32x16_t acc[G::ATW], a2[G::ATW];
-      split_tiles<G::ATW, S / 16, G::PRE>(pa, pb, ako, G::A_HALF, acc, a2);
+      split_tiles<G::ATW, S / 16, G::PRE, false>(pa, pb, 16 * g, G::A_HALF, acc, a2);
 #pragma unroll
       for (int q = 0; q < G::ATW; ++q) {
 #pragma unroll
@@ -469,7 +474,7 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
           const unsigned char* pa[1] = {ahi + (32 * (t / G::MT) + ln) * G::ARS};
           const unsigned char* pb[1] = {ahi + (32 * (t % G::MT) + ln) * G::ARS};
           f32x16_t acc[1], a2[1];
-          split_tiles<1, S / 16, false>(pa, pb, ako, G::A_HALF, acc, a2);
+          split_tiles<1, S / 16, false, false>(pa, pb, 16 * g, G::A_HALF, acc, a2);
 #pragma unroll
           for (int r = 0; r < 16; ++r) at[q][r] = a.b * at[q][r] + a.c * (acc[0][r] + a2[0][r]);  // now B
         }
@@ -570,27 +575,30 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
   // ---- W <- W - step X, then unit L2 rows.  Every thread takes GPT float4
   // groups of the stored matrix (rows of `rowlen`, rowlen / 4 lanes per row,
   // so a row's lanes are an aligned lane group); all W loads are issued
-  // together (with PRE at the start of the kernel, otherwise here, before X
-  // goes to LDS), so their latency is paid once.  W1, W3 rows are columns
-  // of X, W2 rows are rows of X.
-  const int rowlen = tr ? S : L;  // (S and L are powers of two)
-  const int lg_rowlen = tr ? __builtin_ctz(S) : __builtin_ctz(L);
-  if constexpr (!G::PRE) {
-#pragma unroll
-    for (int k = 0; k < GPT; ++k) wv[k] = W4[tid + 2 * L * k];
-  }
-
+  // together (with PRE at the start of the kernel, otherwise here, once X
+  // is in LDS), so their latency is paid once.  X goes back to the staging
+  // layout (W1, W3 rows are columns of X, W2 rows are rows of X).
   __syncthreads();
 #pragma unroll
   for (int ct = 0; ct < G::CT; ++ct) {
 #pragma unroll
     for (int mt = 0; mt < G::MT; ++mt) {
-      unsigned char* xb = lds + (32 * mt + 4 * g) * XFS + 4 * colof(ct);
+      if (tr) {
+        unsigned char* xb = lds + colof(ct) * grs + 4 * (32 * mt + 4 * g);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        *reinterpret_cast<float*>(xb + (8 * (r >> 2) + (r & 3)) * XFS) = x[ct][mt][r];
+        for (int rg = 0; rg < 4; ++rg)
+          *reinterpret_cast<float4*>(xb + 32 * rg) =
+              make_float4(x[ct][mt][4 * rg], x[ct][mt][4 * rg + 1], x[ct][mt][4 * rg + 2], x[ct][mt][4 * rg + 3]);
+      } else {
+        unsigned char* xb = lds + (32 * mt + 4 * g) * grs + 4 * colof(ct);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) *reinterpret_cast<float*>(xb + (8 * (r >> 2) + (r & 3)) * grs) = x[ct][mt][r];
       }
     }
+  }
+  if constexpr (!G::PRE) {
+#pragma unroll
+    for (int k = 0; k < GPT; ++k) wv[k] = W4[tid + 2 * L * k];
   }
   __syncthreads();
   // (every row's squared norm first, then all GPT group reductions together,
@@ -599,7 +607,8 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
 #pragma unroll
   for (int k = 0; k < GPT; ++k) {
     const int e = 4 * (tid + 2 * L * k);
-    const int row = e >> lg_rowlen, col = e & (rowlen - 1);
+    const float4 xs = *reinterpret_cast<const float4*>(lds + (e >> lg_rowlen) * grs + 4 * (e & (rowlen - 1)));
+    const float xq[4] = {xs.x, xs.y, xs.z, xs.w};
     v[k][0] = wv[k].x;
     v[k][1] = wv[k].y;
     v[k][2] = wv[k].z;
@@ -608,8 +617,7 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
     sq[k] = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int i = tr ? col + q : row, j = tr ? row : col + q;  // element of X
-      v[k][q] -= a.step * *reinterpret_cast<const float*>(lds + i * XFS + 4 * j);
+      v[k][q] -= a.step * xq[q];
       sq[k] += v[k][q] * v[k][q];
     }
   }
@@ -638,6 +646,21 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
       const int e = 4 * (tid + 2 * L * k);
       *reinterpret_cast<bf16x4_t*>(Wbm + wb_tiled(e >> lg_rowlen, e & (rowlen - 1), rowlen)) = b4;
     }
+  }
+}
+
+template <int S, int L>
+__global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
+  using G = NSGeo<S, L>;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[G::REGION];
+  __shared__ float red[G::NW];
+  const int mat = blockIdx.x;
+  const int pair = mat / 3, which = mat % 3;  // 0: W1 (h x d), 1: W2 (d x h), 2: W3 (h x d)
+  const int cols = (which == 1) ? a.h : a.d;
+  if (((which == 1) ? a.d : a.h) > cols) {
+    muon_tail_body<S, L, true>(a, lds, red, pair, which);
+  } else {
+    muon_tail_body<S, L, false>(a, lds, red, pair, which);
   }
 }
 
