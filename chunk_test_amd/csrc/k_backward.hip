@@ -22,8 +22,9 @@
 //                   VJP, giving the cotangents of W and of the direction
 //   k_bw_momentum   the momentum buffer's cotangent carried to the earlier
 //                   chunk
-//   k_bw_ns         Newton-Schulz's VJP through every iteration and the
-//                   Frobenius pre-scaling (iterates recomputed)
+//   k_bw_ns_fwd     Newton-Schulz's forward (iterates and A, B kept)
+//   k_bw_ns         its VJP through every iteration and the Frobenius
+//                   pre-scaling
 //   k_bw_copy       layout moves between separate W1 | W2 | W3 arrays and the
 //                   per-pair [W1 | W2 | W3] blocks
 #include "lact_device.h"
@@ -434,145 +435,260 @@ __global__ __launch_bounds__(kThreads) void k_bw_momentum(const float* t, float*
 }
 
 // ---------------------------------------------------------------------------
-// Newton-Schulz VJP, one workgroup per matrix (3P of them, block layout).
-// Forward on X (s x l, s = min(rows, cols), G transposed when rows > cols):
-//   X0 = G / (||G||_F + eps);  A = X X^T;  B = b A + c A A;  X <- a X + B X.
-// Reverse, iterate k = I-1 .. 0 with dY the cotangent of X_{k+1}:
-//   dB = dY X_k^T,  dX = a dY + B^T dY + (dA + dA^T) X_k,
-//   dA = b dB + c (dB A^T + A^T dB);
-// then dG = dX0 / (n + eps) - (<dX0, G> / (n + eps)^2) G / n.
-// The iterates X_0 .. X_I are kept in global scratch.
+// Newton-Schulz and its VJP, one workgroup per matrix (3P of them, block
+// layout), in two kernels around the step's VJP.  On X (s x l,
+// s = min(rows, cols), G transposed when rows > cols):
+//   forward   X0 = G / (||G||_F + eps);  A_k = X_k X_k^T;  B_k = b A_k + c A_k A_k;
+//             X_{k+1} = a X_k + B_k X_k   (iterates, A_k, B_k kept in scratch;
+//             X_I, in G's orientation, is the update direction);
+//   reverse   k = I-1 .. 0 with dY the cotangent of X_{k+1}:
+//             dB = dY X_k^T,  dA = b dB + c (dB A_k^T + A_k^T dB),
+//             dX_k = a dY + B_k^T dY + (dA + dA^T) X_k;
+//   then dG = dX_0 / (n + eps) - (<dX_0, G> / (n + eps)^2) G / n.
+// Every product runs on fp32 MFMA (v_mfma_f32_32x32x2_f32: products and sums
+// in fp32), 32 x 32 output tiles spread over the eight wavefronts, the
+// operands staged through LDS 32 k values at a time.
 // ---------------------------------------------------------------------------
 constexpr int kNSThreads = 512;
+constexpr int kNB = 256;  // output columns per block of a product
 
-__global__ __launch_bounds__(kNSThreads) void k_bw_ns(BwNSArgs a) {
-  __shared__ float red[kNSThreads];
-  const int mat = blockIdx.x;
-  const int pair = mat / 3, which = mat % 3;  // 0: W1, 1: W2, 2: W3
-  const int64_t hd = static_cast<int64_t>(a.h) * a.d;
-  const float* G = a.g + pair * 3 * hd + which * hd;
-  const float* dX = a.dx + pair * 3 * hd + which * hd;
-  float* dG = a.out + pair * 3 * hd + which * hd;
-  const int rows = (which == 1) ? a.d : a.h;
-  const int cols = (which == 1) ? a.h : a.d;
-  const bool tr = rows > cols;
-  const int s = tr ? cols : rows;
-  const int l = tr ? rows : cols;
-  const int64_t sl = static_cast<int64_t>(s) * l, ss = static_cast<int64_t>(s) * s;
-  float* xs = a.scratch + static_cast<int64_t>(mat) * a.per_mat;  // (iters + 1) sl
-  float* dY = xs + (a.iters + 1) * sl;
-  float* dXk = dY + sl;
-  float* A = dXk + sl;
-  float* Bm = A + ss;
-  float* dB = Bm + ss;
-  float* dA = dB + ss;
-  const int tid = threadIdx.x;
-  auto at = [&](const float* M, int i, int j) {  // element (i, j) of the s x l orientation
-    return tr ? M[static_cast<int64_t>(j) * cols + i] : M[static_cast<int64_t>(i) * cols + j];
-  };
-  auto block_sum = [&](float v) {
-    red[tid] = v;
-    __syncthreads();
-    for (int w = kNSThreads / 2; w > 0; w >>= 1) {
-      if (tid < w) red[tid] += red[tid + w];
-      __syncthreads();
+typedef __attribute__((ext_vector_type(16))) float ns_f32x16;
+
+struct MOp {  // element (i, k) of a matrix operand at p[i * rs + k * cs]
+  const float* p;
+  int rs, cs;
+};
+
+// C (M x N) = sum over the terms t < NTERM of op(P_t) (M x K_t) op(Q_t) (K_t x N),
+// handed to epi(i, j, value) element by element.  M <= 128, M, N, K_t
+// multiples of 32.  Ps: 32 x (M + 1) floats, Qs: 32 x (kNB + 1) floats of LDS.
+template <int NTERM, class Epi>
+__device__ __forceinline__ void wg_mm(int M, int N, const int (&K)[NTERM], const MOp (&P)[NTERM],
+                                      const MOp (&Q)[NTERM], float* Ps, float* Qs, Epi epi) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, ln = lane & 31;
+  const int ps = M + 1;
+  for (int nb = 0; nb < N; nb += kNB) {
+    const int NB = min(kNB, N - nb), qs = NB + 1;
+    const int ntl = NB / 32, tiles = (M / 32) * ntl;  // <= 32: at most four per wave
+    ns_f32x16 acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
     }
-    const float r = red[0];
+#pragma unroll
+    for (int t = 0; t < NTERM; ++t) {
+      const MOp p = P[t], q = Q[t];
+      for (int kc = 0; kc < K[t]; kc += 32) {
+        __syncthreads();  // the previous chunk's readers are done
+        // stage op(P)[0..M)[kc..kc+32) as Ps[k][i], op(Q)[kc..kc+32)[nb..nb+NB) as Qs[k][j]
+        // (the loop order follows the operand's contiguous index)
+        if (p.cs == 1) {
+          for (int idx = tid; idx < 32 * M; idx += kNSThreads) {
+            const int k = idx & 31, i = idx >> 5;
+            Ps[k * ps + i] = p.p[static_cast<int64_t>(i) * p.rs + kc + k];
+          }
+        } else {
+          for (int idx = tid; idx < 32 * M; idx += kNSThreads) {
+            const int i = idx % M, k = idx / M;
+            Ps[k * ps + i] = p.p[static_cast<int64_t>(i) * p.rs + static_cast<int64_t>(kc + k) * p.cs];
+          }
+        }
+        if (q.cs == 1) {
+          for (int idx = tid; idx < 32 * NB; idx += kNSThreads) {
+            const int j = idx % NB, k = idx / NB;
+            Qs[k * qs + j] = q.p[static_cast<int64_t>(kc + k) * q.rs + nb + j];
+          }
+        } else {
+          for (int idx = tid; idx < 32 * NB; idx += kNSThreads) {
+            const int k = idx & 31, j = idx >> 5;
+            Qs[k * qs + j] = q.p[static_cast<int64_t>(kc + k) * q.rs + static_cast<int64_t>(nb + j) * q.cs];
+          }
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int ks = 0; ks < 16; ++ks) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int tt = wave + 8 * u;
+            if (tt < tiles) {
+              const int ti = tt / ntl, tj = tt % ntl;
+              const float av = Ps[(2 * ks + g) * ps + 32 * ti + ln];
+              const float bv = Qs[(2 * ks + g) * qs + 32 * tj + ln];
+              acc[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc[u], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+    // acc[u][r] = C[32 ti + 8 (r / 4) + 4 g + r % 4][nb + 32 tj + ln]
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int tt = wave + 8 * u;
+      if (tt < tiles) {
+        const int ti = tt / ntl, tj = tt % ntl;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) epi(32 * ti + 8 * (r >> 2) + 4 * g + (r & 3), nb + 32 * tj + ln, acc[u][r]);
+      }
+    }
+  }
+  __syncthreads();  // every element of C written (global, visible to the workgroup)
+}
+
+// One matrix's geometry and scratch (floats): iterates X_0 .. X_I (s l each),
+// dY and dX (s l), A_0 .. A_{I-1}, B_0 .. B_{I-1} (s s each), dB, dA (s s).
+struct NSMat {
+  int mat, pair, which, rows, cols, s, l;
+  bool tr;
+  int64_t hd, sl, ss;
+  float *xs, *dY, *dX, *As, *Bs, *dB, *dA;
+  __device__ NSMat(const BwNSArgs& a) {
+    mat = blockIdx.x;
+    pair = mat / 3;
+    which = mat % 3;  // 0: W1, 1: W2, 2: W3
+    hd = static_cast<int64_t>(a.h) * a.d;
+    rows = (which == 1) ? a.d : a.h;
+    cols = (which == 1) ? a.h : a.d;
+    tr = rows > cols;
+    s = tr ? cols : rows;
+    l = tr ? rows : cols;
+    sl = static_cast<int64_t>(s) * l;
+    ss = static_cast<int64_t>(s) * s;
+    xs = a.scratch + static_cast<int64_t>(mat) * a.per_mat;
+    dY = xs + (a.iters + 1) * sl;
+    dX = dY + sl;
+    As = dX + sl;
+    Bs = As + a.iters * ss;
+    dB = Bs + a.iters * ss;
+    dA = dB + ss;
+  }
+  __device__ int64_t gidx(int i, int j) const {  // element (i, j) of the s x l orientation in G's storage
+    return tr ? static_cast<int64_t>(j) * cols + i : static_cast<int64_t>(i) * cols + j;
+  }
+};
+
+__device__ __forceinline__ float ns_block_sum(float v, float* red) {
+  const int tid = threadIdx.x;
+  red[tid] = v;
+  __syncthreads();
+  for (int w = kNSThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) red[tid] += red[tid + w];
     __syncthreads();
-    return r;
-  };
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kNSThreads) void k_bw_ns_fwd(BwNSArgs a) {
+  __shared__ float Ps[32 * 129];
+  __shared__ float Qs[32 * (kNB + 1)];
+  __shared__ float red[kNSThreads];
+  const NSMat m(a);
+  const int tid = threadIdx.x;
+  const float ca = a.a, cb = a.b, cc = a.c;
+  const float* G = a.g + m.pair * 3 * m.hd + m.which * m.hd;
+  float* dir = a.out + m.pair * 3 * m.hd + m.which * m.hd;
   float part = 0.f;
-  for (int64_t i = tid; i < sl; i += kNSThreads) {
-    const float v = at(G, static_cast<int>(i / l), static_cast<int>(i % l));
+  for (int64_t i = tid; i < m.sl; i += kNSThreads) {
+    const float v = G[i];
     part += v * v;
   }
-  const float nrm = sqrtf(block_sum(part));
-  const float den = nrm + a.eps;
-  for (int64_t i = tid; i < sl; i += kNSThreads) xs[i] = at(G, static_cast<int>(i / l), static_cast<int>(i % l)) / den;
-  __syncthreads();
-  // forward iterates
-  for (int it = 0; it < a.iters; ++it) {
-    const float* X = xs + it * sl;
-    float* Xn = xs + (it + 1) * sl;
-    for (int64_t idx = tid; idx < ss; idx += kNSThreads) {
-      const int i = static_cast<int>(idx / s), k = static_cast<int>(idx % s);
-      float acc = 0.f;
-      for (int j = 0; j < l; ++j) acc += X[static_cast<int64_t>(i) * l + j] * X[static_cast<int64_t>(k) * l + j];
-      A[idx] = acc;
-    }
-    __syncthreads();
-    for (int64_t idx = tid; idx < ss; idx += kNSThreads) {
-      const int i = static_cast<int>(idx / s), k = static_cast<int>(idx % s);
-      float acc = 0.f;
-      for (int m = 0; m < s; ++m) acc += A[static_cast<int64_t>(i) * s + m] * A[static_cast<int64_t>(m) * s + k];
-      Bm[idx] = a.b * A[idx] + a.c * acc;
-    }
-    __syncthreads();
-    for (int64_t idx = tid; idx < sl; idx += kNSThreads) {
-      const int i = static_cast<int>(idx / l), j = static_cast<int>(idx % l);
-      float acc = 0.f;
-      for (int m = 0; m < s; ++m) acc += Bm[static_cast<int64_t>(i) * s + m] * X[static_cast<int64_t>(m) * l + j];
-      Xn[idx] = a.a * X[idx] + acc;
-    }
-    __syncthreads();
+  const float den = sqrtf(ns_block_sum(part, red)) + a.eps;
+  for (int64_t idx = tid; idx < m.sl; idx += kNSThreads) {
+    const int i = static_cast<int>(idx / m.l), j = static_cast<int>(idx % m.l);
+    m.xs[idx] = G[m.gidx(i, j)] / den;
   }
-  for (int64_t i = tid; i < sl; i += kNSThreads) dY[i] = at(dX, static_cast<int>(i / l), static_cast<int>(i % l));
+  __syncthreads();
+  const int s = m.s, l = m.l;
+  for (int it = 0; it < a.iters; ++it) {
+    const float* X = m.xs + it * m.sl;
+    float* Xn = m.xs + (it + 1) * m.sl;
+    float* A = m.As + it * m.ss;
+    float* B = m.Bs + it * m.ss;
+    {  // A = X X^T
+      const int K[1] = {l};
+      const MOp P[1] = {{X, l, 1}}, Q[1] = {{X, 1, l}};
+      wg_mm(s, s, K, P, Q, Ps, Qs, [&](int i, int j, float v) { A[i * s + j] = v; });
+    }
+    {  // B = b A + c A A
+      const int K[1] = {s};
+      const MOp P[1] = {{A, s, 1}}, Q[1] = {{A, s, 1}};
+      wg_mm(s, s, K, P, Q, Ps, Qs, [&](int i, int j, float v) { B[i * s + j] = cb * A[i * s + j] + cc * v; });
+    }
+    {  // X <- a X + B X
+      const int K[1] = {s};
+      const MOp P[1] = {{B, s, 1}}, Q[1] = {{X, l, 1}};
+      wg_mm(s, l, K, P, Q, Ps, Qs,
+            [&](int i, int j, float v) { Xn[static_cast<int64_t>(i) * l + j] = ca * X[static_cast<int64_t>(i) * l + j] + v; });
+    }
+  }
+  const float* XI = m.xs + a.iters * m.sl;
+  for (int64_t idx = tid; idx < m.sl; idx += kNSThreads) {
+    const int i = static_cast<int>(idx / l), j = static_cast<int>(idx % l);
+    dir[m.gidx(i, j)] = XI[idx];
+  }
+}
+
+__global__ __launch_bounds__(kNSThreads) void k_bw_ns(BwNSArgs a) {
+  __shared__ float Ps[32 * 129];
+  __shared__ float Qs[32 * (kNB + 1)];
+  __shared__ float red[kNSThreads];
+  const NSMat m(a);
+  const int tid = threadIdx.x;
+  const float ca = a.a, cb = a.b, cc = a.c;
+  const float* G = a.g + m.pair * 3 * m.hd + m.which * m.hd;
+  const float* dXin = a.dx + m.pair * 3 * m.hd + m.which * m.hd;
+  float* dG = a.out + m.pair * 3 * m.hd + m.which * m.hd;
+  const int s = m.s, l = m.l;
+  float* dY = m.dY;
+  float* dXn = m.dX;
+  for (int64_t idx = tid; idx < m.sl; idx += kNSThreads) {
+    const int i = static_cast<int>(idx / l), j = static_cast<int>(idx % l);
+    dY[idx] = dXin[m.gidx(i, j)];
+  }
   __syncthreads();
   for (int it = a.iters - 1; it >= 0; --it) {
-    const float* X = xs + it * sl;
-    // A, B of this iterate
-    for (int64_t idx = tid; idx < ss; idx += kNSThreads) {
-      const int i = static_cast<int>(idx / s), k = static_cast<int>(idx % s);
-      float acc = 0.f;
-      for (int j = 0; j < l; ++j) acc += X[static_cast<int64_t>(i) * l + j] * X[static_cast<int64_t>(k) * l + j];
-      A[idx] = acc;
+    const float* X = m.xs + it * m.sl;
+    const float* A = m.As + it * m.ss;
+    const float* B = m.Bs + it * m.ss;
+    {  // dB = dY X^T
+      const int K[1] = {l};
+      const MOp P[1] = {{dY, l, 1}}, Q[1] = {{X, 1, l}};
+      wg_mm(s, s, K, P, Q, Ps, Qs, [&](int i, int j, float v) { m.dB[i * s + j] = v; });
     }
-    __syncthreads();
-    for (int64_t idx = tid; idx < ss; idx += kNSThreads) {
-      const int i = static_cast<int>(idx / s), k = static_cast<int>(idx % s);
-      float acc = 0.f, db = 0.f;
-      for (int m = 0; m < s; ++m) acc += A[static_cast<int64_t>(i) * s + m] * A[static_cast<int64_t>(m) * s + k];
-      for (int j = 0; j < l; ++j) db += dY[static_cast<int64_t>(i) * l + j] * X[static_cast<int64_t>(k) * l + j];
-      Bm[idx] = a.b * A[idx] + a.c * acc;
-      dB[idx] = db;
+    {  // dA = b dB + c (dB A^T + A^T dB)
+      const int K[2] = {s, s};
+      const MOp P[2] = {{m.dB, s, 1}, {A, 1, s}}, Q[2] = {{A, 1, s}, {m.dB, s, 1}};
+      wg_mm(s, s, K, P, Q, Ps, Qs, [&](int i, int j, float v) { m.dA[i * s + j] = cb * m.dB[i * s + j] + cc * v; });
     }
-    __syncthreads();
-    for (int64_t idx = tid; idx < ss; idx += kNSThreads) {
-      const int i = static_cast<int>(idx / s), k = static_cast<int>(idx % s);
-      float acc = 0.f;  // (dB A^T + A^T dB)[i][k]
-      for (int m = 0; m < s; ++m)
-        acc += dB[static_cast<int64_t>(i) * s + m] * A[static_cast<int64_t>(k) * s + m] +
-               A[static_cast<int64_t>(m) * s + i] * dB[static_cast<int64_t>(m) * s + k];
-      dA[idx] = a.b * dB[idx] + a.c * acc;
+    {  // dX = a dY + B^T dY + dA X + dA^T X
+      const int K[3] = {s, s, s};
+      const MOp P[3] = {{B, 1, s}, {m.dA, s, 1}, {m.dA, 1, s}}, Q[3] = {{dY, l, 1}, {X, l, 1}, {X, l, 1}};
+      wg_mm(s, l, K, P, Q, Ps, Qs, [&](int i, int j, float v) {
+        dXn[static_cast<int64_t>(i) * l + j] = ca * dY[static_cast<int64_t>(i) * l + j] + v;
+      });
     }
-    __syncthreads();
-    for (int64_t idx = tid; idx < sl; idx += kNSThreads) {
-      const int i = static_cast<int>(idx / l), j = static_cast<int>(idx % l);
-      float acc = a.a * dY[idx];
-      for (int m = 0; m < s; ++m) {
-        acc += Bm[static_cast<int64_t>(m) * s + i] * dY[static_cast<int64_t>(m) * l + j];
-        acc += (dA[static_cast<int64_t>(i) * s + m] + dA[static_cast<int64_t>(m) * s + i]) *
-               X[static_cast<int64_t>(m) * l + j];
-      }
-      dXk[idx] = acc;
-    }
-    __syncthreads();
-    for (int64_t idx = tid; idx < sl; idx += kNSThreads) dY[idx] = dXk[idx];
-    __syncthreads();
+    float* t = dY;
+    dY = dXn;
+    dXn = t;
   }
   // through X0 = G / (n + eps)
-  float dot = 0.f;
-  for (int64_t i = tid; i < sl; i += kNSThreads) dot += dY[i] * at(G, static_cast<int>(i / l), static_cast<int>(i % l));
-  dot = block_sum(dot);
-  const float coef = nrm > 0.f ? dot / (den * den * nrm) : 0.f;
-  for (int64_t idx = tid; idx < sl; idx += kNSThreads) {
+  float part = 0.f, dot = 0.f;
+  for (int64_t idx = tid; idx < m.sl; idx += kNSThreads) {
     const int i = static_cast<int>(idx / l), j = static_cast<int>(idx % l);
-    const float v = dY[idx] / den - coef * at(G, i, j);
-    if (tr) {
-      dG[static_cast<int64_t>(j) * cols + i] = v;
-    } else {
-      dG[static_cast<int64_t>(i) * cols + j] = v;
-    }
+    const float gv = G[m.gidx(i, j)];
+    part += gv * gv;
+    dot += dY[idx] * gv;
+  }
+  const float nrm = sqrtf(ns_block_sum(part, red));
+  dot = ns_block_sum(dot, red);
+  const float den = nrm + a.eps;
+  const float coef = nrm > 0.f ? dot / (den * den * nrm) : 0.f;
+  for (int64_t idx = tid; idx < m.sl; idx += kNSThreads) {
+    const int i = static_cast<int>(idx / l), j = static_cast<int>(idx % l);
+    const int64_t gi = m.gidx(i, j);
+    dG[gi] = dY[idx] / den - coef * G[gi];
   }
 }
 
@@ -659,11 +775,18 @@ hipError_t launch_bw_momentum(const float* t, float* dM, float* Pout, float beta
 
 int64_t bw_ns_floats_per_matrix(int d, int h, int iters) {
   const int64_t s = d < h ? d : h, l = d < h ? h : d;
-  return (iters + 3) * s * l + 4 * s * s;
+  return (iters + 3) * s * l + (2 * iters + 2) * s * s;
 }
 
 hipError_t launch_bw_ns(const BwNSArgs& a, hipStream_t s) {
+  if (a.d % 32 != 0 || a.h % 32 != 0 || (a.d < a.h ? a.d : a.h) > 128) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_bw_ns, dim3(3 * a.P), dim3(kNSThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bw_ns_fwd(const BwNSArgs& a, hipStream_t s) {
+  if (a.d % 32 != 0 || a.h % 32 != 0 || (a.d < a.h ? a.d : a.h) > 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_bw_ns_fwd, dim3(3 * a.P), dim3(kNSThreads), 0, s, a);
   return hipGetLastError();
 }
 

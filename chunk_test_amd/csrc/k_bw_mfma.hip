@@ -41,35 +41,83 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_t;
 
-constexpr int D = 128;
 constexpr int kThreads = 256;
-constexpr int NT = D / 32;         // 32-wide feature tiles
-constexpr int ROW = 2 * D;         // bytes per token row of A or B (sixteen 16-byte chunks)
-constexpr int HS = 128;            // hidden units per workgroup
+constexpr int HS = 128;            // hidden units per contraction workgroup
 constexpr int XROW = 4 * HS;       // bytes per token row of one factor slice (32 chunks)
-constexpr int TT = 32;             // tokens per stage (two k-steps of 16)
-constexpr int TILE = TT * ROW;     // A or B stage
+constexpr int TT = 32;             // tokens per contraction stage (two k-steps of 16)
 constexpr int XTILE = TT * XROW;   // one factor stage
-constexpr int OFF_A = 0;                    // A[2]
-constexpr int OFF_B = 2 * TILE;             // B[2]
-constexpr int OFF_X = 4 * TILE;             // [2][3] factor stages
-constexpr int OFF_E = OFF_X + 6 * XTILE;    // rates [2][TT]
-constexpr int LDS_BYTES = OFF_E + 2 * TT * 4;
 
-// XOR swizzle of the 16-byte chunks of a 256-byte token row of A or B (the
-// layout of the d = 128 chunk-gradient kernel's key tiles): conflict-free
-// 8-byte transpose reads over four rows 4m .. 4m + 3.
-__device__ __forceinline__ int swz(int r) {
-  return 8 * ((r >> 1) & 1) + 4 * ((r ^ (r >> 3)) & 1) + 2 * (r & 1) + ((r >> 2) & 1);
-}
+// bf16 rows of D features (keys, values, queries, or the weight operands) in
+// LDS: rows of 2 D bytes in 16-byte chunks, chunk c of row r stored at chunk
+// c ^ swz(r), the layouts of the d = 128 and d = 64 chunk-gradient kernels'
+// key tiles: 16-byte row reads (16 consecutive rows, one chunk) and 8-byte
+// transpose reads (four rows 4m .. 4m + 3, lanes 16 Q + 4 k' + a addressing
+// row 4 (Q >> 1) + k' (+ 8 hh) of a 16-row half, features
+// 32 nt + 16 (Q & 1) + 4 a .. +3) are both free of bank conflicts.  A pair of
+// transpose reads (hh = 0, 1) gives an MFMA operand whose slot i holds row
+// 8 (i / 4) + 4 g + i % 4 of the half; 1 KiB DMA pieces hold 1024 / ROW rows,
+// lane l landing in row l / LPR, physical chunk l % LPR.
+template <int D>
+struct Rows;
+template <>
+struct Rows<128> {
+  static constexpr int ROW = 256, LPR = 16;
+  __device__ static int swz(int r) {
+    return 8 * ((r >> 1) & 1) + 4 * ((r ^ (r >> 3)) & 1) + 2 * (r & 1) + ((r >> 2) & 1);
+  }
+  __device__ static void tr_init(int lane, int (&o)[4]) {
+    const int tq = lane >> 4, tk = (lane >> 2) & 3, ta = lane & 3;
+    const int tl = 4 * (tq >> 1) + tk;
+    const int r0 = tl & 1, r1 = (tl >> 1) & 1, r2 = (tl >> 2) & 1;
+    const int low = (2 * (tq & 1) + (ta >> 1)) ^ (2 * r0 + r2);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+#pragma unroll
+      for (int n1 = 0; n1 < 2; ++n1) o[2 * x + n1] = tl * ROW + 16 * (8 * (n1 ^ r1) + 4 * (x ^ r0) + low) + 8 * (ta & 1);
+    }
+  }
+  __device__ static int tr(const int (&o)[4], int nt, int hh) { return o[2 * ((nt & 1) ^ hh) + (nt >> 1)]; }
+};
+template <>
+struct Rows<64> {
+  static constexpr int ROW = 128, LPR = 8;
+  __device__ static int swz(int r) { return 4 * (((r >> 1) ^ (r >> 3)) & 1) + 2 * ((r >> 2) & 1) + ((r >> 1) & 1); }
+  __device__ static void tr_init(int lane, int (&o)[4]) {
+    const int tq = lane >> 4, tk = (lane >> 2) & 3, ta = lane & 3;
+    const int tl = 4 * (tq >> 1) + tk;
+    const int t1 = (tl >> 1) & 1, t2 = (tl >> 2) & 1;
+    const int low = (2 * (tq & 1) + (ta >> 1)) ^ (2 * t2 + t1);
+#pragma unroll
+    for (int x = 0; x < 2; ++x) o[x] = tl * ROW + 16 * (4 * (x ^ t1) + low) + 8 * (ta & 1);
+    o[2] = o[3] = 0;
+  }
+  __device__ static int tr(const int (&o)[4], int nt, int hh) { return o[nt ^ hh]; }
+};
+
+// the contraction kernel's LDS: A[2], B[2] stages, [2][3] factor stages, rates [2][TT]
+template <int D>
+struct CGeo {
+  static constexpr int NT = D / 32;
+  static constexpr int TILE = TT * Rows<D>::ROW;
+  static constexpr int OFF_A = 0;
+  static constexpr int OFF_B = 2 * TILE;
+  static constexpr int OFF_X = 4 * TILE;
+  static constexpr int OFF_E = OFF_X + 6 * XTILE;
+  static constexpr int LDS_BYTES = OFF_E + 2 * TT * 4;
+};
 
 __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_bw_contract_mfma(BwContractArgs a, int hsl, int nbase) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+  using R = Rows<D>;
+  using C = CGeo<D>;
+  constexpr int NT = C::NT, ROW = R::ROW, TILE = C::TILE;
+  constexpr int OFF_A = C::OFF_A, OFF_B = C::OFF_B, OFF_X = C::OFF_X, OFF_E = C::OFF_E;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS_BYTES];
 
   // XCD-aware block order: the hidden slices of one (pair, split) land on the
   // same XCD (block ids congruent mod 8), so their A and B reads share L2.
@@ -102,9 +150,8 @@ void k_bw_contract_mfma(BwContractArgs a, int hsl, int nbase) {
                         a.X3 + static_cast<int64_t>(pair) * a.x_stride + j0,
                         a.X2 + static_cast<int64_t>(pair) * a.x_stride + j0};
 
-  // DMA of one stage into buffer b.  A, B: 1 KiB pieces of four rows, lane l
-  // of a piece landing at byte 16 l (row 4 piece + l / 16, physical chunk
-  // l % 16 holding logical chunk (l % 16) ^ swz(row)).  Factors: 1 KiB pieces
+  // DMA of one stage into buffer b.  A, B: 1 KiB pieces in the Rows<D>
+  // layout (one piece per wave at d = 64, two at d = 128).  Factors: 1 KiB pieces
   // of two 512-byte rows, physical chunk p of row t holding logical chunk
   // p ^ (8 ((t >> 2) & 1)), so the two half-waves of a factor read (tokens
   // four apart) use different banks.  Rows past the split's end re-read its
@@ -113,10 +160,10 @@ void k_bw_contract_mfma(BwContractArgs a, int hsl, int nbase) {
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
 #pragma unroll
-    for (int k = 0; k < TT / 16; ++k) {
+    for (int k = 0; k < TILE / 4096; ++k) {
       const int piece = 4 * k + wv;
-      const int r = 4 * piece + (lane >> 4);
-      const int cl = (lane & 15) ^ swz(r);
+      const int r = (1024 / ROW) * piece + lane / R::LPR;
+      const int cl = (lane % R::LPR) ^ R::swz(r);
       const int tok = static_cast<int>(t0) + r;
       const int tc = tok < t_last ? tok : t_last;
       const unsigned off = static_cast<unsigned>(tc) * D + 8 * cl;
@@ -148,24 +195,9 @@ void k_bw_contract_mfma(BwContractArgs a, int hsl, int nbase) {
     }
   };
 
-  // transpose reads of A and B (as in the d = 128 chunk-gradient kernel):
-  // lane 16 Q + 4 k' + a of each 16-lane row Q addresses token
-  // 4 (Q >> 1) + k' (+ 8 hh) of a 16-token half, features
-  // 32 nt + 16 (Q & 1) + 4 a .. +3; the pair (hh = 0, 1) gives the operand
-  // whose slot i holds token 8 (i / 4) + 4 g + i % 4 of the half.
-  const int tq = lane >> 4, tk = (lane >> 2) & 3, ta = lane & 3;
-  int tr_off[2][2];
-  {
-    const int tl = 4 * (tq >> 1) + tk;
-    const int r0 = tl & 1, r1 = (tl >> 1) & 1, r2 = (tl >> 2) & 1;
-    const int low = (2 * (tq & 1) + (ta >> 1)) ^ (2 * r0 + r2);
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-#pragma unroll
-      for (int n1 = 0; n1 < 2; ++n1)
-        tr_off[x][n1] = tl * ROW + 16 * (8 * (n1 ^ r1) + 4 * (x ^ r0) + low) + 8 * (ta & 1);
-    }
-  }
+  // transpose reads of A and B (tokens as the k index, Rows<D>)
+  int tro[4];
+  R::tr_init(lane, tro);
   // factor reads: slot i of lane (g, ln) is token 8 (i / 4) + 4 g + i % 4 of
   // the 16-token half, hidden unit 32 wave + ln of the slice; bit 2 of those
   // tokens is g, so the swizzled chunk is a lane constant.
@@ -230,7 +262,7 @@ void k_bw_contract_mfma(BwContractArgs a, int hsl, int nbase) {
         s16x4_t ta2[2], tb2[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int off = tr_off[(nt & 1) ^ hh][nt >> 1] + 4096 * s + 2048 * hh;
+          const int off = R::tr(tro, nt, hh) + 16 * ROW * s + 8 * ROW * hh;
           ta2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(ab + off));
           tb2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t)(bb + off));
         }
@@ -265,6 +297,7 @@ void k_bw_contract_mfma(BwContractArgs a, int hsl, int nbase) {
 // Operands of the token kernels: every matrix as bf16 hi and lo parts in
 // [hidden unit][feature] order (W2 and P2, stored [feature][hidden unit], are
 // transposed): op[pair][m][hl][j][e], m over W1, W3, W2 (and P1, P3, P2).
+template <int D>
 __global__ __launch_bounds__(kThreads) void k_bw_ops(BwOpsArgs a) {
   const int64_t hd = static_cast<int64_t>(a.h) * D;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
@@ -283,18 +316,20 @@ __global__ __launch_bounds__(kThreads) void k_bw_ops(BwOpsArgs a) {
   o[hd + e_idx] = lo;
 }
 
-constexpr int KS = D / 16;           // k-steps over the features
-constexpr int QWG = 128;             // queries per workgroup (32 per wave)
+constexpr int QWG = 128;             // tokens per token-kernel workgroup (32 per wave)
 constexpr int JT = 32;               // hidden units per weight tile
-constexpr int WHALF = JT * ROW;      // one matrix part (hi or lo) of a tile: 8 KiB
-constexpr int WTILE3 = 6 * WHALF;    // W1, W3, W2^T, hi and lo
 
 __device__ __forceinline__ float sigmoid_fast(float z) {
   return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
 }
 
+template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_bw_apply_mfma(BwTokArgs a) {
+  using R = Rows<D>;
+  constexpr int NT = D / 32, KS = D / 16, ROW = R::ROW;
+  constexpr int WHALF = JT * ROW;     // one matrix part (hi or lo) of a weight tile
+  constexpr int WTILE3 = 6 * WHALF;   // W1, W3, W2^T, hi and lo
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * WTILE3];
   const int pair = blockIdx.y;
   const int64_t tb = static_cast<int64_t>(blockIdx.x) * QWG;
@@ -324,49 +359,38 @@ void k_bw_apply_mfma(BwTokArgs a) {
     }
   }
 
-  // DMA of weight tile jt (rows 32 jt .. +31 of the six parts) into buffer b:
-  // 48 pieces of 1 KiB (four rows), lane l landing at byte 16 l (row
-  // 4 (piece % 8) + l / 16, physical chunk l % 16 holding chunk (l % 16) ^ swz(row))
+  // DMA of weight tile jt (rows 32 jt .. +31 of the six parts) into buffer b,
+  // 1 KiB pieces in the Rows<D> layout (PP pieces per part)
+  constexpr int PP = WHALF / 1024;
   auto dma_w = [&](int jt, int b) {
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
 #pragma unroll
-    for (int k = 0; k < 12; ++k) {
+    for (int k = 0; k < 6 * PP / 4; ++k) {
       const int piece = 4 * k + wv;
-      const int part = piece >> 3;
-      const int r = 4 * (piece & 7) + (lane >> 4);
-      const int cl = (lane & 15) ^ swz(r);
+      const int part = piece / PP;
+      const int r = (1024 / ROW) * (piece % PP) + lane / R::LPR;
+      const int cl = (lane % R::LPR) ^ R::swz(r);
       const uint16_t* src = opg + part * hd + static_cast<int64_t>(JT * jt + r) * D + 8 * cl;
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(lds + b * WTILE3 + part * WHALF + 1024 * (piece & 7)),
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(lds + b * WTILE3 + part * WHALF + 1024 * (piece % PP)),
                                        16, 0, 0);
     }
   };
 
   // row reads of a part (lane = hidden unit ln of the tile, features
   // 16 ks + 8 g .. +7) and transpose reads (lane = feature 32 nt + ln, slot i
-  // = hidden unit 16 s + 8 (i / 4) + 4 g + i % 4 of the tile)
+  // = hidden unit 16 s + 8 (i / 4) + 4 g + i % 4 of the tile), Rows<D>
   int ak_off[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) ak_off[ks] = ln * ROW + 16 * ((2 * ks + g) ^ swz(ln));
-  const int tq = lane >> 4, tk = (lane >> 2) & 3, ta = lane & 3;
-  int tr_off[2][2];
-  {
-    const int tl = 4 * (tq >> 1) + tk;
-    const int r0 = tl & 1, r1 = (tl >> 1) & 1, r2 = (tl >> 2) & 1;
-    const int low = (2 * (tq & 1) + (ta >> 1)) ^ (2 * r0 + r2);
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-#pragma unroll
-      for (int n1 = 0; n1 < 2; ++n1)
-        tr_off[x][n1] = tl * ROW + 16 * (8 * (n1 ^ r1) + 4 * (x ^ r0) + low) + 8 * (ta & 1);
-    }
-  }
+  for (int ks = 0; ks < KS; ++ks) ak_off[ks] = ln * ROW + 16 * ((2 * ks + g) ^ R::swz(ln));
+  int tro[4];
+  R::tr_init(lane, tro);
   auto tr_read = [&](const unsigned char* base, int nt, int s) {
     s16x4_t t2[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
       t2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4_t)(base + tr_off[(nt & 1) ^ hh][nt >> 1] + 4096 * s + 2048 * hh));
+          (lds_s16x4_t)(base + R::tr(tro, nt, hh) + 16 * ROW * s + 8 * ROW * hh));
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t2[0], t2[1], 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
@@ -473,7 +497,6 @@ void k_bw_apply_mfma(BwTokArgs a) {
   }
 }
 
-constexpr int WTILE6 = 12 * WHALF;  // W1, W3, W2^T, P1, P3, P2^T, hi and lo: 96 KiB
 
 // Token-local VJP of the chunk gradient on MFMA: per key k (value v, rate
 // eta) and hidden unit j, with u = -eta v,
@@ -488,8 +511,13 @@ constexpr int WTILE6 = 12 * WHALF;  // W1, W3, W2^T, P1, P3, P2^T, hi and lo: 96
 // six token-side products per weight tile, all split-operand MFMAs; the
 // weight tile (twelve bf16 parts) is one LDS buffer, refilled after every
 // wave has finished with it.
+template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_bw_grad_mfma(BwTokArgs a) {
+  using R = Rows<D>;
+  constexpr int NT = D / 32, KS = D / 16, ROW = R::ROW;
+  constexpr int WHALF = JT * ROW;     // one matrix part (hi or lo) of a weight tile
+  constexpr int WTILE6 = 12 * WHALF;  // W1, W3, W2^T, P1, P3, P2^T, hi and lo
   __shared__ __attribute__((aligned(16))) unsigned char lds[WTILE6];
   const int pair = blockIdx.y;
   const int64_t tb = static_cast<int64_t>(blockIdx.x) * QWG;
@@ -517,42 +545,32 @@ void k_bw_grad_mfma(BwTokArgs a) {
   }
   const float ne = live ? -a.eta[pair * a.eta_stride + t] : 0.f;
 
+  constexpr int PP = WHALF / 1024;  // 1 KiB pieces per part
   auto dma_w = [&](int jt) {
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
 #pragma unroll
-    for (int k = 0; k < 24; ++k) {
+    for (int k = 0; k < 12 * PP / 4; ++k) {
       const int piece = 4 * k + wv;
-      const int part = piece >> 3;
-      const int r = 4 * (piece & 7) + (lane >> 4);
-      const int cl = (lane & 15) ^ swz(r);
+      const int part = piece / PP;
+      const int r = (1024 / ROW) * (piece % PP) + lane / R::LPR;
+      const int cl = (lane % R::LPR) ^ R::swz(r);
       const uint16_t* src = opg + part * hd + static_cast<int64_t>(JT * jt + r) * D + 8 * cl;
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(lds + part * WHALF + 1024 * (piece & 7)), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(lds + part * WHALF + 1024 * (piece % PP)), 16, 0, 0);
     }
   };
 
   int ak_off[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) ak_off[ks] = ln * ROW + 16 * ((2 * ks + g) ^ swz(ln));
-  const int tq = lane >> 4, tk = (lane >> 2) & 3, ta = lane & 3;
-  int tr_off[2][2];
-  {
-    const int tl = 4 * (tq >> 1) + tk;
-    const int r0 = tl & 1, r1 = (tl >> 1) & 1, r2 = (tl >> 2) & 1;
-    const int low = (2 * (tq & 1) + (ta >> 1)) ^ (2 * r0 + r2);
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-#pragma unroll
-      for (int n1 = 0; n1 < 2; ++n1)
-        tr_off[x][n1] = tl * ROW + 16 * (8 * (n1 ^ r1) + 4 * (x ^ r0) + low) + 8 * (ta & 1);
-    }
-  }
+  for (int ks = 0; ks < KS; ++ks) ak_off[ks] = ln * ROW + 16 * ((2 * ks + g) ^ R::swz(ln));
+  int tro[4];
+  R::tr_init(lane, tro);
   auto tr_read = [&](const unsigned char* base, int nt, int s) {
     s16x4_t t2[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
       t2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_s16x4_t)(base + tr_off[(nt & 1) ^ hh][nt >> 1] + 4096 * s + 2048 * hh));
+          (lds_s16x4_t)(base + R::tr(tro, nt, hh) + 16 * ROW * s + 8 * ROW * hh));
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t2[0], t2[1], 0, 1, 2, 3, 4, 5, 6, 7));
   };
   auto part = [&](int m, int hl) { return static_cast<const unsigned char*>(lds + (2 * m + hl) * WHALF); };
@@ -683,15 +701,21 @@ bool bw_contract_mfma_ok(const BwContractArgs& a) {
   const uintptr_t al = reinterpret_cast<uintptr_t>(a.A) | reinterpret_cast<uintptr_t>(a.B) |
                        reinterpret_cast<uintptr_t>(a.X1) | reinterpret_cast<uintptr_t>(a.X2) |
                        reinterpret_cast<uintptr_t>(a.X3);
-  return a.bf16 && a.d == D && a.h % HS == 0 && (al & 15) == 0 && (a.in_stride % 8) == 0 && (a.x_stride % 4) == 0 &&
-         a.n * D < (int64_t(1) << 31);
+  return a.bf16 && (a.d == 64 || a.d == 128) && a.h % HS == 0 && (al & 15) == 0 && (a.in_stride % 8) == 0 &&
+         (a.x_stride % 4) == 0 && a.n * a.d < (int64_t(1) << 31);
 }
 
 hipError_t launch_bw_contract_mfma(const BwContractArgs& a, hipStream_t s) {
   const int hsl = a.h / HS;
   const int nbase = a.S * a.P;
   const int blocks = ((nbase + 7) / 8) * 8 * hsl;
-  hipLaunchKernelGGL(k_bw_contract_mfma, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  if (a.d == 128) {
+    hipLaunchKernelGGL(k_bw_contract_mfma<128>, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  } else if (a.d == 64) {
+    hipLaunchKernelGGL(k_bw_contract_mfma<64>, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -705,23 +729,34 @@ bool bw_tok_mfma_ok(const BwTokArgs& a, bool apply) {
                        reinterpret_cast<uintptr_t>(a.X3) | reinterpret_cast<uintptr_t>(a.dA) |
                        reinterpret_cast<uintptr_t>(a.op);
   const uintptr_t al2 = apply ? 0 : reinterpret_cast<uintptr_t>(a.dB);
-  return a.op != nullptr && a.bf16 && a.d == D && a.h % JT == 0 && ((al | al2) & 15) == 0 && (a.in_stride % 8) == 0 &&
-         (a.out_stride % 8) == 0 && (a.x_stride % 4) == 0 && (apply || a.eta != nullptr);
+  return a.op != nullptr && a.bf16 && (a.d == 64 || a.d == 128) && a.h % JT == 0 && ((al | al2) & 15) == 0 &&
+         (a.in_stride % 8) == 0 && (a.out_stride % 8) == 0 && (a.x_stride % 4) == 0 && (apply || a.eta != nullptr);
 }
 
 hipError_t launch_bw_ops(const BwOpsArgs& a, hipStream_t s) {
-  if (a.d != D || a.nm < 1 || a.nm > 6 || a.op_stride < static_cast<int64_t>(2) * a.nm * a.h * D) return hipErrorInvalidValue;
-  const int64_t total = static_cast<int64_t>(a.P) * a.nm * a.h * D;
-  hipLaunchKernelGGL(k_bw_ops, dim3(static_cast<unsigned>((total + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, a);
+  if ((a.d != 64 && a.d != 128) || a.nm < 1 || a.nm > 6 ||
+      a.op_stride < static_cast<int64_t>(2) * a.nm * a.h * a.d)
+    return hipErrorInvalidValue;
+  const int64_t total = static_cast<int64_t>(a.P) * a.nm * a.h * a.d;
+  const dim3 grid(static_cast<unsigned>((total + kThreads - 1) / kThreads));
+  if (a.d == 128) {
+    hipLaunchKernelGGL(k_bw_ops<128>, grid, dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(k_bw_ops<64>, grid, dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_bw_tok_mfma(const BwTokArgs& a, bool apply, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((a.n + QWG - 1) / QWG), a.P);
-  if (apply) {
-    hipLaunchKernelGGL(k_bw_apply_mfma, grid, dim3(kThreads), 0, s, a);
+  if (a.d == 128) {
+    if (apply) hipLaunchKernelGGL(k_bw_apply_mfma<128>, grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL(k_bw_grad_mfma<128>, grid, dim3(kThreads), 0, s, a);
+  } else if (a.d == 64) {
+    if (apply) hipLaunchKernelGGL(k_bw_apply_mfma<64>, grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL(k_bw_grad_mfma<64>, grid, dim3(kThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL(k_bw_grad_mfma, grid, dim3(kThreads), 0, s, a);
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

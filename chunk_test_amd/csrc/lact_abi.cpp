@@ -671,7 +671,7 @@ BwLayout bw_layout(const lact_config* c, const Plan& p, int64_t N, int64_t chunk
   b.t = take(sizeof(float) * per);
   b.X = take(sizeof(float) * 3 * static_cast<size_t>(p.P) * static_cast<size_t>(b.rows) * p.h);
   b.part = take(sizeof(float) * per * static_cast<size_t>(b.S));
-  b.op = take(p.bf16 && p.d == 128 ? sizeof(uint16_t) * 4 * per : 0);
+  b.op = take(p.bf16 && (p.d == 64 || p.d == 128) ? sizeof(uint16_t) * 4 * per : 0);
   b.ns = take(p.muon ? sizeof(float) * 3 * static_cast<size_t>(p.P) *
                            static_cast<size_t>(lact::bw_ns_floats_per_matrix(p.d, p.h, c->ns_iters))
                      : 0);
@@ -795,7 +795,7 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
     a.h = p.h;
     a.bf16 = p.bf16;
     hipError_t err;
-    if (p.bf16 && p.d == 128) {  // (the operand region exists exactly then)
+    if (p.bf16 && (p.d == 64 || p.d == 128)) {  // (the operand region exists exactly then)
       // operands of the matrix-core token kernels as bf16 hi | lo: W1, W3, W2^T
       // (and for the chunk gradient's VJP P1, P3, P2^T)
       lact::BwOpsArgs o{};
@@ -876,20 +876,22 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
     }
     const float* direction = gb;
     if (p.muon) {
-      if ((e = hipMemcpyAsync(dirb, gb, sizeof(float) * per, hipMemcpyDeviceToDevice, s)) != hipSuccess)
-        return hip_fail(e, "direction copy");
-      lact::NSArgs a{};
-      a.dir = dirb;
-      a.scratch = reinterpret_cast<float*>(ws + L.fwd.ns);
-      a.P = p.P;
-      a.d = p.d;
-      a.h = p.h;
-      a.iters = c->ns_iters;
-      a.a = c->ns_a;
-      a.b = c->ns_b;
-      a.c = c->ns_c;
-      a.eps = c->ns_eps;
-      if ((e = lact::launch_ns_simple(a, s)) != hipSuccess) return hip_fail(e, "Newton-Schulz kernel");
+      // Newton-Schulz forward: the direction, with the iterates kept in the
+      // VJP's scratch
+      lact::BwNSArgs nf{};
+      nf.g = gb;
+      nf.out = dirb;
+      nf.scratch = reinterpret_cast<float*>(ws + L.ns);
+      nf.per_mat = lact::bw_ns_floats_per_matrix(p.d, p.h, c->ns_iters);
+      nf.P = p.P;
+      nf.d = p.d;
+      nf.h = p.h;
+      nf.iters = c->ns_iters;
+      nf.a = c->ns_a;
+      nf.b = c->ns_b;
+      nf.c = c->ns_c;
+      nf.eps = c->ns_eps;
+      if ((e = lact::launch_bw_ns_fwd(nf, s)) != hipSuccess) return hip_fail(e, "Newton-Schulz kernel");
       direction = dirb;
     }
     // through the step and the row normalisation

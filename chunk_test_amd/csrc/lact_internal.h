@@ -155,7 +155,7 @@ struct BwOpsArgs {  // matrices as bf16 hi | lo parts in [hidden][feature] order
   int nm;           // 3 or 6
   uint16_t* op;     // [P][nm][2][h][d]
   int64_t op_stride;
-  int P, d, h;  // d must be 128
+  int P, d, h;  // d = 64 or 128
 };
 struct BwContractArgs {  // X1^T A, (b B)^T X2, X3^T A over tokens, b = -eta or 1
   const void* A;
@@ -188,19 +188,22 @@ struct BwNSArgs {
 };
 bool backward_shape_ok(int d, int h);
 hipError_t launch_bw_tok(const BwTokArgs& a, bool apply, hipStream_t s);
-// matrix-core token kernel of the query read (bf16, d = 128, h a multiple of 32,
-// operands from launch_bw_ops)
+// matrix-core token kernels (bf16, d = 64 or 128, h a multiple of 32, operands from
+// launch_bw_ops)
 bool bw_tok_mfma_ok(const BwTokArgs& a, bool apply);
 hipError_t launch_bw_tok_mfma(const BwTokArgs& a, bool apply, hipStream_t s);
 hipError_t launch_bw_ops(const BwOpsArgs& a, hipStream_t s);
 hipError_t launch_bw_contract(const BwContractArgs& a, hipStream_t s);
-// the bf16 matrix-core contraction (d = 128, h a multiple of 128, 16-byte aligned inputs)
+// the bf16 matrix-core contraction (d = 64 or 128, h a multiple of 128, 16-byte aligned inputs)
 bool bw_contract_mfma_ok(const BwContractArgs& a);
 hipError_t launch_bw_contract_mfma(const BwContractArgs& a, hipStream_t s);
 hipError_t launch_bw_reduce_add(float* dst, const float* partials, int S, int64_t per, int P, hipStream_t s);
 hipError_t launch_bw_step(const BwStepArgs& a, hipStream_t s);
 hipError_t launch_bw_momentum(const float* t, float* dM, float* Pout, float beta, int64_t total, hipStream_t s);
 int64_t bw_ns_floats_per_matrix(int d, int h, int iters);
+// Newton-Schulz forward (iterates into scratch, direction into out) and its
+// VJP (from the same scratch; dx the direction's cotangent, out the input's)
+hipError_t launch_bw_ns_fwd(const BwNSArgs& a, hipStream_t s);
 hipError_t launch_bw_ns(const BwNSArgs& a, hipStream_t s);
 hipError_t launch_bw_copy(float* blocks, const MatRef& m1, const MatRef& m2, const MatRef& m3, int P, int d, int h,
                           bool to_blocks, hipStream_t s);

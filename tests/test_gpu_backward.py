@@ -78,6 +78,12 @@ CASES += [
     # (ragged last stage and split in the matrix-core contractions)
     S.WORKLOADS["lm"].replace(name="bw-lm-bf16-ragged", B=1, H=2, T_kv=3 * 1000, chunk_kv=1000,
                               T_q=3 * 200, chunk_q=200, order="update_then_apply"),
+    # the same at d = 64 (posed and million-token shapes), Muon, both orders
+    S.WORKLOADS["posed"].replace(name="bw-posed-bf16-ragged", H=2, T_kv=3 * 700, chunk_kv=700,
+                                 T_q=3 * 100, chunk_q=100, products="auto"),
+    S.WORKLOADS["posed"].replace(name="bw-posed-bf16-a", H=3, T_kv=2 * 2048, chunk_kv=2048,
+                                 T_q=2 * 256, chunk_q=256, order="apply_then_update", opt="momentum",
+                                 beta=0.9),
 ]
 
 
