@@ -164,6 +164,21 @@ __device__ __forceinline__ void quad_tr(unsigned& w0, unsigned& w1, int p) {
   w1 = (p & 2) ? n1 : recv;
 }
 
+// Tile u of the tiles on and above the diagonal of an MT x MT tile grid, row
+// by row: (0, 0), (0, 1), .., (0, MT - 1), (1, 1), ...
+template <int MT>
+__device__ __forceinline__ void upper_tile(int u, int& ti, int& tj) {
+  ti = 0;
+#pragma unroll
+  for (int r = 0; r < MT - 1; ++r) {
+    if (u >= MT - ti) {
+      u -= MT - ti;
+      ++ti;
+    }
+  }
+  tj = ti + u;
+}
+
 // Column order of the stored s x s matrices A and B: inside every 16 columns
 // the two groups {0-3, 8-11} and {4-7, 12-15} are stored as contiguous runs of
 // eight, so the B X step (whose k order follows the MFMA output rows of X)
@@ -192,7 +207,15 @@ struct NSGeo {
   static constexpr int R1 = (2 * X_HALF > 2 * A_HALF) ? 2 * X_HALF : 2 * A_HALF;
   static constexpr int REGION = (R1 > STG) ? R1 : STG;  // the staging shares the region
   static constexpr int ATILES = MT * MT;
-  static constexpr int ATW = (ATILES + NW - 1) / NW;  // A tiles per wave
+  // with two wavefronts per SIMD (eight in all) only the tiles on and above
+  // the diagonal of the symmetric A and B are computed (NU of them, at most
+  // UTW per wave: three per SIMD instead of four at s = 128) and each is
+  // stored in both places
+  static constexpr bool SYM = (NW == 8);
+  static constexpr int NU = MT * (MT + 1) / 2;
+  static constexpr int UTW = (NU + NW - 1) / NW;
+  static constexpr int ATW0 = (ATILES + NW - 1) / NW;
+  static constexpr int ATW = SYM ? UTW : ATW0;  // A tiles per wave
   // one wave per SIMD with registers to spare: read each phase's operands
   // ahead, keep X in fp32 across the iteration, load W at the start
   static constexpr bool PRE = (S == 64 && L == 128);
@@ -336,6 +359,42 @@ __device__ __forceinline__ void muon_tail_body(const TailArgs& a, unsigned char*
   unsigned char* ahi = lds;
   unsigned char* alo = lds + G::A_HALF;
 
+  // Stores tile (ti, tj) of a symmetric s x s matrix (A or B) as hi / lo
+  // bf16: transposed, at rows 32 tj + ln, columns 32 ti + 8 (r/4) + 4 g .. +3
+  // (four consecutive bf16 per store, at their stored columns), which for a
+  // symmetric matrix is tile (tj, ti); off the diagonal, with only the tiles
+  // on and above it computed, also in place, through a quad transpose
+  // (lane p of quad m then holds row 32 ti + 8 rg + 4 g + p, columns
+  // 32 tj + 4 m .. +3).
+  auto store_sym = [&](const f32x16_t& v, int ti, int tj) {
+    const int p = ln & 3, m = ln >> 2;
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      bf16x4_t h4, l4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __bf16 hi, lo;
+        split(v[4 * rg + i], hi, lo);
+        h4[i] = hi;
+        l4[i] = lo;
+      }
+      const int off = (32 * tj + ln) * G::ARS + 2 * stored_col(ti, rg, g);
+      *reinterpret_cast<bf16x4_t*>(ahi + off) = h4;
+      *reinterpret_cast<bf16x4_t*>(alo + off) = l4;
+      if (G::SYM && ti != tj) {
+        unsigned hw0 = __builtin_bit_cast(unsigned, bf16x2_t{h4[0], h4[1]});
+        unsigned hw1 = __builtin_bit_cast(unsigned, bf16x2_t{h4[2], h4[3]});
+        unsigned lw0 = __builtin_bit_cast(unsigned, bf16x2_t{l4[0], l4[1]});
+        unsigned lw1 = __builtin_bit_cast(unsigned, bf16x2_t{l4[2], l4[3]});
+        quad_tr(hw0, hw1, p);
+        quad_tr(lw0, lw1, p);
+        const int off2 = (32 * ti + 8 * rg + 4 * g + p) * G::ARS + 2 * stored_col(tj, m >> 1, m & 1);
+        *reinterpret_cast<uint2*>(ahi + off2) = make_uint2(hw0, hw1);
+        *reinterpret_cast<uint2*>(alo + off2) = make_uint2(lw0, lw1);
+      }
+    }
+  };
+
   for (int it = 0; it < a.iters; ++it) {
     // ---- X split once into hi / lo bf16 operands, kept in registers as
     // packed pairs in the B-operand order of B X (k-step s, slot i <->
@@ -389,7 +448,24 @@ __device__ __forceinline__ void muon_tail_body(const TailArgs& a, unsigned char*
     f32x16_t at[G::ATW];
     // chunk 2 ks + g of row 32 t + ln, swizzled (xsw depends on ln % 16 only)
     const int yx = 16 * (g ^ xsw(ln));
-    if constexpr (G::ATILES % G::NW == 0) {
+    if constexpr (G::SYM) {
+#pragma unroll
+      for (int q = 0; q < G::ATW; ++q) {
+        const int u = w + G::NW * q;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) at[q][r] = 0.f;
+        if (u < G::NU) {
+          int ti, tj;
+          upper_tile<G::MT>(u, ti, tj);
+          const unsigned char* pa[1] = {xhi + (32 * ti + ln) * G::XRS};
+          const unsigned char* pb[1] = {xhi + (32 * tj + ln) * G::XRS};
+          f32x16_t hh[1], a2[1];
+          split_tiles<1, L / 16, false, true>(pa, pb, yx, G::X_HALF, hh, a2);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) at[q][r] = hh[0][r] + a2[0][r];
+        }
+      }
+    } else if constexpr (G::ATILES % G::NW == 0) {
       const unsigned char* pa[G::ATW];
       const unsigned char* pb[G::ATW];
 #pragma unroll
@@ -429,28 +505,36 @@ __device__ __forceinline__ void muon_tail_body(const TailArgs& a, unsigned char*
 #pragma unroll
     for (int q = 0; q < G::ATW; ++q) {
       const int t = w + G::NW * q;
-      if (t < G::ATILES) {
-        const int ti = t / G::MT, tj = t % G::MT;
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          bf16x4_t h4, l4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            __bf16 hi, lo;
-            split(at[q][4 * rg + i], hi, lo);
-            h4[i] = hi;
-            l4[i] = lo;
-          }
-          const int off = (32 * tj + ln) * G::ARS + 2 * stored_col(ti, rg, g);
-          *reinterpret_cast<bf16x4_t*>(ahi + off) = h4;
-          *reinterpret_cast<bf16x4_t*>(alo + off) = l4;
+      if (t < (G::SYM ? G::NU : G::ATILES)) {
+        int ti, tj;
+        if constexpr (G::SYM) {
+          upper_tile<G::MT>(t, ti, tj);
+        } else {
+          ti = t / G::MT;
+          tj = t % G::MT;
         }
+        store_sym(at[q], ti, tj);
       }
     }
     __syncthreads();
 
     // ---- B = b A + c A A on the same tiles (A symmetric: both operands are rows of A)
-    if constexpr (G::ATILES % G::NW == 0) {
+    if constexpr (G::SYM) {
+#pragma unroll
+      for (int q = 0; q < G::ATW; ++q) {
+        const int u = w + G::NW * q;
+        if (u < G::NU) {
+          int ti, tj;
+          upper_tile<G::MT>(u, ti, tj);
+          const unsigned char* pa[1] = {ahi + (32 * ti + ln) * G::ARS};
+          const unsigned char* pb[1] = {ahi + (32 * tj + ln) * G::ARS};
+          f32x16_t acc[1], a2[1];
+          split_tiles<1, S / 16, false, false>(pa, pb, 16 * g, G::A_HALF, acc, a2);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) at[q][r] = a.b * at[q][r] + a.c * (acc[0][r] + a2[0][r]);  // now B
+        }
+      }
+    } else if constexpr (G::ATILES % G::NW == 0) {
       const unsigned char* pa[G::ATW];
       const unsigned char* pb[G::ATW];
 #pragma unroll
@@ -485,22 +569,15 @@ __device__ __forceinline__ void muon_tail_body(const TailArgs& a, unsigned char*
 #pragma unroll
     for (int q = 0; q < G::ATW; ++q) {
       const int t = w + G::NW * q;
-      if (t < G::ATILES) {
-        const int ti = t / G::MT, tj = t % G::MT;
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          bf16x4_t h4, l4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            __bf16 hi, lo;
-            split(at[q][4 * rg + i], hi, lo);
-            h4[i] = hi;
-            l4[i] = lo;
-          }
-          const int off = (32 * tj + ln) * G::ARS + 2 * stored_col(ti, rg, g);
-          *reinterpret_cast<bf16x4_t*>(ahi + off) = h4;
-          *reinterpret_cast<bf16x4_t*>(alo + off) = l4;
+      if (t < (G::SYM ? G::NU : G::ATILES)) {
+        int ti, tj;
+        if constexpr (G::SYM) {
+          upper_tile<G::MT>(t, ti, tj);
+        } else {
+          ti = t / G::MT;
+          tj = t % G::MT;
         }
+        store_sym(at[q], ti, tj);
       }
     }
     __syncthreads();
