@@ -461,12 +461,19 @@ struct MOp {  // element (i, k) of a matrix operand at p[i * rs + k * cs]
 
 // C (M x N) = sum over the terms t < NTERM of op(P_t) (M x K_t) op(Q_t) (K_t x N),
 // handed to epi(i, j, value) element by element.  M <= 128, M, N, K_t
-// multiples of 32.  Ps: 32 x (M + 1) floats, Qs: 32 x (kNB + 1) floats of LDS.
+// multiples of 32.  The operands move through LDS 32 k values at a time,
+// double-buffered: while the wavefronts multiply one chunk (Ps: 32 x (M + 1),
+// Qs: 32 x (kNB + 1) floats per buffer), every thread holds its share of the
+// next chunk's global loads in registers and then stores it into the other
+// buffer.  Each thread's share is fixed per term (its LDS slots and element
+// offsets), so only the chunk offset changes from chunk to chunk.
 template <int NTERM, class Epi>
 __device__ __forceinline__ void wg_mm(int M, int N, const int (&K)[NTERM], const MOp (&P)[NTERM],
                                       const MOp (&Q)[NTERM], float* Ps, float* Qs, Epi epi) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, ln = lane & 31;
   const int ps = M + 1;
+  constexpr int PSZ = 32 * 129, QSZ = 32 * (kNB + 1);                        // floats per buffer
+  constexpr int MP = 32 * 128 / kNSThreads, MQ = 32 * kNB / kNSThreads;  // staged values per thread
   for (int nb = 0; nb < N; nb += kNB) {
     const int NB = min(kNB, N - nb), qs = NB + 1;
     const int ntl = NB / 32, tiles = (M / 32) * ntl;  // <= 32: at most four per wave
@@ -476,36 +483,82 @@ __device__ __forceinline__ void wg_mm(int M, int N, const int (&K)[NTERM], const
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
     }
-#pragma unroll
+#pragma unroll 1
     for (int t = 0; t < NTERM; ++t) {
       const MOp p = P[t], q = Q[t];
-      for (int kc = 0; kc < K[t]; kc += 32) {
-        __syncthreads();  // the previous chunk's readers are done
-        // stage op(P)[0..M)[kc..kc+32) as Ps[k][i], op(Q)[kc..kc+32)[nb..nb+NB) as Qs[k][j]
-        // (the loop order follows the operand's contiguous index)
+      // this thread's share of a chunk: element e is idx = tid + 512 e of the
+      // chunk (in the order of the operand's contiguous index), at LDS slot
+      // *l and offset *o from the chunk's first k (recomputed where used:
+      // a few integer operations, where keeping them would cost registers)
+      auto pslot = [&](int e, int& l, int& o) {
+        int t2 = tid;
+        asm volatile("" : "+v"(t2));  // (not hoisted out of the chunk loop)
+        const int idx = t2 + kNSThreads * e;
+        int i, k;
         if (p.cs == 1) {
-          for (int idx = tid; idx < 32 * M; idx += kNSThreads) {
-            const int k = idx & 31, i = idx >> 5;
-            Ps[k * ps + i] = p.p[static_cast<int64_t>(i) * p.rs + kc + k];
-          }
+          k = idx & 31;
+          i = idx >> 5;
         } else {
-          for (int idx = tid; idx < 32 * M; idx += kNSThreads) {
-            const int i = idx % M, k = idx / M;
-            Ps[k * ps + i] = p.p[static_cast<int64_t>(i) * p.rs + static_cast<int64_t>(kc + k) * p.cs];
-          }
+          i = idx % M;
+          k = idx / M;
         }
+        l = k * ps + i;
+        o = i * p.rs + k * p.cs;
+        return idx < 32 * M;
+      };
+      auto qslot = [&](int e, int& l, int& o) {
+        int t2 = tid;
+        asm volatile("" : "+v"(t2));
+        const int idx = t2 + kNSThreads * e;
+        int j, k;
         if (q.cs == 1) {
-          for (int idx = tid; idx < 32 * NB; idx += kNSThreads) {
-            const int j = idx % NB, k = idx / NB;
-            Qs[k * qs + j] = q.p[static_cast<int64_t>(kc + k) * q.rs + nb + j];
-          }
+          j = idx % NB;
+          k = idx / NB;
         } else {
-          for (int idx = tid; idx < 32 * NB; idx += kNSThreads) {
-            const int k = idx & 31, j = idx >> 5;
-            Qs[k * qs + j] = q.p[static_cast<int64_t>(kc + k) * q.rs + static_cast<int64_t>(nb + j) * q.cs];
-          }
+          k = idx & 31;
+          j = idx >> 5;
         }
-        __syncthreads();
+        l = k * qs + j;
+        o = k * q.rs + (nb + j) * q.cs;
+        return idx < 32 * NB;
+      };
+      float vp[MP], vq[MQ];
+      auto load = [&](int kc) {
+        const float* bp = p.p + static_cast<int64_t>(kc) * p.cs;
+        const float* bq = q.p + static_cast<int64_t>(kc) * q.rs;
+#pragma unroll
+        for (int e = 0; e < MP; ++e) {
+          int l, o;
+          vp[e] = pslot(e, l, o) ? bp[o] : 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < MQ; ++e) {
+          int l, o;
+          vq[e] = qslot(e, l, o) ? bq[o] : 0.f;
+        }
+      };
+      auto store = [&](int b) {
+#pragma unroll
+        for (int e = 0; e < MP; ++e) {
+          int l, o;
+          if (pslot(e, l, o)) Ps[b * PSZ + l] = vp[e];
+        }
+#pragma unroll
+        for (int e = 0; e < MQ; ++e) {
+          int l, o;
+          if (qslot(e, l, o)) Qs[b * QSZ + l] = vq[e];
+        }
+      };
+      const int nc = K[t] / 32;
+      load(0);
+      __syncthreads();  // the previous readers of both buffers are done
+      store(0);
+      __syncthreads();
+      for (int c = 0; c < nc; ++c) {
+        const int b = c & 1;
+        if (c + 1 < nc) load(32 * (c + 1));
+        const float* pb = Ps + b * PSZ;
+        const float* qb = Qs + b * QSZ;
 #pragma unroll 4
         for (int ks = 0; ks < 16; ++ks) {
 #pragma unroll
@@ -513,12 +566,14 @@ __device__ __forceinline__ void wg_mm(int M, int N, const int (&K)[NTERM], const
             const int tt = wave + 8 * u;
             if (tt < tiles) {
               const int ti = tt / ntl, tj = tt % ntl;
-              const float av = Ps[(2 * ks + g) * ps + 32 * ti + ln];
-              const float bv = Qs[(2 * ks + g) * qs + 32 * tj + ln];
+              const float av = pb[(2 * ks + g) * ps + 32 * ti + ln];
+              const float bv = qb[(2 * ks + g) * qs + 32 * tj + ln];
               acc[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc[u], 0, 0, 0);
             }
           }
         }
+        if (c + 1 < nc) store(b ^ 1);
+        __syncthreads();
       }
     }
     // acc[u][r] = C[32 ti + 8 (r / 4) + 4 g + r % 4][nb + 32 tj + ln]
@@ -581,8 +636,8 @@ __device__ __forceinline__ float ns_block_sum(float v, float* red) {
 }
 
 __global__ __launch_bounds__(kNSThreads) void k_bw_ns_fwd(BwNSArgs a) {
-  __shared__ float Ps[32 * 129];
-  __shared__ float Qs[32 * (kNB + 1)];
+  __shared__ float Ps[2 * 32 * 129];
+  __shared__ float Qs[2 * 32 * (kNB + 1)];
   __shared__ float red[kNSThreads];
   const NSMat m(a);
   const int tid = threadIdx.x;
@@ -631,8 +686,8 @@ __global__ __launch_bounds__(kNSThreads) void k_bw_ns_fwd(BwNSArgs a) {
 }
 
 __global__ __launch_bounds__(kNSThreads) void k_bw_ns(BwNSArgs a) {
-  __shared__ float Ps[32 * 129];
-  __shared__ float Qs[32 * (kNB + 1)];
+  __shared__ float Ps[2 * 32 * 129];
+  __shared__ float Qs[2 * 32 * (kNB + 1)];
   __shared__ float red[kNSThreads];
   const NSMat m(a);
   const int tid = threadIdx.x;
