@@ -103,7 +103,9 @@ __global__ __launch_bounds__(kThreads) void k_window_attn(WindowArgs a) {
 
 // ---------------------------------------------------------------------------
 // bf16 matrix-core variant for d = 128.  A workgroup of four wavefronts owns
-// 128 consecutive queries of a pair, 32 per wavefront; keys and values of
+// 128 QT consecutive queries of a pair, QT tiles of 32 per wavefront (the
+// launch uses QT = 1: two tiles share each key and value read from LDS, but
+// need one wavefront per SIMD, which measured 1.5x slower); keys and values of
 // 64-token stages move from HBM straight into double-buffered LDS tiles
 // (global_load_lds, rows of 256 bytes with their 16-byte chunks XOR-swizzled
 // per row).  Per wavefront and 32-key sub-tile, on 32x32x16 MFMAs:
@@ -133,7 +135,6 @@ constexpr int NT = D / 32;   // 32-feature tiles of the output
 constexpr int ROW = 2 * D;   // bytes per token row
 constexpr int TT = 64;       // keys per stage
 constexpr int TILE = TT * ROW;
-constexpr int QW = 128;      // queries per workgroup
 
 // XOR swizzle of the sixteen 16-byte chunks of row r (r_i: bit i of r):
 // conflict-free 16-byte row reads over 16 consecutive rows and 8-byte
@@ -144,12 +145,15 @@ __device__ __forceinline__ int swz(int r) {
 }
 }  // namespace mf
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int QT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QT == 1 ? 2 : 1, QT == 1 ? 2 : 1)))
 void k_window_attn_mfma(WindowArgs a) {
   using namespace mf;
+  constexpr int QWV = 32 * QT;     // queries per wavefront
+  constexpr int QWG = 4 * QWV;     // queries per workgroup
   __shared__ __attribute__((aligned(16))) unsigned char lds[4 * TILE];  // K[2], V[2]
   const int pair = blockIdx.y;
-  const int64_t q0 = static_cast<int64_t>(blockIdx.x) * QW;
+  const int64_t q0 = static_cast<int64_t>(blockIdx.x) * QWG;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -162,30 +166,37 @@ void k_window_attn_mfma(WindowArgs a) {
   const uint16_t* Vg = static_cast<const uint16_t*>(a.V) + base;
   const int T = static_cast<int>(a.T);
   const int W = static_cast<int>(a.window < a.T ? a.window : a.T);
-  const int qw0 = static_cast<int>(q0) + 32 * wv;  // this wave's first query
-  const int myq = qw0 + ln;
+  const int qw0 = static_cast<int>(q0) + QWV * wv;  // this wave's first query
   const float c = a.scale * 1.4426950408889634f;   // scores to base-2 exponents
 
-  // this wave's queries as B operands: lane holds query qw0 + ln, features
-  // 16 ks + 8 g .. +7 (queries past the end re-read the last one)
-  bf16x8_t qb[KS];
-  {
+  // this wave's queries as B operands: query tile qt, lane holds query
+  // qw0 + 32 qt + ln, features 16 ks + 8 g .. +7 (queries past the end
+  // re-read the last one)
+  bf16x8_t qb[QT][KS];
+#pragma unroll
+  for (int qt = 0; qt < QT; ++qt) {
+    const int myq = qw0 + 32 * qt + ln;
     const int qr = myq < T ? myq : T - 1;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qb[ks] = *reinterpret_cast<const bf16x8_t*>(Qg + static_cast<int64_t>(qr) * D + 16 * ks + 8 * g);
+      qb[qt][ks] = *reinterpret_cast<const bf16x8_t*>(Qg + static_cast<int64_t>(qr) * D + 16 * ks + 8 * g);
   }
 
-  f32x16_t o[NT];
+  f32x16_t o[QT][NT];
+  float m[QT], l[QT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
+  for (int qt = 0; qt < QT; ++qt) {
+    m[qt] = -INFINITY;
+    l[qt] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[qt][t][r] = 0.f;
+    }
   }
-  float m = -INFINITY, l = 0.f;
 
   // stage range: keys any query of the workgroup can see
-  const int q_hi = static_cast<int>(q0) + QW - 1 < T - 1 ? static_cast<int>(q0) + QW - 1 : T - 1;
+  const int q_hi = static_cast<int>(q0) + QWG - 1 < T - 1 ? static_cast<int>(q0) + QWG - 1 : T - 1;
   int k_begin = static_cast<int>(q0) - W + 1;
   if (k_begin < 0) k_begin = 0;
   k_begin = (k_begin / TT) * TT;
@@ -237,15 +248,22 @@ void k_window_attn_mfma(WindowArgs a) {
     for (int st = 0; st < TT / 32; ++st) {
       const int kb0 = k0 + 32 * st;  // first key of the sub-tile
       // skipped when outside every window of this wave's queries
-      if (kb0 > qw0 + 31 || kb0 + 31 < qw0 - W + 1 || kb0 >= T) continue;
-      f32x16_t s;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+      if (kb0 > qw0 + QWV - 1 || kb0 + 31 < qw0 - W + 1 || kb0 >= T) continue;
+      // key rows of the sub-tile, shared by the wave's query tiles
       bf16x8_t ak[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) ak[ks] = *reinterpret_cast<const bf16x8_t*>(kb + ak_off[ks] + 8192 * st);
+      f32x16_t s[QT];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], qb[ks], s, 0, 0, 0);
+      for (int qt = 0; qt < QT; ++qt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[qt][r] = 0.f;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) s[qt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[ks], qb[qt][ks], s[qt], 0, 0, 0);
+      }
       // value operands of this sub-tile (read while the scores complete)
       bf16x8_t vt[2][NT];
 #pragma unroll
@@ -261,64 +279,73 @@ void k_window_attn_mfma(WindowArgs a) {
           vt[hs][nt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t2[0], t2[1], 0, 1, 2, 3, 4, 5, 6, 7));
         }
       }
-      // register r holds key kb0 + 8 (r / 4) + 4 g + r % 4 of query myq
-      const bool edge = (kb0 + 31 > qw0) || (kb0 < qw0 + 31 - W + 1);
-      if (edge) {
+#pragma unroll
+      for (int qt = 0; qt < QT; ++qt) {
+        // register r holds key kb0 + 8 (r / 4) + 4 g + r % 4 of query myq
+        const int qq = qw0 + 32 * qt, myq = qq + ln;
+        const bool edge = (kb0 + 31 > qq) || (kb0 < qq + 31 - W + 1);
+        if (edge) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
+            if (!(key <= myq && key > myq - W)) s[qt][r] = -INFINITY;
+          }
+        }
+        float mx = s[qt][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[qt][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = fmaxf(m[qt], mx * c);  // running maximum, base-2 units (-inf: nothing seen yet)
+        if (__any(mn != m[qt])) {
+          const float corr = (mn == m[qt]) ? 1.f : exp2f(m[qt] - mn);  // 0 on the first visible sub-tile
+          l[qt] *= corr;
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[qt][t][r] *= corr;
+          }
+          m[qt] = mn;
+        }
+        bf16x8_t p[2];
+        const float mm = (m[qt] == -INFINITY) ? 0.f : m[qt];  // (then every score of the lane is -inf: p = 0)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kb0 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (!(key <= myq && key > myq - W)) s[r] = -INFINITY;
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[qt][r], c, -mm));
+          l[qt] += e;
+          p[r >> 3][r & 7] = static_cast<__bf16>(e);
         }
-      }
-      float mx = s[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m, mx * c);  // running maximum, base-2 units (-inf: nothing seen yet)
-      if (__any(mn != m)) {
-        const float corr = (mn == m) ? 1.f : exp2f(m - mn);  // 0 on the first visible sub-tile
-        l *= corr;
+        for (int hs = 0; hs < 2; ++hs) {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[t][r] *= corr;
+          for (int nt = 0; nt < NT; ++nt)
+            o[qt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[hs][nt], p[hs], o[qt][nt], 0, 0, 0);
         }
-        m = mn;
-      }
-      bf16x8_t p[2];
-      const float mm = (m == -INFINITY) ? 0.f : m;  // (then every score of the lane is -inf: p = 0)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[r], c, -mm));
-        l += e;
-        p[r >> 3][r & 7] = static_cast<__bf16>(e);
-      }
-#pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vt[hs][nt], p[hs], o[nt], 0, 0, 0);
       }
     }
   }
-  l += __shfl_xor(l, 32, 64);
-  if (myq >= T) return;
-  const float inv = 1.f / l;
-  uint16_t* Og = static_cast<uint16_t*>(a.O) + base + static_cast<int64_t>(myq) * D;
-  // register r of tile nt: feature 32 nt + 8 (r / 4) + 4 g + r % 4 (four consecutive per group)
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
+  for (int qt = 0; qt < QT; ++qt) {
+    const float lt = l[qt] + __shfl_xor(l[qt], 32, 64);
+    const int myq = qw0 + 32 * qt + ln;
+    if (myq >= T) continue;
+    const float inv = 1.f / lt;
+    uint16_t* Og = static_cast<uint16_t*>(a.O) + base + static_cast<int64_t>(myq) * D;
+    // register r of tile nt: feature 32 nt + 8 (r / 4) + 4 g + r % 4 (four consecutive per group)
 #pragma unroll
-    for (int rg = 0; rg < 4; ++rg) {
-      const int f = 32 * nt + 8 * rg + 4 * g;
-      bf16x4_t v4;
-      if (a.accumulate) v4 = *reinterpret_cast<const bf16x4_t*>(Og + f);
+    for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float v = o[nt][4 * rg + i] * inv;
-        if (a.accumulate) v += static_cast<float>(v4[i]);
-        v4[i] = static_cast<__bf16>(v);
+      for (int rg = 0; rg < 4; ++rg) {
+        const int f = 32 * nt + 8 * rg + 4 * g;
+        bf16x4_t v4;
+        if (a.accumulate) v4 = *reinterpret_cast<const bf16x4_t*>(Og + f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = o[qt][nt][4 * rg + i] * inv;
+          if (a.accumulate) v += static_cast<float>(v4[i]);
+          v4[i] = static_cast<__bf16>(v);
+        }
+        *reinterpret_cast<bf16x4_t*>(Og + f) = v4;
       }
-      *reinterpret_cast<bf16x4_t*>(Og + f) = v4;
     }
   }
 }
@@ -342,8 +369,9 @@ hipError_t launch_window_attn(const WindowArgs& a, hipStream_t s) {
   const bool aligned = ((reinterpret_cast<uintptr_t>(a.Q) | reinterpret_cast<uintptr_t>(a.K) |
                          reinterpret_cast<uintptr_t>(a.V) | reinterpret_cast<uintptr_t>(a.O)) & 15) == 0;
   if (a.bf16 && a.d == mf::D && aligned && a.T * a.d < (int64_t(1) << 31)) {
-    const dim3 grid(static_cast<unsigned>((a.T + mf::QW - 1) / mf::QW), a.P);
-    hipLaunchKernelGGL(k_window_attn_mfma, grid, dim3(kThreads), 0, s, a);
+    constexpr int QT = 1;  // query tiles per wavefront
+    const dim3 grid(static_cast<unsigned>((a.T + 128 * QT - 1) / (128 * QT)), a.P);
+    hipLaunchKernelGGL(k_window_attn_mfma<QT>, grid, dim3(kThreads), 0, s, a);
     return hipGetLastError();
   }
   switch (a.d) {
