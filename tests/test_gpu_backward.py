@@ -84,6 +84,12 @@ CASES += [
     S.WORKLOADS["posed"].replace(name="bw-posed-bf16-a", H=3, T_kv=2 * 2048, chunk_kv=2048,
                                  T_q=2 * 256, chunk_q=256, order="apply_then_update", opt="momentum",
                                  beta=0.9),
+    # hidden sizes that are multiples of 32 but not of 128: matrix-core token
+    # kernels with the fp32 contraction kernel
+    S.WORKLOADS["lm"].replace(name="bw-d128-h96-bf16", B=1, H=2, h=96, T_kv=2 * 512, chunk_kv=512,
+                              T_q=2 * 128, chunk_q=128, opt="muon", products="auto"),
+    S.WORKLOADS["posed"].replace(name="bw-d64-h64-bf16", H=2, h=64, T_kv=2 * 600, chunk_kv=600,
+                                 T_q=2 * 100, chunk_q=100, opt="gd", products="bf16"),
 ]
 
 
