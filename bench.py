@@ -111,7 +111,7 @@ def cpu_baseline(w: S.Workload, x, st, budget_s: float = 15.0):
 def other_mode(args, w, cfg, dev, Q, K, V, eta, O, ws):
     """--mode backward / block: the step is lact_chunked_backward (given dO and the
     cotangents of the final weights) or lact_block_forward (shared Q, K, V); one
-    JSON line with tokens/s (no flop count is claimed for these)."""
+    JSON line with tokens/s and the dominant kernel's roofline."""
     import torch
     import chunk_test_amd as L
     if args.mode == "backward":
@@ -134,7 +134,7 @@ def other_mode(args, w, cfg, dev, Q, K, V, eta, O, ws):
         def step():
             for n, t in dev.items():
                 t.copy_(init[n])
-            L.lact_block_forward(cfg, dev, K, K, V, eta, O, w.chunk_kv, args.window, ws, order=w.order)
+            L.lact_block_forward(cfg, dev, Q, K, V, eta, O, w.chunk_kv, args.window, ws, order=w.order)
         metric = "LaCT block (window attention + layer) tokens/s"
     for _ in range(args.warmup):
         step()
@@ -147,7 +147,7 @@ def other_mode(args, w, cfg, dev, Q, K, V, eta, O, ws):
         a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a0.record()
         for _ in range(args.steps):
-            L.lact_window_attention(cfg, K, K, V, O, args.window)
+            L.lact_window_attention(cfg, Q, K, V, O, args.window)
         a1.record()
         torch.cuda.synchronize()
         a_ms = a0.elapsed_time(a1) / args.steps
@@ -162,6 +162,36 @@ def other_mode(args, w, cfg, dev, Q, K, V, eta, O, ws):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
+    # the dominant kernel's roofline from the library's per-phase HIP events,
+    # over as many steps again: the key-side backward token kernel (24 d h
+    # flop per key token and pair: six projections, six token-side products),
+    # or the window attention (4 d flop per visible (query, key))
+    L.profile_enable(True)
+    L.profile_read()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    phases = L.profile_read()
+    L.profile_enable(False)
+    roof = None
+    if args.mode == "backward":
+        k_ms, k_n = phases["bw_key_tokens"]
+        if k_n:
+            per_launch = 24.0 * w.d * w.h * w.chunk_kv * w.pairs
+            avg = k_ms / k_n
+            ach = per_launch / (avg * 1e-3) / 1e12
+            roof = {"kernel": "backward key-side token kernel (VJP of the chunk gradient)", "bound": "mfma",
+                    "achieved": round(ach, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None, "avg_launch_ms": round(avg, 5),
+                    "flop_per_launch": per_launch}
+    elif attn is not None:
+        a_ms, a_n = phases["window_attention"]
+        if a_n:
+            avg = a_ms / a_n
+            ach = attn["flop"] / (avg * 1e-3) / 1e12
+            roof = {"kernel": "window attention", "bound": "mfma", "achieved": round(ach, 3),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                    "traffic": None, "avg_launch_ms": round(avg, 5), "flop_per_launch": attn["flop"]}
     line = {
         "metric": metric, "value": round(w.B * w.T_kv / (ms * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -171,8 +201,9 @@ def other_mode(args, w, cfg, dev, Q, K, V, eta, O, ws):
                    "T_kv": w.T_kv, "T_q": w.T_q, "chunk_kv": w.chunk_kv, "chunk_q": w.chunk_q,
                    "order": w.order, "opt": w.opt, "beta": w.beta, "products": w.products,
                    "window": args.window if args.mode == "block" else None},
-        "wall_s_timed": round(wall, 4), "roofline": None, "cpu_baseline": None,
+        "wall_s_timed": round(wall, 4), "roofline": roof, "cpu_baseline": None,
         "window_attention": attn,
+        "phase_ms_per_step": {k: round(v[0] / args.steps, 5) for k, v in phases.items() if v[1]},
     }
     print(json.dumps(line), flush=True)
 

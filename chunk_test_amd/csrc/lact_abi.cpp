@@ -815,7 +815,10 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
       a.op = o.op;
       a.op_stride = o.op_stride;
     }
-    err = lact::launch_bw_tok(a, apply, s);
+    {
+      PhaseTimer t(apply ? 6 : 5, s);
+      err = lact::launch_bw_tok(a, apply, s);
+    }
     if (err != hipSuccess) return hip_fail(err, "backward token kernel");
     const Splits sp = plan_splits(backward_rule(p), n);
     lact::BwContractArgs b{};
@@ -836,6 +839,7 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
     b.S = sp.S;
     b.tps = sp.tps;
     b.bf16 = p.bf16;
+    PhaseTimer tc(7, s);
     if ((err = lact::launch_bw_contract(b, s)) != hipSuccess) return hip_fail(err, "backward contraction kernel");
     if ((err = lact::launch_bw_reduce_add(cot, part, sp.S, 3 * hd, p.P, s)) != hipSuccess)
       return hip_fail(err, "backward reduction kernel");
@@ -891,6 +895,7 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
       nf.b = c->ns_b;
       nf.c = c->ns_c;
       nf.eps = c->ns_eps;
+      PhaseTimer tn(8, s);
       if ((e = lact::launch_bw_ns_fwd(nf, s)) != hipSuccess) return hip_fail(e, "Newton-Schulz kernel");
       direction = dirb;
     }
@@ -924,6 +929,7 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
       na.b = c->ns_b;
       na.c = c->ns_c;
       na.eps = c->ns_eps;
+      PhaseTimer tn(8, s);
       if ((e = lact::launch_bw_ns(na, s)) != hipSuccess) return hip_fail(e, "Newton-Schulz VJP kernel");
       t_in = tb;
     }
@@ -1155,7 +1161,11 @@ int lact_window_attention(const lact_config* cfg, const void* Q, const void* K, 
   a.P = cfg->B * cfg->H;
   a.d = cfg->d;
   a.bf16 = cfg->io_dtype == LACT_BF16;
-  hipError_t e = lact::launch_window_attn(a, static_cast<hipStream_t>(stream));
+  hipError_t e;
+  {
+    PhaseTimer t(9, static_cast<hipStream_t>(stream));
+    e = lact::launch_window_attn(a, static_cast<hipStream_t>(stream));
+  }
   if (e != hipSuccess) return hip_fail(e, "window-attention kernel");
   return LACT_OK;
 }
@@ -1259,6 +1269,6 @@ int lact_profile_read(double* ms, int64_t* launches) {
   return rc;
 }
 
-int lact_version(void) { return 2; }
+int lact_version(void) { return 3; }
 
 }  // extern "C"

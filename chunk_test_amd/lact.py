@@ -23,7 +23,8 @@ LACT_ERR_HIP = -4
 LACT_F32, LACT_BF16 = 0, 1
 LACT_APPLY_THEN_UPDATE, LACT_UPDATE_THEN_APPLY = 0, 1
 LACT_OPT_GD, LACT_OPT_MOMENTUM, LACT_OPT_MUON = 0, 1, 2
-PROFILE_PHASES = ("gradient", "tail", "newton_schulz", "step_norm", "apply")
+PROFILE_PHASES = ("gradient", "tail", "newton_schulz", "step_norm", "apply", "bw_key_tokens", "bw_query_tokens",
+                  "bw_contract", "bw_newton_schulz", "window_attention")
 
 ORDER_CODES = {"apply_then_update": LACT_APPLY_THEN_UPDATE, "update_then_apply": LACT_UPDATE_THEN_APPLY}
 OPT_CODES = {"gd": LACT_OPT_GD, "momentum": LACT_OPT_MOMENTUM, "muon": LACT_OPT_MUON}

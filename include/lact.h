@@ -305,8 +305,12 @@ int lact_mfma_path(int32_t d, int32_t h, int32_t io_dtype);
  * step and row normalisation, and for bf16-mode Muon with Newton-Schulz
  * too: one or two kernels); 2 Newton-Schulz and 3 step + row normalisation
  * when they run as kernels of their own (fp32-arithmetic Muon); 4 query
- * read. */
-#define LACT_PROFILE_PHASES 5
+ * read; in lact_chunked_backward (whose forward rerun also records phases
+ * 0-4): 5 the key-side token kernel (VJP of the chunk gradient), 6 the
+ * query-side token kernel (VJP of the query read), 7 the weight-cotangent
+ * contractions with their fixed-order sum, 8 Newton-Schulz forward and VJP;
+ * 9 window attention (lact_window_attention, lact_block_forward). */
+#define LACT_PROFILE_PHASES 10
 int lact_profile_enable(int on);
 int lact_profile_read(double* ms, int64_t* launches);
 
