@@ -264,15 +264,15 @@ def main():
     def step():
         L.lact_chunked_forward(cfg, dev, Q, K, V, eta, O, w.chunk_kv, w.chunk_q, w.order, ws)
 
-    if args.mode != "forward":
-        return other_mode(args, w, cfg, dev, Q, K, V, eta, O, ws)
-
     if args.copy_probe_mib:
         src = torch.empty(args.copy_probe_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.mode != "forward":
+        return other_mode(args, w, cfg, dev, Q, K, V, eta, O, ws)
 
     # every step starts from the initial state: W (and M) are restored before
     # each step, outside its timed span (the kernels' time depends on the data)

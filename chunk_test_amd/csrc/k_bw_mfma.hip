@@ -331,8 +331,15 @@ void k_bw_apply_mfma(BwTokArgs a) {
   constexpr int WHALF = JT * ROW;     // one matrix part (hi or lo) of a weight tile
   constexpr int WTILE3 = 6 * WHALF;   // W1, W3, W2^T, hi and lo
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * WTILE3];
-  const int pair = blockIdx.y;
-  const int64_t tb = static_cast<int64_t>(blockIdx.x) * QWG;
+  // XCD-aware order: block ids congruent mod 8 run on one XCD, and the
+  // token tiles of a pair take consecutive slots of one XCD's share, so the
+  // pair's weight tiles come from HBM once and then from that XCD's L2
+  const int nblk = gridDim.x;  // a multiple of 8
+  const int ntiles = static_cast<int>((a.n + QWG - 1) / QWG);
+  const int o = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  if (o >= ntiles * a.P) return;
+  const int pair = o / ntiles;
+  const int64_t tb = static_cast<int64_t>(o % ntiles) * QWG;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -519,8 +526,15 @@ void k_bw_grad_mfma(BwTokArgs a) {
   constexpr int WHALF = JT * ROW;     // one matrix part (hi or lo) of a weight tile
   constexpr int WTILE6 = 12 * WHALF;  // W1, W3, W2^T, P1, P3, P2^T, hi and lo
   __shared__ __attribute__((aligned(16))) unsigned char lds[WTILE6];
-  const int pair = blockIdx.y;
-  const int64_t tb = static_cast<int64_t>(blockIdx.x) * QWG;
+  // XCD-aware order: block ids congruent mod 8 run on one XCD, and the
+  // token tiles of a pair take consecutive slots of one XCD's share, so the
+  // pair's weight tiles come from HBM once and then from that XCD's L2
+  const int nblk = gridDim.x;  // a multiple of 8
+  const int ntiles = static_cast<int>((a.n + QWG - 1) / QWG);
+  const int o = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  if (o >= ntiles * a.P) return;
+  const int pair = o / ntiles;
+  const int64_t tb = static_cast<int64_t>(o % ntiles) * QWG;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -748,7 +762,8 @@ hipError_t launch_bw_ops(const BwOpsArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_bw_tok_mfma(const BwTokArgs& a, bool apply, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((a.n + QWG - 1) / QWG), a.P);
+  const int64_t total = (a.n + QWG - 1) / QWG * a.P;
+  const dim3 grid(static_cast<unsigned>((total + 7) / 8 * 8));
   if (a.d == 128) {
     if (apply) hipLaunchKernelGGL(k_bw_apply_mfma<128>, grid, dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL(k_bw_grad_mfma<128>, grid, dim3(kThreads), 0, s, a);
