@@ -1,5 +1,5 @@
-// Backward pass of the LaCT layer on bf16 MFMA (gfx950): the weight
-// cotangents as token contractions,
+// Backward pass of the LaCT layer on bf16 MFMA (gfx950), d = 64 or 128: the
+// weight cotangents as token contractions,
 //   dW1 += X1^T A,   dW3 += X3^T A,   dW2 += (b B)^T X2      (b = -eta or 1),
 // where A, B are the chunk's keys and values (or queries and output
 // cotangents) and X1, X2, X3 the per-(token, hidden unit) factors the token
@@ -14,7 +14,7 @@
 // accumulation (~16 significant bits per factor, products of A and B exact).
 // One workgroup per (pair, token split, 128-unit hidden slice); wave w owns
 // hidden units 32 w .. 32 w + 31 of the slice and every 32-wide feature tile,
-// twelve 32 x 32 accumulator tiles per wave at d = 128.  Each stage of 32
+// twelve 32 x 32 accumulator tiles per wave at d = 128 (six at d = 64).  Each stage of 32
 // tokens (A, B, the rates and the three factor rows of the slice) moves from
 // HBM into double-buffered LDS with global_load_lds one stage ahead; A and B
 // enter the products through LDS transpose reads (tokens as the k index).
