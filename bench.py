@@ -108,6 +108,30 @@ def cpu_baseline(w: S.Workload, x, st, budget_s: float = 15.0):
     }
 
 
+def gemm_reference(n: int = 8192, reps: int = 30):
+    """The vendor BLAS (torch.matmul, bf16 in, fp32 accumulate) on one square
+    n x n x n product, timed back to back under the same sustained load as the
+    steps: a practical matrix-core rate of this GPU, reported beside the
+    published peak (context for the roofline, not part of the layer)."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16, generator=g)
+    c = torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    e1.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    return {"what": f"torch.matmul bf16 {n}x{n}x{n}, {reps} back-to-back launches",
+            "ms": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
 def other_mode(args, w, cfg, dev, Q, K, V, eta, O, ws):
     """--mode backward / block: the step is lact_chunked_backward (given dO and the
     cotangents of the final weights) or lact_block_forward (shared Q, K, V); one
@@ -224,6 +248,9 @@ def main():
     ap.add_argument("--window", type=int, default=2048, help="attention window of --mode block")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip the vendor-BLAS bf16 GEMM timed after the steps (a practical "
+                         "matrix-core rate of this GPU under sustained load, for context)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (a reference for "
                          "hardware byte counters)")
@@ -359,6 +386,10 @@ def main():
         "roofline": roof,
         "cpu_baseline": None,
     }
+    if not args.no_gemm_reference:
+        line["gemm_reference"] = gemm_reference()
+        if grad_tflops and line["gemm_reference"]["tflops"]:
+            roof["frac_of_gemm_reference"] = round(grad_tflops / line["gemm_reference"]["tflops"], 4)
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline (budget {args.cpu_budget} s)")
         line["cpu_baseline"] = cpu_baseline(w, x, st, args.cpu_budget)
