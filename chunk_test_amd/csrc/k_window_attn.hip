@@ -111,9 +111,10 @@ __global__ __launch_bounds__(kThreads) void k_window_attn(WindowArgs a) {
 // per row).  Per wavefront and 32-key sub-tile, on 32x32x16 MFMAs:
 //   S^T = K Q^T   (A = key rows from LDS, B = the wave's queries, held in
 //                  registers): lane = query, 16 registers = 16 keys;
-//   online softmax in that layout: the running maximum of a query is shared
-//   with the lane holding its other 16 keys (lane ^ 32); p = 2^(s c - m),
-//   c = scale log2(e); the output is rescaled only when some maximum grew;
+//   online softmax in that layout: the maximum of a query is shared with the
+//   lane holding its other 16 keys (lane ^ 32); p = 2^(s c - m), c = scale
+//   log2(e), where the reference m moves only when a sub-tile's maximum
+//   exceeds it by more than 8 (so p <= 2^8), and the output is rarely rescaled;
 //   O^T += V^T P^T  (A = value columns from LDS transpose reads, B = p as
 //                  bf16 in the same key order): lane = query, registers =
 //                  features, so the rescale is per lane.
@@ -135,6 +136,7 @@ constexpr int NT = D / 32;   // 32-feature tiles of the output
 constexpr int ROW = 2 * D;   // bytes per token row
 constexpr int TT = 64;       // keys per stage
 constexpr int TILE = TT * ROW;
+constexpr float kLazy = 8.f;  // largest exponent of an unnormalised probability (base 2)
 
 // XOR swizzle of the sixteen 16-byte chunks of row r (r_i: bit i of r):
 // conflict-free 16-byte row reads over 16 consecutive rows and 8-byte
@@ -295,16 +297,21 @@ void k_window_attn_mfma(WindowArgs a) {
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[qt][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float mn = fmaxf(m[qt], mx * c);  // running maximum, base-2 units (-inf: nothing seen yet)
-        if (__any(mn != m[qt])) {
-          const float corr = (mn == m[qt]) ? 1.f : exp2f(m[qt] - mn);  // 0 on the first visible sub-tile
+        // The reference maximum m (base-2 units, -inf: nothing seen yet)
+        // moves only when the sub-tile's maximum exceeds it by more than
+        // kLazy, so every p = 2^(s c - m) stays below 2^kLazy and the rescale
+        // of l and O (which both carry the same factor 2^-m) is rare.
+        const float mxc = mx * c;
+        const bool grow = mxc > m[qt] + kLazy;
+        if (__any(grow)) {
+          const float corr = grow ? exp2f(m[qt] - mxc) : 1.f;  // 0 on the first visible sub-tile
           l[qt] *= corr;
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) o[qt][t][r] *= corr;
           }
-          m[qt] = mn;
+          if (grow) m[qt] = mxc;
         }
         bf16x8_t p[2];
         const float mm = (m[qt] == -INFINITY) ? 0.f : m[qt];  // (then every score of the lane is -inf: p = 0)

@@ -32,6 +32,9 @@ def attention_case(B, H, T, d, io, seed):
     (1, 2, 777, 128, "bf16", 33, 0.5),
     (2, 1, 300, 128, "bf16", 100000, 0.0),
     (1, 1, 4100, 128, "bf16", 4096, 0.0),
+    # scores of tens of units (scale 40 on unit rows): a query's running maximum
+    # moves by more than the kernel's lazy-rescale margin many times
+    (1, 2, 2000, 128, "bf16", 512, 40.0),
 ])
 def test_window_attention_parity(B, H, T, d, io, window, scale):
     import torch
@@ -56,6 +59,34 @@ def test_window_attention_parity(B, H, T, d, io, window, scale):
     L.lact_window_attention(cfg, Q, K, V, O2, window, scale, accumulate=True)
     torch.cuda.synchronize()
     assert G.rel_err(O2.float().cpu().numpy() - 1.0, got) <= 2 * G.tol_of(w)
+
+
+@pytest.mark.parametrize("window", [700, 4096])
+def test_window_attention_rising_scores(window):
+    """Keys whose length grows along the sequence (0.2 to 6 times unit length,
+    scale 4): every query's maximum keeps rising across its window, so the
+    softmax reference moves (and the output is rescaled) again and again,
+    with probabilities both near the lazy margin and far below it."""
+    import torch
+    import chunk_test_amd as L
+    import oracle
+    B, H, T, d = 1, 2, 3000, 128
+    w, x = attention_case(B, H, T, d, "bf16", seed=11 + window)
+    # (scaled in float32, then rounded to the bf16 the kernel reads; the
+    # oracle sees the same rounded values)
+    ramp = np.linspace(0.2, 6.0, T, dtype=np.float32)[None, None, :, None]
+    x["K"] = S.round_bf16(x["K"].astype(np.float32) * ramp)
+    cfg = G.config_of(w)
+    Q, K, V = (G.to_dev(x[n], w) for n in ("Q", "K", "V"))
+    O = torch.empty_like(Q)
+    L.lact_window_attention(cfg, Q, K, V, O, window, 4.0)
+    torch.cuda.synchronize()
+    got = O.float().cpu().numpy()
+    for h in range(H):
+        ref = oracle.window_attention(x["Q"][0, h].astype(np.float64), x["K"][0, h].astype(np.float64),
+                                      x["V"][0, h].astype(np.float64), window, 4.0)
+        err = G.rel_err(got[0, h], ref)
+        assert err <= G.tol_of(w), (h, err)
 
 
 @pytest.mark.parametrize("w,window", [
