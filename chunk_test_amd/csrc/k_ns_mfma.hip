@@ -29,6 +29,7 @@
 // tiles, which for a symmetric matrix is the matrix itself).
 #include "lact_device.h"
 #include "lact_internal.h"
+#include "apply_body.h"
 
 namespace lact {
 namespace {
@@ -741,7 +742,67 @@ __global__ __launch_bounds__(2 * L) void k_muon_tail(TailArgs a) {
   }
 }
 
+// One launch for two independent jobs of the chunk scan (apply-then-update,
+// chunk c >= 1): blocks [0, nt) run the Muon update tail of chunk c (one
+// matrix each; nt is 3P rounded up to a multiple of 8, the blocks past 3P
+// idle), blocks [nt, nt + na) the query read of chunk c, which reads the
+// bf16 copy of W_c that the previous tail wrote while this tail writes W_c+1
+// and the other copy.  The tail fills only 3P CUs; the query read takes the
+// rest of the chip in the same launch (one workgroup per CU for both parts),
+// where two launches would run one after the other.
+template <int S, int L>
+__global__ __launch_bounds__(2 * L) void k_muon_tail_apply(TailArgs ta, ApplyArgs aa, int nt, int na, int per_wg,
+                                                          int wg_per_pair) {
+  using G = NSGeo<S, L>;
+  using AG = apply_detail::AGeo<S, L>;
+  static_assert(AG::THREADS == 2 * L, "one block size for both parts");
+  // (the tail's partial sums sit after its region, inside the one array)
+  constexpr int kRed = (G::REGION + 15) / 16 * 16;
+  constexpr int kTail = kRed + 4 * G::NW;
+  constexpr int kLds = kTail > AG::LDS ? kTail : AG::LDS;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
+  float* red = reinterpret_cast<float*>(lds + kRed);
+  if (static_cast<int>(blockIdx.x) >= nt) {
+    apply_detail::apply_body<S, L, true>(aa, lds, static_cast<int>(blockIdx.x) - nt, na, per_wg, wg_per_pair);
+    return;
+  }
+  const int mat = blockIdx.x;
+  if (mat >= 3 * ta.P) return;
+  const int pair = mat / 3, which = mat % 3;
+  const int cols = (which == 1) ? ta.h : ta.d;
+  if (((which == 1) ? ta.d : ta.h) > cols) {
+    muon_tail_body<S, L, true>(ta, lds, red, pair, which);
+  } else {
+    muon_tail_body<S, L, false>(ta, lds, red, pair, which);
+  }
+}
+
+template <int S, int L>
+hipError_t launch_fused(const TailArgs& ta, const ApplyArgs& aa, hipStream_t st) {
+  const int nt = (3 * ta.P + 7) / 8 * 8;
+  const int slots = (256 - nt) / 8 * 8;
+  int per = 0, gx = 0;
+  apply_detail::apply_plan<S, L>(aa.m, aa.P, slots, &per, &gx);
+  const int na = (gx * aa.P + 7) / 8 * 8;
+  hipLaunchKernelGGL((k_muon_tail_apply<S, L>), dim3(nt + na), dim3(2 * L), 0, st, ta, aa, nt, na, per, gx);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool muon_tail_apply_ok(int d, int h, int P) {
+  return h > d && ns_mfma_shape_ok(d, h) && apply_mfma_shape_ok(d, h) && 3 * P <= 192;
+}
+
+hipError_t launch_muon_tail_apply(const TailArgs& ta, const ApplyArgs& aa, hipStream_t st) {
+  if (!muon_tail_apply_ok(ta.d, ta.h, ta.P) || aa.d != ta.d || aa.h != ta.h || aa.P != ta.P ||
+      aa.Wb1 == nullptr || aa.Wb2 == nullptr || aa.Wb3 == nullptr)
+    return hipErrorInvalidValue;
+  if (ta.d == 64 && ta.h == 128) return launch_fused<64, 128>(ta, aa, st);
+  if (ta.d == 128 && ta.h == 256) return launch_fused<128, 256>(ta, aa, st);
+  if (ta.d == 64 && ta.h == 256) return launch_fused<64, 256>(ta, aa, st);
+  return hipErrorInvalidValue;
+}
 
 bool ns_mfma_shape_ok(int d, int h) {
   const int s = d < h ? d : h, l = d < h ? h : d;

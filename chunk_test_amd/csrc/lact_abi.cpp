@@ -285,8 +285,9 @@ int check_state(const Plan& p, const lact_state* st, bool need_m) {
 
 // Workspace sections (bytes), each 256-byte aligned.
 struct WsLayout {
-  size_t partials = 0, dir = 0, ns = 0, wb = 0, total = 0;
+  size_t partials = 0, dir = 0, ns = 0, wb = 0, wb2 = 0, total = 0;
   bool has_wb = false;  // section for bf16 copies of W1, W2, W3 (P 3 h d values)
+  bool has_wb2 = false;  // a second such section (Muon: the copy of chunk c is read while the next is written)
 };
 
 WsLayout ws_layout(const Plan& p, int64_t max_chunk_kv) {
@@ -332,6 +333,12 @@ WsLayout ws_layout(const Plan& p, int64_t max_chunk_kv) {
   w.wb = off;
   w.has_wb = p.bf16 && lact::apply_mfma_shape_ok(p.d, p.h);
   if (w.has_wb) off += align_up(sizeof(uint16_t) * per * p.P);
+  // with Muon the update tail of chunk c and the query read of chunk c can
+  // share a launch (the read takes the CUs the tail leaves): the read's
+  // copy and the tail's new one alternate between two sections
+  w.wb2 = off;
+  w.has_wb2 = w.has_wb && p.muon && lact::muon_tail_apply_ok(p.d, p.h, p.P);
+  if (w.has_wb2) off += align_up(sizeof(uint16_t) * per * p.P);
   w.total = off;
   return w;
 }
@@ -443,10 +450,22 @@ int run_update_linear(const lact_config* c, const Plan& p, const lact_state* st,
   return LACT_OK;
 }
 
+// Whether a Muon update runs the bf16-mode matrix-core tail (which also
+// writes the bf16 weight copy): bf16 mode, a supported shape, and W and M
+// 16-byte aligned (the tail moves them in 16-byte pieces).
+bool muon_mfma_tail(const Plan& p, const lact_state* st) {
+  const bool state_aligned =
+      ((reinterpret_cast<uintptr_t>(st->W1) | reinterpret_cast<uintptr_t>(st->W2) |
+        reinterpret_cast<uintptr_t>(st->W3) | reinterpret_cast<uintptr_t>(st->M1) |
+        reinterpret_cast<uintptr_t>(st->M2) | reinterpret_cast<uintptr_t>(st->M3)) & 15) == 0;
+  return p.muon && !p.linear && p.bf16 && lact::ns_mfma_shape_ok(p.d, p.h) && state_aligned;
+}
+
 int run_update(const lact_config* c, const Plan& p, const lact_state* st, const void* K,
                const void* V, const float* eta, int64_t n, int64_t kv_stride,
                int64_t eta_stride, char* ws, const WsLayout& L, hipStream_t s,
-               uint16_t* wb = nullptr, bool* wb_written = nullptr) {
+               uint16_t* wb = nullptr, bool* wb_written = nullptr,
+               const lact::ApplyArgs* fused_read = nullptr) {
   if (wb_written != nullptr) *wb_written = false;
   if (p.linear) return run_update_linear(c, p, st, K, V, eta, n, kv_stride, eta_stride, ws, L, s);
   float* partials = reinterpret_cast<float*>(ws + L.partials);
@@ -494,12 +513,7 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
     if (e != hipSuccess) return hip_fail(e, "update-tail kernel");
     return LACT_OK;
   }
-  // (the MFMA tail moves W and M in 16-byte pieces)
-  const bool state_aligned =
-      ((reinterpret_cast<uintptr_t>(st->W1) | reinterpret_cast<uintptr_t>(st->W2) |
-        reinterpret_cast<uintptr_t>(st->W3) | reinterpret_cast<uintptr_t>(st->M1) |
-        reinterpret_cast<uintptr_t>(st->M2) | reinterpret_cast<uintptr_t>(st->M3)) & 15) == 0;
-  if (p.bf16 && lact::ns_mfma_shape_ok(p.d, p.h) && state_aligned) {
+  if (muon_mfma_tail(p, st)) {
     // bf16 mode Muon: one kernel per matrix for reduction, momentum,
     // split-bf16 MFMA Newton-Schulz, step and unit rows.  With many splits
     // the partial sum goes first to a kernel that spreads it over every CU
@@ -526,10 +540,16 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
       ta.M1 = ta.M2 = ta.M3 = nullptr;
     }
     with_wb();
+    if (fused_read != nullptr) {
+      e = lact::launch_muon_tail_apply(ta, *fused_read, s);
+      if (e != hipSuccess) return hip_fail(e, "Muon update-tail + query-read kernel");
+      return LACT_OK;
+    }
     e = lact::launch_muon_tail(ta, s);
     if (e != hipSuccess) return hip_fail(e, "Muon update-tail kernel");
     return LACT_OK;
   }
+  if (fused_read != nullptr) return fail(LACT_ERR_HIP, "internal: fused query read without the bf16 Muon tail");
   // fp32 arithmetic Muon: reduction (+momentum), Newton-Schulz, step + unit rows
   {
     PhaseTimer t(1, s);
@@ -586,6 +606,36 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
 
 // Query read; wb (or NULL): bf16 copies of the current W1, W2, W3 as the
 // update tail stores them.
+// Arguments of the SwiGLU query read; *mfma: the matrix-core kernel applies
+// (bf16, a supported shape, 16-byte aligned Q and O rows); only then is the
+// bf16 copy wb (or NULL) used.
+lact::ApplyArgs apply_args(const Plan& p, const lact_state* st, const void* Q, void* O, int64_t m,
+                           int64_t q_stride, const uint16_t* wb, bool* mfma) {
+  lact::ApplyArgs a{};
+  a.Q = Q;
+  a.O = O;
+  a.m = m;
+  a.q_stride = q_stride;
+  a.W1 = st->W1;
+  a.W2 = st->W2;
+  a.W3 = st->W3;
+  a.P = p.P;
+  a.d = p.d;
+  a.h = p.h;
+  a.bf16 = p.bf16;
+  a.w_vec = ((reinterpret_cast<uintptr_t>(st->W1) | reinterpret_cast<uintptr_t>(st->W2) |
+              reinterpret_cast<uintptr_t>(st->W3)) & 15) == 0;
+  *mfma = p.bf16 && lact::apply_mfma_shape_ok(p.d, p.h) && reinterpret_cast<uintptr_t>(Q) % 16 == 0 &&
+          reinterpret_cast<uintptr_t>(O) % 16 == 0 && q_stride % 8 == 0;
+  if (*mfma && wb != nullptr) {
+    const int64_t phd = static_cast<int64_t>(p.P) * p.h * p.d;
+    a.Wb1 = wb;
+    a.Wb2 = wb + phd;
+    a.Wb3 = wb + 2 * phd;
+  }
+  return a;
+}
+
 int run_apply(const Plan& p, const lact_state* st, const void* Q, void* O, int64_t m,
               int64_t q_stride, hipStream_t s, const uint16_t* wb = nullptr) {
   PhaseTimer t(4, s);
@@ -603,29 +653,8 @@ int run_apply(const Plan& p, const lact_state* st, const void* Q, void* O, int64
     if (e != hipSuccess) return hip_fail(e, "linear query-read kernel");
     return LACT_OK;
   }
-  lact::ApplyArgs a{};
-  a.Q = Q;
-  a.O = O;
-  a.m = m;
-  a.q_stride = q_stride;
-  a.W1 = st->W1;
-  a.W2 = st->W2;
-  a.W3 = st->W3;
-  a.P = p.P;
-  a.d = p.d;
-  a.h = p.h;
-  a.bf16 = p.bf16;
-  a.w_vec = ((reinterpret_cast<uintptr_t>(st->W1) | reinterpret_cast<uintptr_t>(st->W2) |
-              reinterpret_cast<uintptr_t>(st->W3)) & 15) == 0;
-  const bool use_mfma = p.bf16 && lact::apply_mfma_shape_ok(p.d, p.h) &&
-                        reinterpret_cast<uintptr_t>(Q) % 16 == 0 &&
-                        reinterpret_cast<uintptr_t>(O) % 16 == 0 && q_stride % 8 == 0;
-  if (use_mfma && wb != nullptr) {
-    const int64_t phd = static_cast<int64_t>(p.P) * p.h * p.d;
-    a.Wb1 = wb;
-    a.Wb2 = wb + phd;
-    a.Wb3 = wb + 2 * phd;
-  }
+  bool use_mfma = false;
+  const lact::ApplyArgs a = apply_args(p, st, Q, O, m, q_stride, wb, &use_mfma);
   hipError_t e = use_mfma ? lact::launch_apply_mfma(a, s) : lact::launch_apply_simple(a, s);
   if (e != hipSuccess) return hip_fail(e, "query-read kernel");
   return LACT_OK;
@@ -1091,6 +1120,40 @@ int lact_chunked_forward(const lact_config* cfg, const lact_state* st, const voi
   // bf16 copy of the weights as the last update left them (none before it)
   uint16_t* wb = L.has_wb ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + L.wb) : nullptr;
   bool wb_valid = false;
+  // Apply-then-update with the matrix-core Muon tail: from the second chunk
+  // on, the tail of chunk c and the query read of chunk c share one launch
+  // (the read takes the CUs the 3P tail workgroups leave); the read loads
+  // the bf16 copy of W_c (written by the previous tail) while the tail
+  // writes W_c+1 and the other copy.  The first chunk's read goes first, on
+  // its own (no copy exists yet).
+  bool fuse = order == LACT_APPLY_THEN_UPDATE && N >= 2 && L.has_wb2 && muon_mfma_tail(p, st);
+  if (fuse) {
+    bool mfma = false;
+    (void)apply_args(p, st, Qc, Oc, chunk_q, T_q * p.d, nullptr, &mfma);
+    fuse = mfma;
+  }
+  if (fuse) {
+    uint16_t* cp[2] = {wb, reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + L.wb2)};
+    for (int64_t c = 0; c < N; ++c) {
+      const void* Kp = Kc + static_cast<size_t>(c * chunk_kv * p.d) * eb;
+      const void* Vp = Vc + static_cast<size_t>(c * chunk_kv * p.d) * eb;
+      const float* ep = eta + c * chunk_kv;
+      const void* Qp = Qc + static_cast<size_t>(c * chunk_q * p.d) * eb;
+      void* Op = Oc + static_cast<size_t>(c * chunk_q * p.d) * eb;
+      if (c == 0) {
+        if ((rc = run_apply(p, st, Qp, Op, chunk_q, T_q * p.d, s, nullptr))) return rc;
+        rc = run_update(cfg, p, st, Kp, Vp, ep, chunk_kv, T_kv * p.d, T_kv, static_cast<char*>(ws), L, s, cp[1],
+                        &wb_valid);
+      } else {
+        bool mfma = false;
+        const lact::ApplyArgs aa = apply_args(p, st, Qp, Op, chunk_q, T_q * p.d, cp[c & 1], &mfma);
+        rc = run_update(cfg, p, st, Kp, Vp, ep, chunk_kv, T_kv * p.d, T_kv, static_cast<char*>(ws), L, s,
+                        cp[(c + 1) & 1], &wb_valid, &aa);
+      }
+      if (rc) return rc;
+    }
+    return LACT_OK;
+  }
   for (int64_t c = 0; c < N; ++c) {
     const void* Kp = Kc + static_cast<size_t>(c * chunk_kv * p.d) * eb;
     const void* Vp = Vc + static_cast<size_t>(c * chunk_kv * p.d) * eb;

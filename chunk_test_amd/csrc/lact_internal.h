@@ -239,6 +239,11 @@ bool grad_d128_shape_ok(int d, int h);  // d = 128, LDS-DMA staging, bf16 or spl
 int grad_d128_stage_tokens(bool split);
 hipError_t launch_grad_d128(const GradArgs& a, bool split, hipStream_t s);
 bool ns_mfma_shape_ok(int d, int h);
+// Muon update tail of one chunk and the query read of the same chunk (from
+// the bf16 copy of its weights) in one launch, where h > d, both have
+// matrix-core kernels and 3P <= 192 (the tail leaves CUs for the read).
+bool muon_tail_apply_ok(int d, int h, int P);
+hipError_t launch_muon_tail_apply(const TailArgs& ta, const ApplyArgs& aa, hipStream_t s);
 bool apply_mfma_shape_ok(int d, int h);
 hipError_t launch_apply_mfma(const ApplyArgs& a, hipStream_t s);
 hipError_t launch_muon_tail(const TailArgs& a, hipStream_t s);  // bf16-mode Muon tail

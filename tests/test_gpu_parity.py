@@ -231,6 +231,44 @@ def test_scan_weight_copy_matches_per_chunk_calls():
         assert np.array_equal(dst[n].cpu().numpy(), s_scan[n]), n
 
 
+@pytest.mark.parametrize("base,kw", [
+    ("video", dict(H=3, T_kv=4 * 1024, T_q=4 * 512, chunk_kv=1024, chunk_q=512)),
+    ("posed", dict(B=2, H=5, T_kv=3 * 2048, T_q=3 * 300, chunk_kv=2048, chunk_q=300,
+                   order="apply_then_update", beta=0.5)),
+], ids=["d128-h256", "d64-h128-momentum-ragged"])
+def test_muon_scan_fused_read_matches_per_chunk_calls(base, kw):
+    """Apply-then-update with the matrix-core Muon tail: from the second chunk
+    on, the scan runs each chunk's update tail and query read in one launch
+    (the read loads the bf16 copy of the chunk's weights while the tail writes
+    the next ones).  Per-chunk lact_apply + lact_update calls (separate
+    launches, fp32 weights converted on the fly) give the same bits."""
+    import torch
+    import chunk_test_amd as L
+    w = small(base, name=f"fused-{base}", **kw)
+    st = S.gen_weights(w)
+    x = S.gen_inputs(w)
+    O_scan, s_scan = G.run_gpu(w, x, st)
+    cfg = G.config_of(w)
+    dst = G.device_state(w, st)
+    Q, K, V = (G.to_dev(x[n], w) for n in ("Q", "K", "V"))
+    eta = G.to_dev(x["eta"], w, io=False)
+    ws = L.alloc_workspace(cfg, w.chunk_kv, w.chunk_q)
+    O = torch.empty_like(Q)
+    for c in range(w.T_kv // w.chunk_kv):
+        kv = slice(c * w.chunk_kv, (c + 1) * w.chunk_kv)
+        qs = slice(c * w.chunk_q, (c + 1) * w.chunk_q)
+        k, v, e = (t[:, :, kv].contiguous() for t in (K, V, eta))
+        q = Q[:, :, qs].contiguous()
+        o = torch.empty_like(q)
+        L.lact_apply(cfg, dst, q, o, ws=ws)
+        L.lact_update(cfg, dst, k, v, e, ws)
+        O[:, :, qs] = o
+    torch.cuda.synchronize()
+    assert np.array_equal(O.float().cpu().numpy(), O_scan)
+    for n in s_scan:
+        assert np.array_equal(dst[n].cpu().numpy(), s_scan[n]), n
+
+
 def test_update_and_apply_entry_points_and_strided_views():
     import torch
     import chunk_test_amd as L
