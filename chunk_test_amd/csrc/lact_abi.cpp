@@ -509,6 +509,7 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
     // GD / momentum: one row-wise kernel for reduction, momentum, step, unit rows
     PhaseTimer t(1, s);
     with_wb();
+    if (fused_read != nullptr) return fail(LACT_ERR_HIP, "internal: fused query read without the Muon tail");
     e = lact::launch_reduce_step(ta, s);
     if (e != hipSuccess) return hip_fail(e, "update-tail kernel");
     return LACT_OK;
@@ -549,7 +550,7 @@ int run_update(const lact_config* c, const Plan& p, const lact_state* st, const 
     if (e != hipSuccess) return hip_fail(e, "Muon update-tail kernel");
     return LACT_OK;
   }
-  if (fused_read != nullptr) return fail(LACT_ERR_HIP, "internal: fused query read without the bf16 Muon tail");
+  if (fused_read != nullptr) return fail(LACT_ERR_HIP, "internal: fused query read without the matrix-core Muon tail");
   // fp32 arithmetic Muon: reduction (+momentum), Newton-Schulz, step + unit rows
   {
     PhaseTimer t(1, s);

@@ -235,13 +235,17 @@ def test_scan_weight_copy_matches_per_chunk_calls():
     ("video", dict(H=3, T_kv=4 * 1024, T_q=4 * 512, chunk_kv=1024, chunk_q=512)),
     ("posed", dict(B=2, H=5, T_kv=3 * 2048, T_q=3 * 300, chunk_kv=2048, chunk_q=300,
                    order="apply_then_update", beta=0.5)),
-], ids=["d128-h256", "d64-h128-momentum-ragged"])
-def test_muon_scan_fused_read_matches_per_chunk_calls(base, kw):
-    """Apply-then-update with the matrix-core Muon tail: from the second chunk
-    on, the scan runs each chunk's update tail and query read in one launch
-    (the read loads the bf16 copy of the chunk's weights while the tail writes
-    the next ones).  Per-chunk lact_apply + lact_update calls (separate
-    launches, fp32 weights converted on the fly) give the same bits."""
+    ("lm", dict(B=1, H=4, T_kv=4 * 1024, T_q=4 * 512, chunk_kv=1024, chunk_q=512)),
+    ("posed", dict(B=3, H=3, T_kv=3 * 2048, T_q=3 * 200, chunk_kv=2048, chunk_q=200,
+                   order="apply_then_update", opt="gd")),
+], ids=["muon-d128-h256", "muon-momentum-d64-h128-ragged", "momentum-d128-h256", "gd-d64-h128-ragged"])
+def test_scan_fused_read_matches_per_chunk_calls(base, kw):
+    """Apply-then-update scans whose query reads load the bf16 weight copy the
+    previous update tail wrote; with the matrix-core Muon tail, from the
+    second chunk on, each chunk's tail and query read run in one launch (the
+    read loads the copy of the chunk's weights while the tail writes the next
+    ones).  Per-chunk lact_apply + lact_update calls (separate launches, fp32
+    weights converted on the fly) give the same bits."""
     import torch
     import chunk_test_amd as L
     w = small(base, name=f"fused-{base}", **kw)
