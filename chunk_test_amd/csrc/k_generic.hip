@@ -577,6 +577,34 @@ __global__ __launch_bounds__(kThreads) void k_reduce_step_v4(TailArgs a, int64_t
 }
 
 // ---------------------------------------------------------------------------
+// The bf16 weight copy of the chunk scan made from the fp32 weights (the
+// update tails write the same values, in the same operand order, after every
+// update): four consecutive floats of one stored row per thread, rounded to
+// nearest even.  Matrix m of pair p: W1 (h x d), W2 (d x h), W3 (h x d).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_wb_copy(const float* W1, const float* W2, const float* W3,
+                                                      uint16_t* wb, int P, int d, int h) {
+  const int64_t hd = static_cast<int64_t>(h) * d;
+  const int64_t per = hd / 4;  // float4 groups per matrix and pair
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= 3 * per * P) return;
+  const int m = static_cast<int>(i / (per * P));
+  const int64_t j = i % (per * P);
+  const int64_t pair = j / per;
+  const int64_t e = 4 * (j % per);
+  const int cols = m == 1 ? h : d;
+  const float* W = (m == 0 ? W1 : m == 1 ? W2 : W3) + pair * hd;
+  const float4 x = *reinterpret_cast<const float4*>(W + e);
+  bf16x4_t b;
+  b[0] = static_cast<__bf16>(x.x);
+  b[1] = static_cast<__bf16>(x.y);
+  b[2] = static_cast<__bf16>(x.z);
+  b[3] = static_cast<__bf16>(x.w);
+  uint16_t* dst = wb + static_cast<int64_t>(m) * P * hd + pair * hd;
+  *reinterpret_cast<bf16x4_t*>(dst + wb_tiled(static_cast<int>(e / cols), static_cast<int>(e % cols), cols)) = b;
+}
+
+// ---------------------------------------------------------------------------
 // Query read O = W2 (silu(W1 q) * (W3 q)).  Grid (ceil(m/32), P); hidden
 // units in slices of 256 staged through LDS.
 // ---------------------------------------------------------------------------
@@ -738,6 +766,17 @@ hipError_t launch_reduce_step(const TailArgs& a, hipStream_t s) {
   const int64_t rows = static_cast<int64_t>(a.P) * (2 * a.h + a.d);
   const unsigned blocks = static_cast<unsigned>((rows + 3) / 4);
   hipLaunchKernelGGL(k_reduce_step, dim3(blocks), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_wb_copy(const float* W1, const float* W2, const float* W3, uint16_t* wb, int P, int d, int h,
+                          hipStream_t s) {
+  if ((reinterpret_cast<uintptr_t>(W1) | reinterpret_cast<uintptr_t>(W2) | reinterpret_cast<uintptr_t>(W3)) & 15 ||
+      d % 16 || h % 16)
+    return hipErrorInvalidValue;
+  const int64_t groups = 3 * static_cast<int64_t>(h) * d / 4 * P;
+  hipLaunchKernelGGL(k_wb_copy, dim3(static_cast<unsigned>((groups + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+                     W1, W2, W3, wb, P, d, h);
   return hipGetLastError();
 }
 

@@ -1121,19 +1121,27 @@ int lact_chunked_forward(const lact_config* cfg, const lact_state* st, const voi
   // bf16 copy of the weights as the last update left them (none before it)
   uint16_t* wb = L.has_wb ? reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + L.wb) : nullptr;
   bool wb_valid = false;
-  // Apply-then-update with the matrix-core Muon tail: from the second chunk
-  // on, the tail of chunk c and the query read of chunk c share one launch
-  // (the read takes the CUs the 3P tail workgroups leave); the read loads
-  // the bf16 copy of W_c (written by the previous tail) while the tail
-  // writes W_c+1 and the other copy.  The first chunk's read goes first, on
-  // its own (no copy exists yet).
-  bool fuse = order == LACT_APPLY_THEN_UPDATE && N >= 2 && L.has_wb2 && muon_mfma_tail(p, st);
-  if (fuse) {
-    bool mfma = false;
-    (void)apply_args(p, st, Qc, Oc, chunk_q, T_q * p.d, nullptr, &mfma);
-    fuse = mfma;
+  // Apply-then-update with a matrix-core query read: the bf16 copy of the
+  // initial weights is made first (one small kernel), so every query read,
+  // the first one included, loads the copy instead of converting the fp32
+  // weights.
+  bool read_mfma = false;
+  if (order == LACT_APPLY_THEN_UPDATE && L.has_wb && !p.linear)
+    (void)apply_args(p, st, Qc, Oc, chunk_q, T_q * p.d, nullptr, &read_mfma);
+  const bool w_aligned = ((reinterpret_cast<uintptr_t>(st->W1) | reinterpret_cast<uintptr_t>(st->W2) |
+                           reinterpret_cast<uintptr_t>(st->W3)) & 15) == 0;
+  // With the matrix-core Muon tail the tail of chunk c and the query read of
+  // chunk c also share one launch (the read takes the CUs the 3P tail
+  // workgroups leave); the read loads the copy of W_c while the tail writes
+  // W_c+1 and the other copy.
+  const bool fuse = read_mfma && L.has_wb2 && muon_mfma_tail(p, st);
+  if (read_mfma && w_aligned) {
+    PhaseTimer t(4, s);
+    hipError_t e = lact::launch_wb_copy(st->W1, st->W2, st->W3, wb, p.P, p.d, p.h, s);
+    if (e != hipSuccess) return hip_fail(e, "bf16 weight-copy kernel");
+    wb_valid = true;
   }
-  if (fuse) {
+  if (fuse && wb_valid) {
     uint16_t* cp[2] = {wb, reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + L.wb2)};
     for (int64_t c = 0; c < N; ++c) {
       const void* Kp = Kc + static_cast<size_t>(c * chunk_kv * p.d) * eb;
@@ -1141,17 +1149,11 @@ int lact_chunked_forward(const lact_config* cfg, const lact_state* st, const voi
       const float* ep = eta + c * chunk_kv;
       const void* Qp = Qc + static_cast<size_t>(c * chunk_q * p.d) * eb;
       void* Op = Oc + static_cast<size_t>(c * chunk_q * p.d) * eb;
-      if (c == 0) {
-        if ((rc = run_apply(p, st, Qp, Op, chunk_q, T_q * p.d, s, nullptr))) return rc;
-        rc = run_update(cfg, p, st, Kp, Vp, ep, chunk_kv, T_kv * p.d, T_kv, static_cast<char*>(ws), L, s, cp[1],
-                        &wb_valid);
-      } else {
-        bool mfma = false;
-        const lact::ApplyArgs aa = apply_args(p, st, Qp, Op, chunk_q, T_q * p.d, cp[c & 1], &mfma);
-        rc = run_update(cfg, p, st, Kp, Vp, ep, chunk_kv, T_kv * p.d, T_kv, static_cast<char*>(ws), L, s,
-                        cp[(c + 1) & 1], &wb_valid, &aa);
-      }
-      if (rc) return rc;
+      bool mfma = false;
+      const lact::ApplyArgs aa = apply_args(p, st, Qp, Op, chunk_q, T_q * p.d, cp[c & 1], &mfma);
+      if ((rc = run_update(cfg, p, st, Kp, Vp, ep, chunk_kv, T_kv * p.d, T_kv, static_cast<char*>(ws), L, s,
+                           cp[(c + 1) & 1], &wb_valid, &aa)))
+        return rc;
     }
     return LACT_OK;
   }

@@ -244,6 +244,10 @@ bool ns_mfma_shape_ok(int d, int h);
 // matrix-core kernels and 3P <= 192 (the tail leaves CUs for the read).
 bool muon_tail_apply_ok(int d, int h, int P);
 hipError_t launch_muon_tail_apply(const TailArgs& ta, const ApplyArgs& aa, hipStream_t s);
+// The bf16 weight copy (P h d values per matrix, W1 | W2 | W3, each matrix in
+// the operand order of wb_tiled) from 16-byte aligned fp32 weights.
+hipError_t launch_wb_copy(const float* W1, const float* W2, const float* W3, uint16_t* wb, int P, int d, int h,
+                          hipStream_t s);
 bool apply_mfma_shape_ok(int d, int h);
 hipError_t launch_apply_mfma(const ApplyArgs& a, hipStream_t s);
 hipError_t launch_muon_tail(const TailArgs& a, hipStream_t s);  // bf16-mode Muon tail
