@@ -135,10 +135,10 @@ def test_random_config_parity(seed):
 
 
 FULL = [
-    ("posed", [(0, 0), (0, 7)], {}),
-    ("million", [(0, 3)], {}),
-    ("lm", [(0, 0), (5, 3)], {}),
-    ("video", [(0, 0), (0, 39)], {}),
+    ("posed", [(0, 0), (0, 4), (0, 7), (0, 11)], {}),
+    ("million", [(0, 3), (0, 10)], {}),
+    ("lm", [(0, 0), (2, 5), (5, 3), (7, 7)], {}),
+    ("video", [(0, 0), (0, 13), (0, 26), (0, 39)], {}),
     # the variants at full size
     ("posed", [(0, 5)], {"eta_per_matrix": True}),
     ("lm", [(2, 6)], {"norm": "keep"}),
@@ -238,7 +238,13 @@ def test_scan_weight_copy_matches_per_chunk_calls():
     ("lm", dict(B=1, H=4, T_kv=4 * 1024, T_q=4 * 512, chunk_kv=1024, chunk_q=512)),
     ("posed", dict(B=3, H=3, T_kv=3 * 2048, T_q=3 * 200, chunk_kv=2048, chunk_q=200,
                    order="apply_then_update", opt="gd")),
-], ids=["muon-d128-h256", "muon-momentum-d64-h128-ragged", "momentum-d128-h256", "gd-d64-h128-ragged"])
+    # one chunk (the shared launch from the first chunk on), and 3P = 198 tail
+    # workgroups (above the 192 that leave room for the read: separate launches)
+    ("posed", dict(H=2, T_kv=2048, T_q=17, chunk_kv=2048, chunk_q=17, order="apply_then_update")),
+    ("posed", dict(B=6, H=11, T_kv=2 * 1024, T_q=2 * 64, chunk_kv=1024, chunk_q=64,
+                   order="apply_then_update")),
+], ids=["muon-d128-h256", "muon-momentum-d64-h128-ragged", "momentum-d128-h256", "gd-d64-h128-ragged",
+        "muon-one-chunk", "muon-66-pairs"])
 def test_scan_fused_read_matches_per_chunk_calls(base, kw):
     """Apply-then-update scans whose query reads load the bf16 weight copy the
     previous update tail wrote; with the matrix-core Muon tail, from the
