@@ -204,9 +204,29 @@ void k_window_attn_mfma(WindowArgs a) {
   k_begin = (k_begin / TT) * TT;
   const int k_end = q_hi + 1;  // exclusive
 
+  // (element offset of this lane's 16 bytes inside a stage, per piece: a
+  // lane constant, so a whole stage needs only the stage's base address)
+  int dofs[TT / 16];
+#pragma unroll
+  for (int k = 0; k < TT / 16; ++k) {
+    const int r = 4 * (4 * k + wv) + (lane >> 4);
+    dofs[k] = r * D + 8 * ((lane & 15) ^ swz(r));
+  }
   auto dma_stage = [&](int k0, int b) {
-    int lane = threadIdx.x & 63;
-    asm volatile("" : "+v"(lane));
+    if (k0 + TT <= T) {
+      const uint16_t* kst = Kg + static_cast<int64_t>(k0) * D;
+      const uint16_t* vst = Vg + static_cast<int64_t>(k0) * D;
+#pragma unroll
+      for (int k = 0; k < TT / 16; ++k) {
+        const int piece = 4 * k + wv;
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(kst + dofs[k]), (lds_ptr_t)(lds + b * TILE + 1024 * piece), 16, 0,
+                                         0);
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(vst + dofs[k]), (lds_ptr_t)(lds + (2 + b) * TILE + 1024 * piece),
+                                         16, 0, 0);
+      }
+      return;
+    }
+    // the last stage: rows past the end re-read the last token
 #pragma unroll
     for (int k = 0; k < TT / 16; ++k) {
       const int piece = 4 * k + wv;
