@@ -11,7 +11,9 @@
 //
 // A and B arrive in bf16 and enter the products exactly; the fp32 factors are
 // split, x = x_hi + x_lo (both bf16), so every product is two MFMAs with fp32
-// accumulation (~16 significant bits per factor, products of A and B exact).
+// accumulation (~16 significant bits per factor, products of A and B exact)
+// -- or, where the layer runs with plain bf16 operand products (the
+// forward's products setting), rounded to bf16, one MFMA per product.
 // One workgroup per (pair, token split, 128-unit hidden slice); wave w owns
 // hidden units 32 w .. 32 w + 31 of the slice and every 32-wide feature tile,
 // twelve 32 x 32 accumulator tiles per wave at d = 128 (six at d = 64).  Each stage of 32
@@ -25,7 +27,9 @@
 //   dq = W1^T X1 + W3^T X3,
 // the three projections and dq as split-operand MFMAs (the weights enter as
 // bf16 hi + lo operands prepared once per call by k_bw_ops, the queries and
-// output cotangents exactly), the element math in fp32.
+// output cotangents exactly), the element math in fp32.  With plain bf16
+// products (SPLIT false) every operand is its bf16 rounding (the hi part
+// alone) and every product one MFMA, as in the forward pass.
 #include "lact_device.h"
 #include "lact_internal.h"
 
@@ -110,7 +114,7 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_bw_contract_mfma(BwContractArgs a, int hsl, int nbase) {
   using R = Rows<D>;
@@ -254,7 +258,7 @@ void k_bw_contract_mfma(BwContractArgs a, int hsl, int nbase) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           xh[x][i] = static_cast<__bf16>(xv[x][i]);
-          xl[x][i] = static_cast<__bf16>(xv[x][i] - static_cast<float>(xh[x][i]));
+          if constexpr (SPLIT) xl[x][i] = static_cast<__bf16>(xv[x][i] - static_cast<float>(xh[x][i]));
         }
       }
 #pragma unroll
@@ -271,9 +275,11 @@ void k_bw_contract_mfma(BwContractArgs a, int hsl, int nbase) {
         acc1[nt] = mfma32(xh[0], opA, acc1[nt]);
         acc3[nt] = mfma32(xh[1], opA, acc3[nt]);
         acc2[nt] = mfma32(opB, xh[2], acc2[nt]);
-        acc1[nt] = mfma32(xl[0], opA, acc1[nt]);
-        acc3[nt] = mfma32(xl[1], opA, acc3[nt]);
-        acc2[nt] = mfma32(opB, xl[2], acc2[nt]);
+        if constexpr (SPLIT) {
+          acc1[nt] = mfma32(xl[0], opA, acc1[nt]);
+          acc3[nt] = mfma32(xl[1], opA, acc3[nt]);
+          acc2[nt] = mfma32(opB, xl[2], acc2[nt]);
+        }
       }
     }
   }
@@ -313,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void k_bw_ops(BwOpsArgs a) {
   const __bf16 lo = static_cast<__bf16>(x - static_cast<float>(hi));
   __bf16* o = reinterpret_cast<__bf16*>(a.op) + pair * a.op_stride + static_cast<int64_t>(m) * 2 * hd;
   o[e_idx] = hi;
-  o[hd + e_idx] = lo;
+  if (!a.hi_only) o[hd + e_idx] = lo;
 }
 
 constexpr int QWG = 128;             // tokens per token-kernel workgroup (32 per wave)
@@ -323,13 +329,14 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
   return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
 }
 
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_bw_apply_mfma(BwTokArgs a) {
   using R = Rows<D>;
   constexpr int NT = D / 32, KS = D / 16, ROW = R::ROW;
   constexpr int WHALF = JT * ROW;     // one matrix part (hi or lo) of a weight tile
-  constexpr int WTILE3 = 6 * WHALF;   // W1, W3, W2^T, hi and lo
+  constexpr int NPART = SPLIT ? 6 : 3;
+  constexpr int WTILE3 = NPART * WHALF;  // W1, W3, W2^T: hi and lo parts (hi only without SPLIT)
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * WTILE3];
   // XCD-aware order: block ids congruent mod 8 run on one XCD, and the
   // token tiles of a pair take consecutive slots of one XCD's share, so the
@@ -373,12 +380,13 @@ void k_bw_apply_mfma(BwTokArgs a) {
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
 #pragma unroll
-    for (int k = 0; k < 6 * PP / 4; ++k) {
+    for (int k = 0; k < NPART * PP / 4; ++k) {
       const int piece = 4 * k + wv;
       const int part = piece / PP;
       const int r = (1024 / ROW) * (piece % PP) + lane / R::LPR;
       const int cl = (lane % R::LPR) ^ R::swz(r);
-      const uint16_t* src = opg + part * hd + static_cast<int64_t>(JT * jt + r) * D + 8 * cl;
+      const int src_part = SPLIT ? part : 2 * part;  // (the hi parts only)
+      const uint16_t* src = opg + src_part * hd + static_cast<int64_t>(JT * jt + r) * D + 8 * cl;
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(lds + b * WTILE3 + part * WHALF + 1024 * (piece % PP)),
                                        16, 0, 0);
     }
@@ -418,12 +426,13 @@ void k_bw_apply_mfma(BwTokArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile jt has landed
     __syncthreads();
     if (jt + 1 < ntile) dma_w(jt + 1, b ^ 1);
+    constexpr int HL = SPLIT ? 2 : 1;  // parts per matrix
     const unsigned char* w1h = lds + b * WTILE3;
     const unsigned char* w1l = w1h + WHALF;
-    const unsigned char* w3h = w1h + 2 * WHALF;
-    const unsigned char* w3l = w1h + 3 * WHALF;
-    const unsigned char* w2h = w1h + 4 * WHALF;
-    const unsigned char* w2l = w1h + 5 * WHALF;
+    const unsigned char* w3h = w1h + HL * WHALF;
+    const unsigned char* w3l = w3h + WHALF;
+    const unsigned char* w2h = w1h + 2 * HL * WHALF;
+    const unsigned char* w2l = w2h + WHALF;
     // projections, transposed: c[j][query] (lane = query, register r =
     // hidden unit 8 (r / 4) + 4 g + r % 4 of the tile)
     f32x16_t c1, c3, cb;
@@ -432,17 +441,19 @@ void k_bw_apply_mfma(BwTokArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(w1h + ak_off[ks]);
-      const bf16x8_t l1 = *reinterpret_cast<const bf16x8_t*>(w1l + ak_off[ks]);
       const bf16x8_t a3 = *reinterpret_cast<const bf16x8_t*>(w3h + ak_off[ks]);
-      const bf16x8_t l3 = *reinterpret_cast<const bf16x8_t*>(w3l + ak_off[ks]);
       const bf16x8_t a2 = *reinterpret_cast<const bf16x8_t*>(w2h + ak_off[ks]);
-      const bf16x8_t l2 = *reinterpret_cast<const bf16x8_t*>(w2l + ak_off[ks]);
       c1 = mfma32(a1, qop[ks], c1);
       c3 = mfma32(a3, qop[ks], c3);
       cb = mfma32(a2, oop[ks], cb);
-      c1 = mfma32(l1, qop[ks], c1);
-      c3 = mfma32(l3, qop[ks], c3);
-      cb = mfma32(l2, oop[ks], cb);
+      if constexpr (SPLIT) {
+        const bf16x8_t l1 = *reinterpret_cast<const bf16x8_t*>(w1l + ak_off[ks]);
+        const bf16x8_t l3 = *reinterpret_cast<const bf16x8_t*>(w3l + ak_off[ks]);
+        const bf16x8_t l2 = *reinterpret_cast<const bf16x8_t*>(w2l + ak_off[ks]);
+        c1 = mfma32(l1, qop[ks], c1);
+        c3 = mfma32(l3, qop[ks], c3);
+        cb = mfma32(l2, oop[ks], cb);
+      }
     }
     // element math; x1 = X1, x3 = X3 (the operands of dq), G
     float x1[16], x3[16], gg[16];
@@ -471,20 +482,25 @@ void k_bw_apply_mfma(BwTokArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         b1h[i] = static_cast<__bf16>(x1[8 * s + i]);
-        b1l[i] = static_cast<__bf16>(x1[8 * s + i] - static_cast<float>(b1h[i]));
         b3h[i] = static_cast<__bf16>(x3[8 * s + i]);
-        b3l[i] = static_cast<__bf16>(x3[8 * s + i] - static_cast<float>(b3h[i]));
+        if constexpr (SPLIT) {
+          b1l[i] = static_cast<__bf16>(x1[8 * s + i] - static_cast<float>(b1h[i]));
+          b3l[i] = static_cast<__bf16>(x3[8 * s + i] - static_cast<float>(b3h[i]));
+        }
       }
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        const bf16x8_t o1h = tr_read(w1h, nt, s), o1l = tr_read(w1l, nt, s);
-        const bf16x8_t o3h = tr_read(w3h, nt, s), o3l = tr_read(w3l, nt, s);
+        const bf16x8_t o1h = tr_read(w1h, nt, s);
+        const bf16x8_t o3h = tr_read(w3h, nt, s);
         dq[nt] = mfma32(o1h, b1h, dq[nt]);
         dq[nt] = mfma32(o3h, b3h, dq[nt]);
-        dq[nt] = mfma32(o1h, b1l, dq[nt]);
-        dq[nt] = mfma32(o3h, b3l, dq[nt]);
-        dq[nt] = mfma32(o1l, b1h, dq[nt]);
-        dq[nt] = mfma32(o3l, b3h, dq[nt]);
+        if constexpr (SPLIT) {
+          const bf16x8_t o1l = tr_read(w1l, nt, s), o3l = tr_read(w3l, nt, s);
+          dq[nt] = mfma32(o1h, b1l, dq[nt]);
+          dq[nt] = mfma32(o3h, b3l, dq[nt]);
+          dq[nt] = mfma32(o1l, b1h, dq[nt]);
+          dq[nt] = mfma32(o3l, b3h, dq[nt]);
+        }
       }
     }
   }
@@ -518,13 +534,14 @@ void k_bw_apply_mfma(BwTokArgs a) {
 // six token-side products per weight tile, all split-operand MFMAs; the
 // weight tile (twelve bf16 parts) is one LDS buffer, refilled after every
 // wave has finished with it.
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_bw_grad_mfma(BwTokArgs a) {
   using R = Rows<D>;
   constexpr int NT = D / 32, KS = D / 16, ROW = R::ROW;
   constexpr int WHALF = JT * ROW;     // one matrix part (hi or lo) of a weight tile
-  constexpr int WTILE6 = 12 * WHALF;  // W1, W3, W2^T, P1, P3, P2^T, hi and lo
+  constexpr int NPART = SPLIT ? 12 : 6;
+  constexpr int WTILE6 = NPART * WHALF;  // W1, W3, W2^T, P1, P3, P2^T: hi and lo (hi only without SPLIT)
   __shared__ __attribute__((aligned(16))) unsigned char lds[WTILE6];
   // XCD-aware order: block ids congruent mod 8 run on one XCD, and the
   // token tiles of a pair take consecutive slots of one XCD's share, so the
@@ -564,12 +581,13 @@ void k_bw_grad_mfma(BwTokArgs a) {
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
 #pragma unroll
-    for (int k = 0; k < 12 * PP / 4; ++k) {
+    for (int k = 0; k < NPART * PP / 4; ++k) {
       const int piece = 4 * k + wv;
       const int part = piece / PP;
       const int r = (1024 / ROW) * (piece % PP) + lane / R::LPR;
       const int cl = (lane % R::LPR) ^ R::swz(r);
-      const uint16_t* src = opg + part * hd + static_cast<int64_t>(JT * jt + r) * D + 8 * cl;
+      const int src_part = SPLIT ? part : 2 * part;  // (the hi parts only)
+      const uint16_t* src = opg + src_part * hd + static_cast<int64_t>(JT * jt + r) * D + 8 * cl;
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(lds + part * WHALF + 1024 * (piece % PP)), 16, 0, 0);
     }
   };
@@ -587,7 +605,9 @@ void k_bw_grad_mfma(BwTokArgs a) {
           (lds_s16x4_t)(base + R::tr(tro, nt, hh) + 16 * ROW * s + 8 * ROW * hh));
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t2[0], t2[1], 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  auto part = [&](int m, int hl) { return static_cast<const unsigned char*>(lds + (2 * m + hl) * WHALF); };
+  auto part = [&](int m, int hl) {
+    return static_cast<const unsigned char*>(lds + (SPLIT ? 2 * m + hl : m) * WHALF);
+  };
 
   f32x16_t ub[NT], kb[NT];
 #pragma unroll
@@ -616,10 +636,12 @@ void k_bw_grad_mfma(BwTokArgs a) {
 #pragma unroll
       for (int m = 0; m < 6; ++m) {
         const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(part(m, 0) + ak_off[ks]);
-        const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(part(m, 1) + ak_off[ks]);
         const bf16x8_t bo = (m == 2 || m == 5) ? vop[ks] : kop[ks];
         c[m] = mfma32(ah, bo, c[m]);
-        c[m] = mfma32(al, bo, c[m]);
+        if constexpr (SPLIT) {
+          const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(part(m, 1) + ak_off[ks]);
+          c[m] = mfma32(al, bo, c[m]);
+        }
       }
     }
     // element math (fp32)
@@ -660,7 +682,7 @@ void k_bw_grad_mfma(BwTokArgs a) {
 #pragma unroll
         for (int q = 0; q < 6; ++q) {
           bh[q][i] = static_cast<__bf16>(v6[q]);
-          bl[q][i] = static_cast<__bf16>(v6[q] - static_cast<float>(bh[q][i]));
+          if constexpr (SPLIT) bl[q][i] = static_cast<__bf16>(v6[q] - static_cast<float>(bh[q][i]));
         }
       }
       // matrix of each B operand: P2^T, W2^T (ubar); P1, P3, W1, W3 (kbar)
@@ -669,11 +691,14 @@ void k_bw_grad_mfma(BwTokArgs a) {
       for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
         for (int q = 0; q < 6; ++q) {
-          const bf16x8_t oh = tr_read(part(mat[q], 0), nt, s), ol = tr_read(part(mat[q], 1), nt, s);
+          const bf16x8_t oh = tr_read(part(mat[q], 0), nt, s);
           f32x16_t& acc = q < 2 ? ub[nt] : kb[nt];
           acc = mfma32(oh, bh[q], acc);
-          acc = mfma32(oh, bl[q], acc);
-          acc = mfma32(ol, bh[q], acc);
+          if constexpr (SPLIT) {
+            const bf16x8_t ol = tr_read(part(mat[q], 1), nt, s);
+            acc = mfma32(oh, bl[q], acc);
+            acc = mfma32(ol, bh[q], acc);
+          }
         }
       }
     }
@@ -724,9 +749,15 @@ hipError_t launch_bw_contract_mfma(const BwContractArgs& a, hipStream_t s) {
   const int nbase = a.S * a.P;
   const int blocks = ((nbase + 7) / 8) * 8 * hsl;
   if (a.d == 128) {
-    hipLaunchKernelGGL(k_bw_contract_mfma<128>, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+    if (a.split)
+      hipLaunchKernelGGL((k_bw_contract_mfma<128, true>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+    else
+      hipLaunchKernelGGL((k_bw_contract_mfma<128, false>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
   } else if (a.d == 64) {
-    hipLaunchKernelGGL(k_bw_contract_mfma<64>, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+    if (a.split)
+      hipLaunchKernelGGL((k_bw_contract_mfma<64, true>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+    else
+      hipLaunchKernelGGL((k_bw_contract_mfma<64, false>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
   } else {
     return hipErrorInvalidValue;
   }
@@ -764,12 +795,18 @@ hipError_t launch_bw_ops(const BwOpsArgs& a, hipStream_t s) {
 hipError_t launch_bw_tok_mfma(const BwTokArgs& a, bool apply, hipStream_t s) {
   const int64_t total = (a.n + QWG - 1) / QWG * a.P;
   const dim3 grid(static_cast<unsigned>((total + 7) / 8 * 8));
-  if (a.d == 128) {
-    if (apply) hipLaunchKernelGGL(k_bw_apply_mfma<128>, grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL(k_bw_grad_mfma<128>, grid, dim3(kThreads), 0, s, a);
+  if (a.d == 128 && a.split) {
+    if (apply) hipLaunchKernelGGL((k_bw_apply_mfma<128, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_bw_grad_mfma<128, true>), grid, dim3(kThreads), 0, s, a);
+  } else if (a.d == 128) {
+    if (apply) hipLaunchKernelGGL((k_bw_apply_mfma<128, false>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_bw_grad_mfma<128, false>), grid, dim3(kThreads), 0, s, a);
+  } else if (a.d == 64 && a.split) {
+    if (apply) hipLaunchKernelGGL((k_bw_apply_mfma<64, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_bw_grad_mfma<64, true>), grid, dim3(kThreads), 0, s, a);
   } else if (a.d == 64) {
-    if (apply) hipLaunchKernelGGL(k_bw_apply_mfma<64>, grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL(k_bw_grad_mfma<64>, grid, dim3(kThreads), 0, s, a);
+    if (apply) hipLaunchKernelGGL((k_bw_apply_mfma<64, false>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_bw_grad_mfma<64, false>), grid, dim3(kThreads), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }

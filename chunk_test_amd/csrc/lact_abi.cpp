@@ -824,6 +824,9 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
     a.d = p.d;
     a.h = p.h;
     a.bf16 = p.bf16;
+    // the matrix-core kernels follow the layer's product precision: hi + lo
+    // operands with split products, plain bf16 operands with bf16 products
+    a.split = p.split;
     hipError_t err;
     if (p.bf16 && (p.d == 64 || p.d == 128)) {  // (the operand region exists exactly then)
       // operands of the matrix-core token kernels as bf16 hi | lo: W1, W3, W2^T
@@ -841,6 +844,7 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
       o.P = p.P;
       o.d = p.d;
       o.h = p.h;
+      o.hi_only = !p.split;
       if ((err = lact::launch_bw_ops(o, s)) != hipSuccess) return hip_fail(err, "backward operand kernel");
       a.op = o.op;
       a.op_stride = o.op_stride;
@@ -869,6 +873,7 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
     b.S = sp.S;
     b.tps = sp.tps;
     b.bf16 = p.bf16;
+    b.split = p.split;
     PhaseTimer tc(7, s);
     if ((err = lact::launch_bw_contract(b, s)) != hipSuccess) return hip_fail(err, "backward contraction kernel");
     if ((err = lact::launch_bw_reduce_add(cot, part, sp.S, 3 * hd, p.P, s)) != hipSuccess)

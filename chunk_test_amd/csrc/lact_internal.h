@@ -149,6 +149,7 @@ struct BwTokArgs {  // token-local VJPs (chunk gradient: A = K, B = V; query rea
   int bf16;
   const uint16_t* op;  // bf16 hi | lo operands of W1, W3, W2^T ([P][3][2][h][d]) or NULL
   int64_t op_stride;   // elements per pair of op
+  int split;           // matrix-core kernels: 1 hi + lo operands (~16 bits), 0 plain bf16 (hi only)
 };
 struct BwOpsArgs {  // matrices as bf16 hi | lo parts in [hidden][feature] order
   MatRef m[6];      // W1, W3, W2 (then P1, P3, P2): m[2], m[5] stored [d][h]
@@ -156,6 +157,7 @@ struct BwOpsArgs {  // matrices as bf16 hi | lo parts in [hidden][feature] order
   uint16_t* op;     // [P][nm][2][h][d]
   int64_t op_stride;
   int P, d, h;  // d = 64 or 128
+  int hi_only;  // write the hi parts only (plain bf16 products)
 };
 struct BwContractArgs {  // X1^T A, (b B)^T X2, X3^T A over tokens, b = -eta or 1
   const void* A;
@@ -168,6 +170,7 @@ struct BwContractArgs {  // X1^T A, (b B)^T X2, X3^T A over tokens, b = -eta or 
   int P, d, h, S;
   int64_t tps;
   int bf16;
+  int split;  // matrix-core kernel: 1 factors as hi + lo (two MFMAs per product), 0 plain bf16
 };
 struct BwStepArgs {
   MatRef W_in[3], W_out[3];  // W1, W2, W3 before and after the update
