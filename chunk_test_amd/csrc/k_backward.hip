@@ -791,6 +791,7 @@ bool backward_shape_ok(int d, int h) { return (d == 32 || d == 64 || d == 128) &
 
 hipError_t launch_bw_tok(const BwTokArgs& a, bool apply, hipStream_t s) {
   if (bw_tok_mfma_ok(a, apply)) return launch_bw_tok_mfma(a, apply, s);
+  if (a.x_bf16) return hipErrorInvalidValue;  // (bf16 factors only from the matrix-core kernels)
   switch (a.d) {
     case 32: return launch_tok_d<32>(a, apply, s);
     case 64: return launch_tok_d<64>(a, apply, s);
@@ -801,6 +802,7 @@ hipError_t launch_bw_tok(const BwTokArgs& a, bool apply, hipStream_t s) {
 
 hipError_t launch_bw_contract(const BwContractArgs& a, hipStream_t s) {
   if (bw_contract_mfma_ok(a)) return launch_bw_contract_mfma(a, s);
+  if (a.x_bf16) return hipErrorInvalidValue;  // (bf16 factors only for the matrix-core contraction)
   switch (a.d) {
     case 32: return launch_contract_d<32>(a, s);
     case 64: return launch_contract_d<64>(a, s);

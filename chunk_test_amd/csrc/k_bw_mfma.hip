@@ -99,14 +99,16 @@ struct Rows<64> {
 };
 
 // the contraction kernel's LDS: A[2], B[2] stages, [2][3] factor stages, rates [2][TT]
-template <int D>
+// (bf16 factors, XB: rows of the 128-unit slice in the Rows<128> layout)
+template <int D, bool XB = false>
 struct CGeo {
   static constexpr int NT = D / 32;
   static constexpr int TILE = TT * Rows<D>::ROW;
+  static constexpr int XT = XB ? TT * Rows<128>::ROW : XTILE;  // one factor stage
   static constexpr int OFF_A = 0;
   static constexpr int OFF_B = 2 * TILE;
   static constexpr int OFF_X = 4 * TILE;
-  static constexpr int OFF_E = OFF_X + 6 * XTILE;
+  static constexpr int OFF_E = OFF_X + 6 * XT;
   static constexpr int LDS_BYTES = OFF_E + 2 * TT * 4;
 };
 
@@ -114,11 +116,13 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool XB>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_bw_contract_mfma(BwContractArgs a, int hsl, int nbase) {
+  static_assert(!(SPLIT && XB), "bf16 factors come with plain products");
   using R = Rows<D>;
-  using C = CGeo<D>;
+  using C = CGeo<D, XB>;
+  constexpr int XT = C::XT;
   constexpr int NT = C::NT, ROW = R::ROW, TILE = C::TILE;
   constexpr int OFF_A = C::OFF_A, OFF_B = C::OFF_B, OFF_X = C::OFF_X, OFF_E = C::OFF_E;
   __shared__ __attribute__((aligned(16))) unsigned char lds[C::LDS_BYTES];
@@ -153,6 +157,10 @@ void k_bw_contract_mfma(BwContractArgs a, int hsl, int nbase) {
   const float* Xg[3] = {a.X1 + static_cast<int64_t>(pair) * a.x_stride + j0,
                         a.X3 + static_cast<int64_t>(pair) * a.x_stride + j0,
                         a.X2 + static_cast<int64_t>(pair) * a.x_stride + j0};
+  // (bf16 factors: the same element offsets in arrays of 2-byte elements)
+  const uint16_t* Xh[3] = {reinterpret_cast<const uint16_t*>(a.X1) + static_cast<int64_t>(pair) * a.x_stride + j0,
+                           reinterpret_cast<const uint16_t*>(a.X3) + static_cast<int64_t>(pair) * a.x_stride + j0,
+                           reinterpret_cast<const uint16_t*>(a.X2) + static_cast<int64_t>(pair) * a.x_stride + j0};
 
   // DMA of one stage into buffer b.  A, B: 1 KiB pieces in the Rows<D>
   // layout (one piece per wave at d = 64, two at d = 128).  Factors: 1 KiB pieces
@@ -176,16 +184,31 @@ void k_bw_contract_mfma(BwContractArgs a, int hsl, int nbase) {
     }
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
+      if constexpr (XB) {
+        // bf16 factor rows of 256 bytes in the Rows<128> layout: 1 KiB pieces of four rows
 #pragma unroll
-      for (int k = 0; k < TT / 8; ++k) {
-        const int piece = 4 * k + wv;  // rows 2 piece, 2 piece + 1
-        const int r = 2 * piece + (lane >> 5);
-        const int cl = (lane & 31) ^ (8 * ((r >> 2) & 1));
-        const int tok = static_cast<int>(t0) + r;
-        const int tc = tok < t_last ? tok : t_last;
-        const float* src = Xg[x] + static_cast<int64_t>(tc) * h + 4 * cl;
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(lds + OFF_X + (b * 3 + x) * XTILE + 1024 * piece),
-                                         16, 0, 0);
+        for (int k = 0; k < TT / 16; ++k) {
+          const int piece = 4 * k + wv;
+          const int r = 4 * piece + (lane >> 4);
+          const int cl = (lane & 15) ^ Rows<128>::swz(r);
+          const int tok = static_cast<int>(t0) + r;
+          const int tc = tok < t_last ? tok : t_last;
+          const uint16_t* src = Xh[x] + static_cast<int64_t>(tc) * h + 8 * cl;
+          __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(lds + OFF_X + (b * 3 + x) * XT + 1024 * piece),
+                                           16, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < TT / 8; ++k) {
+          const int piece = 4 * k + wv;  // rows 2 piece, 2 piece + 1
+          const int r = 2 * piece + (lane >> 5);
+          const int cl = (lane & 31) ^ (8 * ((r >> 2) & 1));
+          const int tok = static_cast<int>(t0) + r;
+          const int tc = tok < t_last ? tok : t_last;
+          const float* src = Xg[x] + static_cast<int64_t>(tc) * h + 4 * cl;
+          __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(lds + OFF_X + (b * 3 + x) * XT + 1024 * piece),
+                                           16, 0, 0);
+        }
       }
     }
     if (etag != nullptr && wv == 0 && lane < TT) {
@@ -199,9 +222,11 @@ void k_bw_contract_mfma(BwContractArgs a, int hsl, int nbase) {
     }
   };
 
-  // transpose reads of A and B (tokens as the k index, Rows<D>)
-  int tro[4];
+  // transpose reads of A and B (tokens as the k index, Rows<D>), and of the
+  // bf16 factors (Rows<128>: lane = hidden unit 32 wave + ln of the slice)
+  int tro[4], trx[4];
   R::tr_init(lane, tro);
+  Rows<128>::tr_init(lane, trx);
   // factor reads: slot i of lane (g, ln) is token 8 (i / 4) + 4 g + i % 4 of
   // the 16-token half, hidden unit 32 wave + ln of the slice; bit 2 of those
   // tokens is g, so the swizzled chunk is a lane constant.
@@ -226,39 +251,61 @@ void k_bw_contract_mfma(BwContractArgs a, int hsl, int nbase) {
     if (t0 + TT < t_end) dma_stage(t0 + TT, b ^ 1);
     const unsigned char* ab = lds + OFF_A + b * TILE;
     const unsigned char* bb = lds + OFF_B + b * TILE;
-    const unsigned char* xb = lds + OFF_X + b * 3 * XTILE;
+    const unsigned char* xb = lds + OFF_X + b * 3 * XT;
     const float* eb = reinterpret_cast<const float*>(lds + OFF_E + b * TT * 4);
     const int valid = static_cast<int>(t_end - t0);  // tokens of this stage that exist (may exceed TT)
 #pragma unroll
     for (int s = 0; s < TT / 16; ++s) {
-      // factors of this lane's eight tokens, zero past the end; the rate
-      // (for the contraction with B) multiplies X2
-      float xv[3][8];
-#pragma unroll
-      for (int x = 0; x < 3; ++x) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int t = 16 * s + 8 * (i >> 2) + 4 * g + (i & 3);
-          const float v = *reinterpret_cast<const float*>(xb + x * XTILE + t * XROW + x_off);
-          xv[x][i] = t < valid ? v : 0.f;
-        }
-      }
-      if (etag != nullptr) {
-        const f32x4_t e0 = *reinterpret_cast<const f32x4_t*>(eb + 16 * s + 4 * g);
-        const f32x4_t e1 = *reinterpret_cast<const f32x4_t*>(eb + 16 * s + 8 + 4 * g);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          xv[2][i] *= -e0[i];
-          xv[2][4 + i] *= -e1[i];
-        }
-      }
       bf16x8_t xh[3], xl[3];
+      if constexpr (XB) {
+        // bf16 factors (X2 already carries the rate) by transpose reads: slot
+        // i = token 16 s + 8 (i / 4) + 4 g + i % 4; zero past the end
 #pragma unroll
-      for (int x = 0; x < 3; ++x) {
+        for (int x = 0; x < 3; ++x) {
+          s16x4_t t2[2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          xh[x][i] = static_cast<__bf16>(xv[x][i]);
-          if constexpr (SPLIT) xl[x][i] = static_cast<__bf16>(xv[x][i] - static_cast<float>(xh[x][i]));
+          for (int hh = 0; hh < 2; ++hh)
+            t2[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4_t)(xb + x * XT + Rows<128>::tr(trx, wave, hh) + 16 * Rows<128>::ROW * s +
+                              8 * Rows<128>::ROW * hh));
+          xh[x] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t2[0], t2[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          if (valid < TT) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const int t = 16 * s + 8 * (i >> 2) + 4 * g + (i & 3);
+              if (t >= valid) xh[x][i] = static_cast<__bf16>(0.f);
+            }
+          }
+        }
+      } else {
+        // factors of this lane's eight tokens, zero past the end; the rate
+        // (for the contraction with B) multiplies X2
+        float xv[3][8];
+#pragma unroll
+        for (int x = 0; x < 3; ++x) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int t = 16 * s + 8 * (i >> 2) + 4 * g + (i & 3);
+            const float v = *reinterpret_cast<const float*>(xb + x * XT + t * XROW + x_off);
+            xv[x][i] = t < valid ? v : 0.f;
+          }
+        }
+        if (etag != nullptr) {
+          const f32x4_t e0 = *reinterpret_cast<const f32x4_t*>(eb + 16 * s + 4 * g);
+          const f32x4_t e1 = *reinterpret_cast<const f32x4_t*>(eb + 16 * s + 8 + 4 * g);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            xv[2][i] *= -e0[i];
+            xv[2][4 + i] *= -e1[i];
+          }
+        }
+#pragma unroll
+        for (int x = 0; x < 3; ++x) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            xh[x][i] = static_cast<__bf16>(xv[x][i]);
+            if constexpr (SPLIT) xl[x][i] = static_cast<__bf16>(xv[x][i] - static_cast<float>(xh[x][i]));
+          }
         }
       }
 #pragma unroll
@@ -320,6 +367,15 @@ __global__ __launch_bounds__(kThreads) void k_bw_ops(BwOpsArgs a) {
   __bf16* o = reinterpret_cast<__bf16*>(a.op) + pair * a.op_stride + static_cast<int64_t>(m) * 2 * hd;
   o[e_idx] = hi;
   if (!a.hi_only) o[hd + e_idx] = lo;
+}
+
+// four factors at hidden units j .. j + 3 of a token's bf16 factor row Xb,
+// times f, rounded to bf16
+__device__ __forceinline__ void store_bf16x4(uint16_t* Xb, int j, const float* v, float f) {
+  bf16x4_t b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = static_cast<__bf16>(f * v[i]);
+  *reinterpret_cast<bf16x4_t*>(Xb + j) = b;
 }
 
 constexpr int QWG = 128;             // tokens per token-kernel workgroup (32 per wave)
@@ -418,6 +474,10 @@ void k_bw_apply_mfma(BwTokArgs a) {
   float* X1 = a.X1 + pair * a.x_stride + t * h;
   float* X2 = a.X2 + pair * a.x_stride + t * h;
   float* X3 = a.X3 + pair * a.x_stride + t * h;
+  // (bf16 factors: the same element offsets in arrays of 2-byte elements)
+  uint16_t* Xb1 = reinterpret_cast<uint16_t*>(a.X1) + pair * a.x_stride + t * h;
+  uint16_t* Xb2 = reinterpret_cast<uint16_t*>(a.X2) + pair * a.x_stride + t * h;
+  uint16_t* Xb3 = reinterpret_cast<uint16_t*>(a.X3) + pair * a.x_stride + t * h;
   const bool live = t < a.n;
 
   dma_w(0, 0);
@@ -470,9 +530,15 @@ void k_bw_apply_mfma(BwTokArgs a) {
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int j = JT * jt + 8 * rg + 4 * g;
-        *reinterpret_cast<f32x4_t*>(X1 + j) = f32x4_t{x1[4 * rg], x1[4 * rg + 1], x1[4 * rg + 2], x1[4 * rg + 3]};
-        *reinterpret_cast<f32x4_t*>(X2 + j) = f32x4_t{gg[4 * rg], gg[4 * rg + 1], gg[4 * rg + 2], gg[4 * rg + 3]};
-        *reinterpret_cast<f32x4_t*>(X3 + j) = f32x4_t{x3[4 * rg], x3[4 * rg + 1], x3[4 * rg + 2], x3[4 * rg + 3]};
+        if (a.x_bf16) {
+          store_bf16x4(Xb1, j, x1 + 4 * rg, 1.f);
+          store_bf16x4(Xb2, j, gg + 4 * rg, 1.f);
+          store_bf16x4(Xb3, j, x3 + 4 * rg, 1.f);
+        } else {
+          *reinterpret_cast<f32x4_t*>(X1 + j) = f32x4_t{x1[4 * rg], x1[4 * rg + 1], x1[4 * rg + 2], x1[4 * rg + 3]};
+          *reinterpret_cast<f32x4_t*>(X2 + j) = f32x4_t{gg[4 * rg], gg[4 * rg + 1], gg[4 * rg + 2], gg[4 * rg + 3]};
+          *reinterpret_cast<f32x4_t*>(X3 + j) = f32x4_t{x3[4 * rg], x3[4 * rg + 1], x3[4 * rg + 2], x3[4 * rg + 3]};
+        }
       }
     }
     // dq[e][query] += sum over the tile's hidden units of W1[j][e] X1 + W3[j][e] X3
@@ -618,6 +684,10 @@ void k_bw_grad_mfma(BwTokArgs a) {
   float* X1 = a.X1 + pair * a.x_stride + t * h;
   float* X2 = a.X2 + pair * a.x_stride + t * h;
   float* X3 = a.X3 + pair * a.x_stride + t * h;
+  // (bf16 factors: the same element offsets in arrays of 2-byte elements)
+  uint16_t* Xb1 = reinterpret_cast<uint16_t*>(a.X1) + pair * a.x_stride + t * h;
+  uint16_t* Xb2 = reinterpret_cast<uint16_t*>(a.X2) + pair * a.x_stride + t * h;
+  uint16_t* Xb3 = reinterpret_cast<uint16_t*>(a.X3) + pair * a.x_stride + t * h;
 
   dma_w(0);
   for (int jt = 0; jt < ntile; ++jt) {
@@ -666,9 +736,15 @@ void k_bw_grad_mfma(BwTokArgs a) {
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int j = JT * jt + 8 * rg + 4 * g;
-        *reinterpret_cast<f32x4_t*>(X1 + j) = f32x4_t{x1[4 * rg], x1[4 * rg + 1], x1[4 * rg + 2], x1[4 * rg + 3]};
-        *reinterpret_cast<f32x4_t*>(X2 + j) = f32x4_t{x2[4 * rg], x2[4 * rg + 1], x2[4 * rg + 2], x2[4 * rg + 3]};
-        *reinterpret_cast<f32x4_t*>(X3 + j) = f32x4_t{x3[4 * rg], x3[4 * rg + 1], x3[4 * rg + 2], x3[4 * rg + 3]};
+        if (a.x_bf16) {
+          store_bf16x4(Xb1, j, x1 + 4 * rg, 1.f);
+          store_bf16x4(Xb2, j, x2 + 4 * rg, ne);  // (the rate of the contraction with V)
+          store_bf16x4(Xb3, j, x3 + 4 * rg, 1.f);
+        } else {
+          *reinterpret_cast<f32x4_t*>(X1 + j) = f32x4_t{x1[4 * rg], x1[4 * rg + 1], x1[4 * rg + 2], x1[4 * rg + 3]};
+          *reinterpret_cast<f32x4_t*>(X2 + j) = f32x4_t{x2[4 * rg], x2[4 * rg + 1], x2[4 * rg + 2], x2[4 * rg + 3]};
+          *reinterpret_cast<f32x4_t*>(X3 + j) = f32x4_t{x3[4 * rg], x3[4 * rg + 1], x3[4 * rg + 2], x3[4 * rg + 3]};
+        }
       }
     }
     // token-side sums over the tile's hidden units
@@ -750,14 +826,18 @@ hipError_t launch_bw_contract_mfma(const BwContractArgs& a, hipStream_t s) {
   const int blocks = ((nbase + 7) / 8) * 8 * hsl;
   if (a.d == 128) {
     if (a.split)
-      hipLaunchKernelGGL((k_bw_contract_mfma<128, true>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+      hipLaunchKernelGGL((k_bw_contract_mfma<128, true, false>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+    else if (a.x_bf16)
+      hipLaunchKernelGGL((k_bw_contract_mfma<128, false, true>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
     else
-      hipLaunchKernelGGL((k_bw_contract_mfma<128, false>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+      hipLaunchKernelGGL((k_bw_contract_mfma<128, false, false>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
   } else if (a.d == 64) {
     if (a.split)
-      hipLaunchKernelGGL((k_bw_contract_mfma<64, true>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+      hipLaunchKernelGGL((k_bw_contract_mfma<64, true, false>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+    else if (a.x_bf16)
+      hipLaunchKernelGGL((k_bw_contract_mfma<64, false, true>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
     else
-      hipLaunchKernelGGL((k_bw_contract_mfma<64, false>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+      hipLaunchKernelGGL((k_bw_contract_mfma<64, false, false>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
   } else {
     return hipErrorInvalidValue;
   }

@@ -849,11 +849,6 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
       a.op = o.op;
       a.op_stride = o.op_stride;
     }
-    {
-      PhaseTimer t(apply ? 6 : 5, s);
-      err = lact::launch_bw_tok(a, apply, s);
-    }
-    if (err != hipSuccess) return hip_fail(err, "backward token kernel");
     const Splits sp = plan_splits(backward_rule(p), n);
     lact::BwContractArgs b{};
     b.A = A;
@@ -874,6 +869,15 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
     b.tps = sp.tps;
     b.bf16 = p.bf16;
     b.split = p.split;
+    // with plain bf16 products and matrix-core kernels on both sides the
+    // factors travel as bf16 (half the bytes; the contraction rounds them to
+    // bf16 operands either way), X2 of the chunk gradient already times -eta
+    a.x_bf16 = b.x_bf16 = !p.split && lact::bw_tok_mfma_ok(a, apply) && lact::bw_contract_mfma_ok(b);
+    {
+      PhaseTimer t(apply ? 6 : 5, s);
+      err = lact::launch_bw_tok(a, apply, s);
+    }
+    if (err != hipSuccess) return hip_fail(err, "backward token kernel");
     PhaseTimer tc(7, s);
     if ((err = lact::launch_bw_contract(b, s)) != hipSuccess) return hip_fail(err, "backward contraction kernel");
     if ((err = lact::launch_bw_reduce_add(cot, part, sp.S, 3 * hd, p.P, s)) != hipSuccess)

@@ -150,6 +150,8 @@ struct BwTokArgs {  // token-local VJPs (chunk gradient: A = K, B = V; query rea
   const uint16_t* op;  // bf16 hi | lo operands of W1, W3, W2^T ([P][3][2][h][d]) or NULL
   int64_t op_stride;   // elements per pair of op
   int split;           // matrix-core kernels: 1 hi + lo operands (~16 bits), 0 plain bf16 (hi only)
+  int x_bf16;          // matrix-core kernels: factors stored as bf16 (X2 of the chunk gradient
+                       // times -eta), for the plain-bf16 matrix-core contraction; else fp32
 };
 struct BwOpsArgs {  // matrices as bf16 hi | lo parts in [hidden][feature] order
   MatRef m[6];      // W1, W3, W2 (then P1, P3, P2): m[2], m[5] stored [d][h]
@@ -171,6 +173,7 @@ struct BwContractArgs {  // X1^T A, (b B)^T X2, X3^T A over tokens, b = -eta or 
   int64_t tps;
   int bf16;
   int split;  // matrix-core kernel: 1 factors as hi + lo (two MFMAs per product), 0 plain bf16
+  int x_bf16;  // the factors are bf16 (X2 of the chunk gradient already times -eta; needs split 0)
 };
 struct BwStepArgs {
   MatRef W_in[3], W_out[3];  // W1, W2, W3 before and after the update
