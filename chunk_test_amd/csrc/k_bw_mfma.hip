@@ -350,23 +350,55 @@ void k_bw_contract_mfma(BwContractArgs a, int hsl, int nbase) {
 // Operands of the token kernels: every matrix as bf16 hi and lo parts in
 // [hidden unit][feature] order (W2 and P2, stored [feature][hidden unit], are
 // transposed): op[pair][m][hl][j][e], m over W1, W3, W2 (and P1, P3, P2).
+// the matrices stored [hidden][feature] (W1, W3, P1, P3): element by element
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_bw_ops(BwOpsArgs a) {
   const int64_t hd = static_cast<int64_t>(a.h) * D;
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t total = static_cast<int64_t>(a.P) * a.nm * hd;
+  const int nd = a.nm == 6 ? 4 : 2;  // direct matrices: m = 0, 1 (and 3, 4)
+  const int64_t total = static_cast<int64_t>(a.P) * nd * hd;
   if (idx >= total) return;
   const int64_t pm = idx / hd, e_idx = idx % hd;
-  const int pair = static_cast<int>(pm / a.nm), m = static_cast<int>(pm % a.nm);
-  const int j = static_cast<int>(e_idx / D), e = static_cast<int>(e_idx % D);
+  const int pair = static_cast<int>(pm / nd), k = static_cast<int>(pm % nd);
+  const int m = k < 2 ? k : k + 1;
   const MatRef& r = a.m[m];
-  const bool tr = (m % 3) == 2;  // W2, P2: stored [D][h]
-  const float x = r.p[pair * r.pair_stride + (tr ? static_cast<int64_t>(e) * a.h + j : e_idx)];
+  const float x = r.p[pair * r.pair_stride + e_idx];
   const __bf16 hi = static_cast<__bf16>(x);
-  const __bf16 lo = static_cast<__bf16>(x - static_cast<float>(hi));
   __bf16* o = reinterpret_cast<__bf16*>(a.op) + pair * a.op_stride + static_cast<int64_t>(m) * 2 * hd;
   o[e_idx] = hi;
-  if (!a.hi_only) o[hd + e_idx] = lo;
+  if (!a.hi_only) o[hd + e_idx] = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+
+// W2 and P2 (stored [feature][hidden]) transposed into [hidden][feature]:
+// one 64 x 64 tile per workgroup through LDS, so both the fp32 reads (64
+// hidden units of a feature row) and the bf16 writes (64 features of a
+// hidden row) are contiguous
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_bw_ops_tr(BwOpsArgs a) {
+  __shared__ float tile[64][65];
+  const int jt = blockIdx.x;           // 64-unit hidden tile
+  const int et = blockIdx.y;           // 64-feature tile
+  const int pair = blockIdx.z / (a.nm == 6 ? 2 : 1);
+  const int m = (a.nm == 6 && (blockIdx.z & 1)) ? 5 : 2;
+  const MatRef& r = a.m[m];
+  const int64_t hd = static_cast<int64_t>(a.h) * D;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const float* src = r.p + pair * r.pair_stride;
+  for (int i = ty; i < 64; i += kThreads / 64) {
+    const int e = 64 * et + i, j = 64 * jt + tx;
+    tile[i][tx] = (e < D && j < a.h) ? src[static_cast<int64_t>(e) * a.h + j] : 0.f;
+  }
+  __syncthreads();
+  __bf16* o = reinterpret_cast<__bf16*>(a.op) + pair * a.op_stride + static_cast<int64_t>(m) * 2 * hd;
+  for (int i = ty; i < 64; i += kThreads / 64) {
+    const int j = 64 * jt + i, e = 64 * et + tx;
+    if (j < a.h && e < D) {
+      const float x = tile[tx][i];
+      const __bf16 hi = static_cast<__bf16>(x);
+      o[static_cast<int64_t>(j) * D + e] = hi;
+      if (!a.hi_only) o[hd + static_cast<int64_t>(j) * D + e] = static_cast<__bf16>(x - static_cast<float>(hi));
+    }
+  }
 }
 
 // four factors at hidden units j .. j + 3 of a token's bf16 factor row Xb,
@@ -859,15 +891,19 @@ bool bw_tok_mfma_ok(const BwTokArgs& a, bool apply) {
 }
 
 hipError_t launch_bw_ops(const BwOpsArgs& a, hipStream_t s) {
-  if ((a.d != 64 && a.d != 128) || a.nm < 1 || a.nm > 6 ||
-      a.op_stride < static_cast<int64_t>(2) * a.nm * a.h * a.d)
+  if ((a.d != 64 && a.d != 128) || (a.nm != 3 && a.nm != 6) ||
+      a.op_stride < static_cast<int64_t>(2) * a.nm * a.h * a.d || static_cast<int64_t>(a.P) * (a.nm / 3) > 65535)
     return hipErrorInvalidValue;
-  const int64_t total = static_cast<int64_t>(a.P) * a.nm * a.h * a.d;
+  const int64_t total = static_cast<int64_t>(a.P) * (a.nm == 6 ? 4 : 2) * a.h * a.d;
   const dim3 grid(static_cast<unsigned>((total + kThreads - 1) / kThreads));
+  const dim3 grid_tr(static_cast<unsigned>((a.h + 63) / 64), static_cast<unsigned>((a.d + 63) / 64),
+                     static_cast<unsigned>(a.P * (a.nm / 3)));
   if (a.d == 128) {
     hipLaunchKernelGGL(k_bw_ops<128>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(k_bw_ops_tr<128>, grid_tr, dim3(kThreads), 0, s, a);
   } else {
     hipLaunchKernelGGL(k_bw_ops<64>, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(k_bw_ops_tr<64>, grid_tr, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }
