@@ -362,7 +362,9 @@ __global__ __launch_bounds__(kThreads) void k_bw_reduce_add(float* dst, const fl
 
 // ---------------------------------------------------------------------------
 // Through W' = rows(W - step d) for every stored row (one wavefront per row):
-// R = W - step d recomputed, Y = W' (checkpoint), dY the running cotangent;
+// R = W - step d recomputed, Y = W' (checkpoint), dY the running cotangent
+// (plus the split sums of the contractions still pending, in the order a
+// separate reduction pass would have added them);
 //   dR = (dY - Y (Y . dY)) / ||R||   (dY / norm_eps where ||R|| <= norm_eps),
 // then the running cotangent becomes dR (W enters R directly) and the
 // direction's cotangent is -step dR.
@@ -402,10 +404,20 @@ __global__ __launch_bounds__(kThreads) void k_bw_step(BwStepArgs a) {
     const int e = lane + 64 * k;
     dy[k] = y[k] = 0.f;
     if (e < len) {
-      const float rr = W[e] - a.step * a.dir[blk + e];
+      const float dv = a.dir != nullptr ? a.dir[blk + e] : a.dir_m[m].p[pair * a.dir_m[m].pair_stride + off + e];
+      const float rr = W[e] - a.step * dv;
       ss += rr * rr;
       y[k] = Y[e];
       dy[k] = a.cot[blk + e];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if (a.pend[q] != nullptr) {
+          const float* src = a.pend[q] + pair * a.pend_S[q] * 3 * hd + m * hd + off + e;
+          float g = 0.f;
+          for (int sp = 0; sp < a.pend_S[q]; ++sp) g += src[sp * 3 * hd];
+          dy[k] += g;
+        }
+      }
       yd += y[k] * dy[k];
     }
   }
@@ -419,7 +431,14 @@ __global__ __launch_bounds__(kThreads) void k_bw_step(BwStepArgs a) {
     if (e < len) {
       const float dr = big ? (dy[k] - y[k] * yd) / nrm : dy[k] / a.norm_eps;
       a.cot[blk + e] = dr;
-      a.ddir[blk + e] = -a.step * dr;
+      const float dd = __fmul_rn(-a.step, dr);
+      if (a.dM != nullptr) {
+        const float v = __fadd_rn(dd, a.dM[blk + e]);
+        a.pc[blk + e] = v;
+        a.dM[blk + e] = __fmul_rn(a.beta, v);
+      } else {
+        a.ddir[blk + e] = dd;
+      }
     }
   }
 }

@@ -351,10 +351,11 @@ void k_bw_contract_mfma(BwContractArgs a, int hsl, int nbase) {
 // [hidden unit][feature] order (W2 and P2, stored [feature][hidden unit], are
 // transposed): op[pair][m][hl][j][e], m over W1, W3, W2 (and P1, P3, P2).
 // the matrices stored [hidden][feature] (W1, W3, P1, P3): element by element
+// (four consecutive elements per thread: hd is a multiple of 64)
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_bw_ops(BwOpsArgs a) {
   const int64_t hd = static_cast<int64_t>(a.h) * D;
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t idx = 4 * (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x);
   const int nd = a.nm == 6 ? 4 : 2;  // direct matrices: m = 0, 1 (and 3, 4)
   const int64_t total = static_cast<int64_t>(a.P) * nd * hd;
   if (idx >= total) return;
@@ -362,11 +363,23 @@ __global__ __launch_bounds__(kThreads) void k_bw_ops(BwOpsArgs a) {
   const int pair = static_cast<int>(pm / nd), k = static_cast<int>(pm % nd);
   const int m = k < 2 ? k : k + 1;
   const MatRef& r = a.m[m];
-  const float x = r.p[pair * r.pair_stride + e_idx];
-  const __bf16 hi = static_cast<__bf16>(x);
+  const float* src = r.p + pair * r.pair_stride + e_idx;
+  f32x4_t x;
+  if ((reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+    x = *reinterpret_cast<const f32x4_t*>(src);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = src[i];
+  }
+  bf16x4_t hi, lo;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = static_cast<__bf16>(x[i]);
+    lo[i] = static_cast<__bf16>(x[i] - static_cast<float>(hi[i]));
+  }
   __bf16* o = reinterpret_cast<__bf16*>(a.op) + pair * a.op_stride + static_cast<int64_t>(m) * 2 * hd;
-  o[e_idx] = hi;
-  if (!a.hi_only) o[hd + e_idx] = static_cast<__bf16>(x - static_cast<float>(hi));
+  *reinterpret_cast<bf16x4_t*>(o + e_idx) = hi;
+  if (!a.hi_only) *reinterpret_cast<bf16x4_t*>(o + hd + e_idx) = lo;
 }
 
 // W2 and P2 (stored [feature][hidden]) transposed into [hidden][feature]:
@@ -894,7 +907,7 @@ hipError_t launch_bw_ops(const BwOpsArgs& a, hipStream_t s) {
   if ((a.d != 64 && a.d != 128) || (a.nm != 3 && a.nm != 6) ||
       a.op_stride < static_cast<int64_t>(2) * a.nm * a.h * a.d || static_cast<int64_t>(a.P) * (a.nm / 3) > 65535)
     return hipErrorInvalidValue;
-  const int64_t total = static_cast<int64_t>(a.P) * (a.nm == 6 ? 4 : 2) * a.h * a.d;
+  const int64_t total = static_cast<int64_t>(a.P) * (a.nm == 6 ? 4 : 2) * a.h * a.d / 4;
   const dim3 grid(static_cast<unsigned>((total + kThreads - 1) / kThreads));
   const dim3 grid_tr(static_cast<unsigned>((a.h + 63) / 64), static_cast<unsigned>((a.d + 63) / 64),
                      static_cast<unsigned>(a.P * (a.nm / 3)));

@@ -668,7 +668,7 @@ struct BwLayout {
   size_t ckW = 0, ckM = 0;  // N + 1 slots of W1 | W2 | W3 (and of M1 | M2 | M3)
   size_t cot = 0, dM = 0, g = 0, dir = 0, ddir = 0, pc = 0, t = 0;  // [P, 3hd] each
   size_t X = 0;           // three [P, max(chunk_kv, chunk_q), h] factor arrays
-  size_t part = 0;        // contraction partials [P, S, 3hd]
+  size_t part = 0, part2 = 0;  // contraction partials [P, S, 3hd] (chunk gradient's, query read's)
   size_t ns = 0;          // Newton-Schulz VJP scratch
   size_t op = 0;          // bf16 hi | lo operands of the matrix-core token kernels [P][6][2][h][d]
   size_t total = 0;
@@ -701,6 +701,7 @@ BwLayout bw_layout(const lact_config* c, const Plan& p, int64_t N, int64_t chunk
   b.t = take(sizeof(float) * per);
   b.X = take(sizeof(float) * 3 * static_cast<size_t>(p.P) * static_cast<size_t>(b.rows) * p.h);
   b.part = take(sizeof(float) * per * static_cast<size_t>(b.S));
+  b.part2 = take(sizeof(float) * per * static_cast<size_t>(b.S));
   b.op = take(p.bf16 && (p.d == 64 || p.d == 128) ? sizeof(uint16_t) * 4 * per : 0);
   b.ns = take(p.muon ? sizeof(float) * 3 * static_cast<size_t>(p.P) *
                            static_cast<size_t>(lact::bw_ns_floats_per_matrix(p.d, p.h, c->ns_iters))
@@ -739,7 +740,11 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
   float* pc = reinterpret_cast<float*>(ws + L.pc);
   float* tb = reinterpret_cast<float*>(ws + L.t);
   float* X = reinterpret_cast<float*>(ws + L.X);
-  float* part = reinterpret_cast<float*>(ws + L.part);
+  // split partials of the last contractions (0: chunk gradient, 1: query
+  // read), summed into the cotangent by the next step kernel or at the end
+  float* const partbuf[2] = {reinterpret_cast<float*>(ws + L.part), reinterpret_cast<float*>(ws + L.part2)};
+  const float* pend[2] = {nullptr, nullptr};
+  int pend_S[2] = {0, 0};
   const int64_t xs = L.rows * p.h;  // pair stride of a factor array
   hipError_t e;
   // slot c of the checkpoints as a state: W1 | W2 | W3, each [P, ...]
@@ -795,9 +800,12 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
         (e = lact::launch_bw_copy(dM, z, z, z, p.P, p.d, p.h, true, s)) != hipSuccess)
       return hip_fail(e, "cotangent init");
   }
-  // token-local VJP + weight contraction, added into cot
+  // token-local VJP + weight contraction; its split partials stay pending
+  // (added into cot by the next step kernel, or at the end)
+  // (ops_ready: the operand region already holds W's operands, written by the
+  // previous call with the same weights)
   auto tok_and_contract = [&](bool apply, const lact_state& W, const char* A, const char* B, const float* et,
-                              int64_t n, int64_t in_stride, char* dA, char* dB, float* de) -> int {
+                              int64_t n, int64_t in_stride, char* dA, char* dB, float* de, bool ops_ready) -> int {
     lact::BwTokArgs a{};
     a.A = A;
     a.B = B;
@@ -845,7 +853,8 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
       o.d = p.d;
       o.h = p.h;
       o.hi_only = !p.split;
-      if ((err = lact::launch_bw_ops(o, s)) != hipSuccess) return hip_fail(err, "backward operand kernel");
+      if (!ops_ready && (err = lact::launch_bw_ops(o, s)) != hipSuccess)
+        return hip_fail(err, "backward operand kernel");
       a.op = o.op;
       a.op_stride = o.op_stride;
     }
@@ -861,7 +870,7 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
     b.X2 = a.X2;
     b.X3 = a.X3;
     b.x_stride = xs;
-    b.partials = part;
+    b.partials = partbuf[apply ? 1 : 0];
     b.P = p.P;
     b.d = p.d;
     b.h = p.h;
@@ -880,8 +889,8 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
     if (err != hipSuccess) return hip_fail(err, "backward token kernel");
     PhaseTimer tc(7, s);
     if ((err = lact::launch_bw_contract(b, s)) != hipSuccess) return hip_fail(err, "backward contraction kernel");
-    if ((err = lact::launch_bw_reduce_add(cot, part, sp.S, 3 * hd, p.P, s)) != hipSuccess)
-      return hip_fail(err, "backward reduction kernel");
+    pend[apply ? 1 : 0] = b.partials;
+    pend_S[apply ? 1 : 0] = sp.S;
     return LACT_OK;
   };
   char* dQ = static_cast<char*>(out->dQ);
@@ -895,13 +904,17 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
     const float* ec = eta + cidx * chunk_kv;
     int rc;
     if (order == LACT_UPDATE_THEN_APPLY &&
-        (rc = tok_and_contract(true, Wout, Q + qo, dO + qo, nullptr, chunk_q, T_q * p.d, dQ + qo, nullptr, nullptr)))
+        (rc = tok_and_contract(true, Wout, Q + qo, dO + qo, nullptr, chunk_q, T_q * p.d, dQ + qo, nullptr, nullptr,
+                               false)))
       return rc;
     // the update's direction, recomputed: g (GD, Muon without momentum) or
     // the new momentum M_{c+1}; through Newton-Schulz for Muon
+    // (momentum without Newton-Schulz: the step kernel reads M_{c+1} from its
+    // checkpoint and runs the momentum VJP in the same pass)
+    const bool mom_in_step = p.momentum && !p.muon;
     if (p.momentum) {
       MatRef m1{Wout.M1, hd}, m2{Wout.M2, hd}, m3{Wout.M3, hd};
-      if ((e = lact::launch_bw_copy(gb, m1, m2, m3, p.P, p.d, p.h, true, s)) != hipSuccess)
+      if (!mom_in_step && (e = lact::launch_bw_copy(gb, m1, m2, m3, p.P, p.d, p.h, true, s)) != hipSuccess)
         return hip_fail(e, "momentum gather");
     } else {
       Splits sp;
@@ -942,9 +955,20 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
     lact::BwStepArgs sa{};
     refs(Win.W1, Win.W2, Win.W3, hd, sa.W_in);
     refs(Wout.W1, Wout.W2, Wout.W3, hd, sa.W_out);
-    sa.dir = direction;
+    sa.dir = mom_in_step ? nullptr : direction;
+    if (mom_in_step) {
+      refs(Wout.M1, Wout.M2, Wout.M3, hd, sa.dir_m);
+      sa.dM = dM;
+      sa.pc = pc;
+      sa.beta = c->beta;
+    }
     sa.cot = cot;
-    sa.ddir = ddir;
+    sa.ddir = (p.momentum || p.muon) ? ddir : pc;
+    for (int q = 0; q < 2; ++q) {
+      sa.pend[q] = pend[q];
+      sa.pend_S[q] = pend_S[q];
+      pend[q] = nullptr;
+    }
     sa.step = c->step;
     sa.norm_eps = c->norm_eps;
     sa.P = p.P;
@@ -972,20 +996,23 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
       if ((e = lact::launch_bw_ns(na, s)) != hipSuccess) return hip_fail(e, "Newton-Schulz VJP kernel");
       t_in = tb;
     }
-    if (p.momentum) {
-      if ((e = lact::launch_bw_momentum(t_in, dM, pc, c->beta, per, s)) != hipSuccess)
-        return hip_fail(e, "momentum VJP kernel");
-    } else if (!p.muon) {
-      if ((e = hipMemcpyAsync(pc, ddir, sizeof(float) * per, hipMemcpyDeviceToDevice, s)) != hipSuccess)
-        return hip_fail(e, "cotangent copy");
-    }
+    // (plain GD: the step kernel wrote the direction's cotangent into pc itself)
+    if (p.momentum && !mom_in_step &&
+        (e = lact::launch_bw_momentum(t_in, dM, pc, c->beta, per, s)) != hipSuccess)
+      return hip_fail(e, "momentum VJP kernel");
     // through the chunk gradient
     if ((rc = tok_and_contract(false, Win, K + ko, V + ko, ec, chunk_kv, T_kv * p.d, dK + ko, dV + ko,
-                               out->deta + cidx * chunk_kv)))
+                               out->deta + cidx * chunk_kv, false)))
       return rc;
+    // (the chunk gradient's call has just converted W_in, the read's weights here)
     if (order == LACT_APPLY_THEN_UPDATE &&
-        (rc = tok_and_contract(true, Win, Q + qo, dO + qo, nullptr, chunk_q, T_q * p.d, dQ + qo, nullptr, nullptr)))
+        (rc = tok_and_contract(true, Win, Q + qo, dO + qo, nullptr, chunk_q, T_q * p.d, dQ + qo, nullptr, nullptr,
+                               true)))
       return rc;
+  }
+  for (int q = 0; q < 2; ++q) {
+    if (pend[q] != nullptr && (e = lact::launch_bw_reduce_add(cot, pend[q], pend_S[q], 3 * hd, p.P, s)) != hipSuccess)
+      return hip_fail(e, "backward reduction kernel");
   }
   MatRef o1{out->dW1, hd}, o2{out->dW2, hd}, o3{out->dW3, hd};
   if ((e = lact::launch_bw_copy(cot, o1, o2, o3, p.P, p.d, p.h, false, s)) != hipSuccess)

@@ -177,9 +177,21 @@ struct BwContractArgs {  // X1^T A, (b B)^T X2, X3^T A over tokens, b = -eta or 
 };
 struct BwStepArgs {
   MatRef W_in[3], W_out[3];  // W1, W2, W3 before and after the update
-  const float* dir;          // [P, 3hd] direction of the update
+  const float* dir;          // [P, 3hd] direction of the update (NULL: dir_m)
+  MatRef dir_m[3];           // the direction as W1, W2, W3 matrices (the momentum's checkpoint)
   float* cot;                // [P, 3hd] cotangent of W_out in, of W_in (direct path) out
+  // split partials [P, S, 3hd] of contractions not yet added into cot: the
+  // incoming cotangent is (cot + sum pend[0]) + sum pend[1], each sum in split
+  // order (NULL: none)
+  const float* pend[2];
+  int pend_S[2];
   float* ddir;               // [P, 3hd] cotangent of the direction
+  // momentum without Newton-Schulz, when dM is set: the momentum VJP in the
+  // same pass (v = cotangent of the direction + dM; pc = v; dM = beta v),
+  // ddir is not written
+  float* dM;
+  float* pc;
+  float beta;
   float step, norm_eps;
   int P, d, h;
 };

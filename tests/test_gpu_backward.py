@@ -131,3 +131,19 @@ def test_backward_lm_full_size_sampled():
     assert not bad, bad
     for n in NAMES:
         assert np.all(np.isfinite(got[n])), n
+
+
+@pytest.mark.parametrize("name", ["bw-posed-bf16", "bw-lm-bf16"])
+def test_backward_repeat_is_bitwise_equal(name):
+    """The matrix-core contraction sums its token splits in the workgroup that
+    finishes last; the sum runs in split order whichever that is, so two runs
+    give the same bits."""
+    w = next(c for c in CASES if c.name == name)
+    G.say(f"case {w.name} twice")
+    st = S.gen_weights(w)
+    x = S.gen_inputs(w)
+    dO, dWf = cotangent_inputs(w)
+    a = run_backward_gpu(w, x, st, dO, dWf)
+    b = run_backward_gpu(w, x, st, dO, dWf)
+    for n in NAMES:
+        assert np.array_equal(a[n], b[n]), n
