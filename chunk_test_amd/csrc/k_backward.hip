@@ -609,6 +609,171 @@ __device__ __forceinline__ void wg_mm(int M, int N, const int (&K)[NTERM], const
   __syncthreads();  // every element of C written (global, visible to the workgroup)
 }
 
+// The same products with every fp32 operand value x split into bf16 parts
+// hi = bf16(x), lo = bf16(x - hi) and the three products hi hi + hi lo + lo hi
+// on v_mfma_f32_32x32x16_bf16 (fp32 sums; the dropped lo lo term is ~2^-16 of
+// a product): about five times the fp32 matrix-core rate.  LDS holds 32 k
+// values per operand row as bf16 (hi and lo arrays), rows of 80 bytes, so the
+// 16-byte operand reads of 16 consecutive rows fall into distinct banks.
+// Each thread stages eight k values of one operand row per task (one task of
+// the M x 32 chunk of op(P), two of the NB x 32 chunk of op(Q)), loading
+// along whichever index is contiguous in memory.
+typedef __attribute__((ext_vector_type(8))) __bf16 nsb_bf16x8;
+typedef __attribute__((ext_vector_type(4))) float nsb_f32x4;
+constexpr int kBRow = 40;                   // bf16 per LDS row (32 + 8 padding)
+constexpr int kBP = 128 * kBRow;            // bf16 of one P part (hi or lo)
+constexpr int kBQ = kNB * kBRow;            // bf16 of one Q part
+constexpr int kBBuf = 2 * kBP + 2 * kBQ;    // one stage: P hi, P lo, Q hi, Q lo
+constexpr int kNSBfLds = 2 * kBBuf * 2;     // bytes, two stages
+constexpr int kNSF32Lds = (2 * 32 * 129 + 2 * 32 * (kNB + 1)) * 4;
+
+__device__ __forceinline__ void nsb_split(const float (&v)[8], nsb_bf16x8& hi, nsb_bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    hi[e] = static_cast<__bf16>(v[e]);
+    lo[e] = static_cast<__bf16>(v[e] - static_cast<float>(hi[e]));
+  }
+}
+
+// eight values of a matrix starting at src with element stride st (16-byte
+// aligned vector loads where st == 1)
+__device__ __forceinline__ void nsb_load8(const float* src, int st, float (&v)[8]) {
+  if (st == 1) {
+    const nsb_f32x4 a = *reinterpret_cast<const nsb_f32x4*>(src);
+    const nsb_f32x4 b = *reinterpret_cast<const nsb_f32x4*>(src + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = a[e];
+      v[4 + e] = b[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = src[static_cast<int64_t>(e) * st];
+  }
+}
+
+template <int NTERM, class Epi>
+__device__ __forceinline__ void wg_mm_bf(int M, int N, const int (&K)[NTERM], const MOp (&P)[NTERM],
+                                         const MOp (&Q)[NTERM], uint16_t* lds, Epi epi) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 5, ln = lane & 31;
+  for (int nb = 0; nb < N; nb += kNB) {
+    const int NB = min(kNB, N - nb);
+    const int ntl = NB / 32, tiles = (M / 32) * ntl;  // <= 32: at most four per wave
+    ns_f32x16 acc[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
+    }
+#pragma unroll 1
+    for (int t = 0; t < NTERM; ++t) {
+      const MOp p = P[t], q = Q[t];
+      // tasks: (row, octet of k); rows follow the contiguous index when k is not it
+      int pi, po, qj[2], qo[2];
+      if (p.cs == 1) {
+        pi = tid >> 2;
+        po = tid & 3;
+      } else {
+        pi = tid % M;
+        po = tid / M;
+      }
+      const bool pv = tid < 4 * M;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int task = tid + kNSThreads * u;
+        if (q.rs == 1) {
+          qj[u] = task >> 2;
+          qo[u] = task & 3;
+        } else {
+          qj[u] = task % NB;
+          qo[u] = task / NB;
+        }
+      }
+      float vp[8], vq[2][8];
+      auto load = [&](int kc) {
+        if (pv) nsb_load8(p.p + static_cast<int64_t>(pi) * p.rs + static_cast<int64_t>(kc + 8 * po) * p.cs, p.cs, vp);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          if (tid + kNSThreads * u < 4 * NB)
+            nsb_load8(q.p + static_cast<int64_t>(kc + 8 * qo[u]) * q.rs + static_cast<int64_t>(nb + qj[u]) * q.cs,
+                      q.rs, vq[u]);
+        }
+      };
+      auto store = [&](int b) {
+        uint16_t* base = lds + b * kBBuf;
+        nsb_bf16x8 hi, lo;
+        if (pv) {
+          nsb_split(vp, hi, lo);
+          *reinterpret_cast<nsb_bf16x8*>(base + pi * kBRow + 8 * po) = hi;
+          *reinterpret_cast<nsb_bf16x8*>(base + kBP + pi * kBRow + 8 * po) = lo;
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          if (tid + kNSThreads * u < 4 * NB) {
+            nsb_split(vq[u], hi, lo);
+            *reinterpret_cast<nsb_bf16x8*>(base + 2 * kBP + qj[u] * kBRow + 8 * qo[u]) = hi;
+            *reinterpret_cast<nsb_bf16x8*>(base + 2 * kBP + kBQ + qj[u] * kBRow + 8 * qo[u]) = lo;
+          }
+        }
+      };
+      const int nc = K[t] / 32;
+      load(0);
+      __syncthreads();  // the previous readers of both buffers are done
+      store(0);
+      __syncthreads();
+      for (int c = 0; c < nc; ++c) {
+        const int b = c & 1;
+        if (c + 1 < nc) load(32 * (c + 1));
+        const uint16_t* base = lds + b * kBBuf;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int tt = wave + 8 * u;
+            if (tt < tiles) {
+              const int ti = tt / ntl, tj = tt % ntl;
+              const int pa = (32 * ti + ln) * kBRow + 16 * ks + 8 * g;
+              const int qa = 2 * kBP + (32 * tj + ln) * kBRow + 16 * ks + 8 * g;
+              const nsb_bf16x8 ah = *reinterpret_cast<const nsb_bf16x8*>(base + pa);
+              const nsb_bf16x8 al = *reinterpret_cast<const nsb_bf16x8*>(base + kBP + pa);
+              const nsb_bf16x8 bh = *reinterpret_cast<const nsb_bf16x8*>(base + qa);
+              const nsb_bf16x8 bl = *reinterpret_cast<const nsb_bf16x8*>(base + kBQ + qa);
+              acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[u], 0, 0, 0);
+              acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[u], 0, 0, 0);
+              acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[u], 0, 0, 0);
+            }
+          }
+        }
+        if (c + 1 < nc) store(b ^ 1);
+        __syncthreads();
+      }
+    }
+    // acc[u][r] = C[32 ti + 8 (r / 4) + 4 g + r % 4][nb + 32 tj + ln]
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int tt = wave + 8 * u;
+      if (tt < tiles) {
+        const int ti = tt / ntl, tj = tt % ntl;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) epi(32 * ti + 8 * (r >> 2) + 4 * g + (r & 3), nb + 32 * tj + ln, acc[u][r]);
+      }
+    }
+  }
+  __syncthreads();  // every element of C written (global, visible to the workgroup)
+}
+
+// the products of one Newton-Schulz kernel: fp32 or split-bf16 matrix cores
+template <bool BF, int NTERM, class Epi>
+__device__ __forceinline__ void ns_mm(int M, int N, const int (&K)[NTERM], const MOp (&P)[NTERM],
+                                     const MOp (&Q)[NTERM], unsigned char* lds, Epi epi) {
+  if constexpr (BF) {
+    wg_mm_bf(M, N, K, P, Q, reinterpret_cast<uint16_t*>(lds), epi);
+  } else {
+    float* f = reinterpret_cast<float*>(lds);
+    wg_mm(M, N, K, P, Q, f, f + 2 * 32 * 129, epi);
+  }
+}
+
 // One matrix's geometry and scratch (floats): iterates X_0 .. X_I (s l each),
 // dY and dX (s l), A_0 .. A_{I-1}, B_0 .. B_{I-1} (s s each), dB, dA (s s).
 struct NSMat {
@@ -654,9 +819,9 @@ __device__ __forceinline__ float ns_block_sum(float v, float* red) {
   return r;
 }
 
+template <bool BF>
 __global__ __launch_bounds__(kNSThreads) void k_bw_ns_fwd(BwNSArgs a) {
-  __shared__ float Ps[2 * 32 * 129];
-  __shared__ float Qs[2 * 32 * (kNB + 1)];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[BF ? kNSBfLds : kNSF32Lds];
   __shared__ float red[kNSThreads];
   const NSMat m(a);
   const int tid = threadIdx.x;
@@ -683,17 +848,17 @@ __global__ __launch_bounds__(kNSThreads) void k_bw_ns_fwd(BwNSArgs a) {
     {  // A = X X^T
       const int K[1] = {l};
       const MOp P[1] = {{X, l, 1}}, Q[1] = {{X, 1, l}};
-      wg_mm(s, s, K, P, Q, Ps, Qs, [&](int i, int j, float v) { A[i * s + j] = v; });
+      ns_mm<BF>(s, s, K, P, Q, lds, [&](int i, int j, float v) { A[i * s + j] = v; });
     }
     {  // B = b A + c A A
       const int K[1] = {s};
       const MOp P[1] = {{A, s, 1}}, Q[1] = {{A, s, 1}};
-      wg_mm(s, s, K, P, Q, Ps, Qs, [&](int i, int j, float v) { B[i * s + j] = cb * A[i * s + j] + cc * v; });
+      ns_mm<BF>(s, s, K, P, Q, lds, [&](int i, int j, float v) { B[i * s + j] = cb * A[i * s + j] + cc * v; });
     }
     {  // X <- a X + B X
       const int K[1] = {s};
       const MOp P[1] = {{B, s, 1}}, Q[1] = {{X, l, 1}};
-      wg_mm(s, l, K, P, Q, Ps, Qs,
+      ns_mm<BF>(s, l, K, P, Q, lds,
             [&](int i, int j, float v) { Xn[static_cast<int64_t>(i) * l + j] = ca * X[static_cast<int64_t>(i) * l + j] + v; });
     }
   }
@@ -704,9 +869,9 @@ __global__ __launch_bounds__(kNSThreads) void k_bw_ns_fwd(BwNSArgs a) {
   }
 }
 
+template <bool BF>
 __global__ __launch_bounds__(kNSThreads) void k_bw_ns(BwNSArgs a) {
-  __shared__ float Ps[2 * 32 * 129];
-  __shared__ float Qs[2 * 32 * (kNB + 1)];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[BF ? kNSBfLds : kNSF32Lds];
   __shared__ float red[kNSThreads];
   const NSMat m(a);
   const int tid = threadIdx.x;
@@ -729,17 +894,17 @@ __global__ __launch_bounds__(kNSThreads) void k_bw_ns(BwNSArgs a) {
     {  // dB = dY X^T
       const int K[1] = {l};
       const MOp P[1] = {{dY, l, 1}}, Q[1] = {{X, 1, l}};
-      wg_mm(s, s, K, P, Q, Ps, Qs, [&](int i, int j, float v) { m.dB[i * s + j] = v; });
+      ns_mm<BF>(s, s, K, P, Q, lds, [&](int i, int j, float v) { m.dB[i * s + j] = v; });
     }
     {  // dA = b dB + c (dB A^T + A^T dB)
       const int K[2] = {s, s};
       const MOp P[2] = {{m.dB, s, 1}, {A, 1, s}}, Q[2] = {{A, 1, s}, {m.dB, s, 1}};
-      wg_mm(s, s, K, P, Q, Ps, Qs, [&](int i, int j, float v) { m.dA[i * s + j] = cb * m.dB[i * s + j] + cc * v; });
+      ns_mm<BF>(s, s, K, P, Q, lds, [&](int i, int j, float v) { m.dA[i * s + j] = cb * m.dB[i * s + j] + cc * v; });
     }
     {  // dX = a dY + B^T dY + dA X + dA^T X
       const int K[3] = {s, s, s};
       const MOp P[3] = {{B, 1, s}, {m.dA, s, 1}, {m.dA, 1, s}}, Q[3] = {{dY, l, 1}, {X, l, 1}, {X, l, 1}};
-      wg_mm(s, l, K, P, Q, Ps, Qs, [&](int i, int j, float v) {
+      ns_mm<BF>(s, l, K, P, Q, lds, [&](int i, int j, float v) {
         dXn[static_cast<int64_t>(i) * l + j] = ca * dY[static_cast<int64_t>(i) * l + j] + v;
       });
     }
@@ -856,13 +1021,19 @@ int64_t bw_ns_floats_per_matrix(int d, int h, int iters) {
 
 hipError_t launch_bw_ns(const BwNSArgs& a, hipStream_t s) {
   if (a.d % 32 != 0 || a.h % 32 != 0 || (a.d < a.h ? a.d : a.h) > 128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_bw_ns, dim3(3 * a.P), dim3(kNSThreads), 0, s, a);
+  if (a.bf16_split)
+    hipLaunchKernelGGL(k_bw_ns<true>, dim3(3 * a.P), dim3(kNSThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_bw_ns<false>, dim3(3 * a.P), dim3(kNSThreads), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_bw_ns_fwd(const BwNSArgs& a, hipStream_t s) {
   if (a.d % 32 != 0 || a.h % 32 != 0 || (a.d < a.h ? a.d : a.h) > 128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_bw_ns_fwd, dim3(3 * a.P), dim3(kNSThreads), 0, s, a);
+  if (a.bf16_split)
+    hipLaunchKernelGGL(k_bw_ns_fwd<true>, dim3(3 * a.P), dim3(kNSThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_bw_ns_fwd<false>, dim3(3 * a.P), dim3(kNSThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -947,6 +947,7 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
       nf.b = c->ns_b;
       nf.c = c->ns_c;
       nf.eps = c->ns_eps;
+      nf.bf16_split = p.bf16;  // (bf16 I/O: split-bf16 products; fp32 I/O: fp32 products)
       PhaseTimer tn(8, s);
       if ((e = lact::launch_bw_ns_fwd(nf, s)) != hipSuccess) return hip_fail(e, "Newton-Schulz kernel");
       direction = dirb;
@@ -992,6 +993,7 @@ int run_backward(const lact_config* c, const Plan& p, const lact_state* st0, con
       na.b = c->ns_b;
       na.c = c->ns_c;
       na.eps = c->ns_eps;
+      na.bf16_split = p.bf16;  // (bf16 I/O: split-bf16 products; fp32 I/O: fp32 products)
       PhaseTimer tn(8, s);
       if ((e = lact::launch_bw_ns(na, s)) != hipSuccess) return hip_fail(e, "Newton-Schulz VJP kernel");
       t_in = tb;

@@ -203,6 +203,7 @@ struct BwNSArgs {
   int64_t per_mat;
   int P, d, h, iters;
   float a, b, c, eps;
+  int bf16_split;   // products on bf16 matrix cores with hi + lo operands (else fp32 matrix cores)
 };
 bool backward_shape_ok(int d, int h);
 hipError_t launch_bw_tok(const BwTokArgs& a, bool apply, hipStream_t s);
