@@ -465,8 +465,9 @@ __global__ __launch_bounds__(kThreads) void k_bw_momentum(const float* t, float*
 //             dX_k = a dY + B_k^T dY + (dA + dA^T) X_k;
 //   then dG = dX_0 / (n + eps) - (<dX_0, G> / (n + eps)^2) G / n.
 // Every product runs on fp32 MFMA (v_mfma_f32_32x32x2_f32: products and sums
-// in fp32), 32 x 32 output tiles spread over the eight wavefronts, the
-// operands staged through LDS 32 k values at a time.
+// in fp32; fp32 I/O) or as three bf16 MFMAs on hi + lo parts (wg_mm_bf; bf16
+// I/O), 32 x 32 output tiles spread over the eight wavefronts, the operands
+// staged through LDS 32 k values at a time.
 // ---------------------------------------------------------------------------
 constexpr int kNSThreads = 512;
 constexpr int kNB = 256;  // output columns per block of a product
