@@ -654,8 +654,9 @@ void k_bw_grad_mfma(BwTokArgs a) {
   constexpr int NPART = SPLIT ? 12 : 6;
   constexpr int WTILE6 = NPART * WHALF;  // W1, W3, W2^T, P1, P3, P2^T: hi and lo (hi only without SPLIT)
   __shared__ __attribute__((aligned(16))) unsigned char lds[WTILE6];
-  // LDS operand reads grouped ahead of their products (not in the split
-  // d = 128 kernel, which has no registers left for them)
+  // the token-side products' LDS operand reads grouped ahead of their
+  // products too (not in the split d = 128 kernel, which has no registers
+  // left for them)
   constexpr bool GROUP = !(SPLIT && D == 128);
   // XCD-aware order: block ids congruent mod 8 run on one XCD, and the
   // token tiles of a pair take consecutive slots of one XCD's share, so the
@@ -751,33 +752,20 @@ void k_bw_grad_mfma(BwTokArgs a) {
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if constexpr (GROUP) {
-        // (a k-step's weight reads are issued together, ahead of its
-        // products: with one wavefront per SIMD nothing else hides their latency)
-        bf16x8_t wh[6], wl[6];
+      // (a k-step's weight reads are issued together, ahead of its products:
+      // with one wavefront per SIMD nothing else hides their latency)
+      bf16x8_t wh[6], wl[6];
 #pragma unroll
-        for (int m = 0; m < 6; ++m) {
-          wh[m] = *reinterpret_cast<const bf16x8_t*>(part(m, 0) + ak_off[ks]);
-          if constexpr (SPLIT) wl[m] = *reinterpret_cast<const bf16x8_t*>(part(m, 1) + ak_off[ks]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int m = 0; m < 6; ++m) {
+        wh[m] = *reinterpret_cast<const bf16x8_t*>(part(m, 0) + ak_off[ks]);
+        if constexpr (SPLIT) wl[m] = *reinterpret_cast<const bf16x8_t*>(part(m, 1) + ak_off[ks]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int m = 0; m < 6; ++m) {
-          const bf16x8_t bo = (m == 2 || m == 5) ? vop[ks] : kop[ks];
-          c[m] = mfma32(wh[m], bo, c[m]);
-          if constexpr (SPLIT) c[m] = mfma32(wl[m], bo, c[m]);
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < 6; ++m) {
-          const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(part(m, 0) + ak_off[ks]);
-          const bf16x8_t bo = (m == 2 || m == 5) ? vop[ks] : kop[ks];
-          c[m] = mfma32(ah, bo, c[m]);
-          if constexpr (SPLIT) {
-            const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(part(m, 1) + ak_off[ks]);
-            c[m] = mfma32(al, bo, c[m]);
-          }
-        }
+      for (int m = 0; m < 6; ++m) {
+        const bf16x8_t bo = (m == 2 || m == 5) ? vop[ks] : kop[ks];
+        c[m] = mfma32(wh[m], bo, c[m]);
+        if constexpr (SPLIT) c[m] = mfma32(wl[m], bo, c[m]);
       }
     }
     // element math (fp32)
