@@ -149,13 +149,19 @@ __device__ __forceinline__ int swz(int r) {
 
 template <int QT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(QT == 1 ? 2 : 1, QT == 1 ? 2 : 1)))
-void k_window_attn_mfma(WindowArgs a) {
+void k_window_attn_mfma(WindowArgs a, int nq) {
   using namespace mf;
   constexpr int QWV = 32 * QT;     // queries per wavefront
   constexpr int QWG = 4 * QWV;     // queries per workgroup
   __shared__ __attribute__((aligned(16))) unsigned char lds[4 * TILE];  // K[2], V[2]
-  const int pair = blockIdx.y;
-  const int64_t q0 = static_cast<int64_t>(blockIdx.x) * QWG;
+  // XCD-aware order: block ids congruent mod 8 run on one XCD, and each
+  // XCD takes a contiguous run of (pair, query block)s in order, so the
+  // neighbouring query blocks that read the same keys and values share its L2
+  const int nblk = gridDim.x;  // a multiple of 8
+  const int ob = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
+  if (ob >= nq * a.P) return;
+  const int pair = ob / nq;
+  const int64_t q0 = static_cast<int64_t>(ob % nq) * QWG;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -397,8 +403,11 @@ hipError_t launch_window_attn(const WindowArgs& a, hipStream_t s) {
                          reinterpret_cast<uintptr_t>(a.V) | reinterpret_cast<uintptr_t>(a.O)) & 15) == 0;
   if (a.bf16 && a.d == mf::D && aligned && a.T * a.d < (int64_t(1) << 31)) {
     constexpr int QT = 1;  // query tiles per wavefront
-    const dim3 grid(static_cast<unsigned>((a.T + 128 * QT - 1) / (128 * QT)), a.P);
-    hipLaunchKernelGGL(k_window_attn_mfma<QT>, grid, dim3(kThreads), 0, s, a);
+    const int64_t nq = (a.T + 128 * QT - 1) / (128 * QT);
+    const int64_t blocks = (nq * a.P + 7) / 8 * 8;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_window_attn_mfma<QT>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, s, a,
+                       static_cast<int>(nq));
     return hipGetLastError();
   }
   switch (a.d) {
