@@ -242,6 +242,8 @@ def main():
                     help="variant: updated rows to unit length (default) or kept at their length")
     ap.add_argument("--eta-per-matrix", action="store_true",
                     help="variant: a learning rate per token and matrix (W1, W2, W3)")
+    ap.add_argument("--products", default=None, choices=("auto", "bf16", "split"),
+                    help="product precision of bf16 mode (default: the workload's own)")
     ap.add_argument("--mode", default="forward", choices=("forward", "backward", "block"),
                     help="forward: the layer (default); backward: lact_chunked_backward on the "
                          "same workload; block: window attention + the layer on shared Q, K, V")
@@ -271,6 +273,8 @@ def main():
         w = w.replace(name=w.name + ("-keep" if args.norm == "keep" else "")
                       + ("-eta3" if args.eta_per_matrix else ""),
                       norm=args.norm, eta_per_matrix=args.eta_per_matrix)
+    if args.products is not None and args.products != w.products:
+        w = w.replace(name=w.name + "-" + args.products, products=args.products)
     log(f"[bench] workload {w.name}: generating inputs")
     st = S.gen_weights(w)
     x = S.gen_inputs(w)

@@ -1,4 +1,5 @@
-// Chunk gradient of the LaCT layer for d = 64 on bf16 MFMA (gfx950).
+// Chunk gradient of the LaCT layer for d = 64 on bf16 MFMA (gfx950), with
+// plain bf16 products or with near-fp32 "split" products.
 //
 // For one (pair, token split, 128-unit hidden slice) a workgroup of four
 // wavefronts (32 hidden units each) sums, over the split's tokens i,
@@ -25,6 +26,14 @@
 //   (token order inside an operand is the same permutation on both sides).
 //   The token-side operands (K, V with tokens along k) come from the
 //   row-major tiles through LDS transpose reads.
+//
+// Split products: keys and values are exact bf16 inputs, so only the other
+// operand of every product is split, x = x_hi + x_lo (both bf16), and each
+// product is two MFMAs (~16 significant bits per operand, twice the matrix
+// work): K W^T = K W_hi^T + K W_lo^T with both parts of W in registers, and
+// the contractions take the SwiGLU outputs as hi and lo parts.  That needs
+// more registers than two wavefronts per SIMD leave, so the split kernel
+// runs one workgroup per CU.
 #include "lact_device.h"
 #include "lact_internal.h"
 
@@ -80,10 +89,16 @@ __device__ __forceinline__ f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// lo bf16 part of a float given its hi part (the rounded remainder)
+__device__ __forceinline__ __bf16 lo_bf16(float x, __bf16 hi) {
+  return static_cast<__bf16>(x - static_cast<float>(hi));
+}
+
 // PM: a learning rate per token and matrix (rows of rates for W1, W2, W3,
-// a.eta_mat elements apart); otherwise one rate per token.
-template <bool PM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// a.eta_mat elements apart); otherwise one rate per token.  SPLIT: split
+// products (one wavefront per SIMD).
+template <bool PM, bool SPLIT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SPLIT ? 1 : 2, SPLIT ? 1 : 2)))
 void k_grad_d64(GradArgs a, int hsl, int nbase) {
   __shared__ __attribute__((aligned(16))) unsigned char buf0[buf_bytes<PM>()];
   __shared__ __attribute__((aligned(16))) unsigned char buf1[buf_bytes<PM>()];
@@ -110,8 +125,9 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
   const int n0 = hs * kHidPerWG + wave * kHidPerWave;  // this wave's hidden units
 
   // ---- W^T operands of the projections: lane holds hidden unit n0 + ln,
-  // features 16 ks + 8 g .. +7
+  // features 16 ks + 8 g .. +7 (with split products also the lo parts)
   bf16x8_t w1b[KS], w3b[KS], w2b[KS];
+  bf16x8_t w1l[SPLIT ? KS : 1], w3l[SPLIT ? KS : 1], w2l[SPLIT ? KS : 1];
   {
     const float* W1 = a.W1 + pair * hd + static_cast<int64_t>(n0 + ln) * D;
     const float* W3 = a.W3 + pair * hd + static_cast<int64_t>(n0 + ln) * D;
@@ -121,9 +137,15 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int dd = 16 * ks + 8 * g + i;
-        w1b[ks][i] = static_cast<__bf16>(kNegLog2e * W1[dd]);
-        w3b[ks][i] = static_cast<__bf16>(W3[dd]);
-        w2b[ks][i] = static_cast<__bf16>(W2[static_cast<int64_t>(dd) * h]);
+        const float x1 = kNegLog2e * W1[dd], x3 = W3[dd], x2 = W2[static_cast<int64_t>(dd) * h];
+        w1b[ks][i] = static_cast<__bf16>(x1);
+        w3b[ks][i] = static_cast<__bf16>(x3);
+        w2b[ks][i] = static_cast<__bf16>(x2);
+        if constexpr (SPLIT) {
+          w1l[ks][i] = lo_bf16(x1, w1b[ks][i]);
+          w3l[ks][i] = lo_bf16(x3, w3b[ks][i]);
+          w2l[ks][i] = lo_bf16(x2, w2b[ks][i]);
+        }
       }
     }
   }
@@ -258,6 +280,11 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
         c1 = mfma32(ak[ks], w1b[ks], c1);
         c3 = mfma32(ak[ks], w3b[ks], c3);
         cg = mfma32(av[ks], w2b[ks], cg);
+        if constexpr (SPLIT) {
+          c1 = mfma32(ak[ks], w1l[ks], c1);
+          c3 = mfma32(ak[ks], w3l[ks], c3);
+          cg = mfma32(av[ks], w2l[ks], cg);
+        }
       }
       // SwiGLU forward and backward, one 16-token half at a time (operand
       // slot i <-> token 16 s + 8 (i / 4) + 4 g + i % 4 of the sub-tile).
@@ -299,7 +326,7 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
           bk[nt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(kt[0], kt[1], 0, 1, 2, 3, 4, 5, 6, 7));
           bv[nt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(vt[0], vt[1], 0, 1, 2, 3, 4, 5, 6, 7));
         }
-        bf16x8_t pg, pd1, pd3;
+        bf16x8_t pg, pd1, pd3, lg, l1, l3;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int r = 8 * s + i;
@@ -312,16 +339,27 @@ void k_grad_d64(GradArgs a, int hsl, int nbase) {
           const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(z));
           const float act = z * sg;
           const float gs = act * h3;
-          pg[i] = static_cast<__bf16>(ne * gs);
-          pd3[i] = static_cast<__bf16>(dg3 * act);
           const float t = fmaf(h3, kNegLog2e, -gs);
-          pd1[i] = static_cast<__bf16>(dg1 * fmaf(sg, t, gs));
+          const float vg = ne * gs, v3 = dg3 * act, v1 = dg1 * fmaf(sg, t, gs);
+          pg[i] = static_cast<__bf16>(vg);
+          pd3[i] = static_cast<__bf16>(v3);
+          pd1[i] = static_cast<__bf16>(v1);
+          if constexpr (SPLIT) {
+            lg[i] = lo_bf16(vg, pg[i]);
+            l3[i] = lo_bf16(v3, pd3[i]);
+            l1[i] = lo_bf16(v1, pd1[i]);
+          }
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           aW1[nt] = mfma32(pd1, bk[nt], aW1[nt]);
           aW3[nt] = mfma32(pd3, bk[nt], aW3[nt]);
           aW2[nt] = mfma32(bv[nt], pg, aW2[nt]);
+          if constexpr (SPLIT) {
+            aW1[nt] = mfma32(l1, bk[nt], aW1[nt]);
+            aW3[nt] = mfma32(l3, bk[nt], aW3[nt]);
+            aW2[nt] = mfma32(bv[nt], lg, aW2[nt]);
+          }
         }
       }
     }
@@ -355,15 +393,20 @@ bool grad_d64_shape_ok(int d, int h) {
   return d == D && h % kHidPerWG == 0 && h >= kHidPerWG && h <= 1024;
 }
 
-hipError_t launch_grad_d64(const GradArgs& a, hipStream_t s) {
+hipError_t launch_grad_d64(const GradArgs& a, bool split, hipStream_t s) {
   if (a.d != D) return hipErrorInvalidValue;
   const int hsl = a.h / kHidPerWG;
   const int nbase = a.S * a.P;
   const int blocks = ((nbase + 7) / 8) * 8 * hsl;
-  if (a.eta_mat != 0) {
-    hipLaunchKernelGGL(k_grad_d64<true>, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  const bool pm = a.eta_mat != 0;
+  if (split && pm) {
+    hipLaunchKernelGGL((k_grad_d64<true, true>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  } else if (split) {
+    hipLaunchKernelGGL((k_grad_d64<false, true>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  } else if (pm) {
+    hipLaunchKernelGGL((k_grad_d64<true, false>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
   } else {
-    hipLaunchKernelGGL(k_grad_d64<false>, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+    hipLaunchKernelGGL((k_grad_d64<false, false>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
   }
   return hipGetLastError();
 }

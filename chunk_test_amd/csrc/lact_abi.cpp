@@ -133,7 +133,8 @@ SplitRule linear_rule(const Plan& p) { return {static_cast<int64_t>(p.P), 1024, 
 
 // Which chunk-gradient kernel runs.  The MFMA kernels read 16-byte rows with
 // 32-bit offsets inside a pair's rows: they need aligned K, V and strides and
-// n d < 2^31.  Split products run on MFMA at d = 128 only.
+// n d < 2^31.  With split products the d = 64 kernel runs one workgroup per
+// CU (one wavefront per SIMD).
 enum class GradKind { Generic, D64, D128 };
 
 // Above this many token splits the Muon tail's partial sum runs as a
@@ -149,7 +150,7 @@ struct GradChoice {
 GradChoice grad_choice(const Plan& p, bool aligned, int64_t n) {
   const bool fits = aligned && n * p.d < (static_cast<int64_t>(1) << 31);
   if (p.mfma && fits) {
-    if (!p.split && lact::grad_d64_shape_ok(p.d, p.h)) return {GradKind::D64, 128, 2};
+    if (lact::grad_d64_shape_ok(p.d, p.h)) return {GradKind::D64, 128, p.split ? 1 : 2};
     if (lact::grad_d128_shape_ok(p.d, p.h))
       return {GradKind::D128, lact::grad_d128_stage_tokens(p.split), 1};
   }
@@ -391,7 +392,7 @@ int launch_gradient(const lact_config* c, const Plan& p, const lact_state* st, c
   g.bf16 = p.bf16;
   hipError_t e;
   switch (gk.kind) {
-    case GradKind::D64: e = lact::launch_grad_d64(g, s); break;
+    case GradKind::D64: e = lact::launch_grad_d64(g, p.split, s); break;
     case GradKind::D128: e = lact::launch_grad_d128(g, p.split, s); break;
     default: e = lact::launch_grad_simple(g, s); break;
   }

@@ -253,7 +253,7 @@ bool simple_shape_ok(int d, int h);
 
 // ---- bf16 MFMA kernels (gfx950) ----
 bool grad_d64_shape_ok(int d, int h);  // d = 64, LDS-DMA staging
-hipError_t launch_grad_d64(const GradArgs& a, hipStream_t s);
+hipError_t launch_grad_d64(const GradArgs& a, bool split, hipStream_t s);
 bool grad_d128_shape_ok(int d, int h);  // d = 128, LDS-DMA staging, bf16 or split products
 int grad_d128_stage_tokens(bool split);
 hipError_t launch_grad_d128(const GradArgs& a, bool split, hipStream_t s);

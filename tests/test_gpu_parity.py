@@ -53,6 +53,15 @@ SMALL_CASES = [
     # bf16, two 128-unit hidden slices at d = 64; 1000 queries (two query-read
     # workgroups of several pipelined 128-query steps, the last one ragged)
     small("posed", name="posed-h256", H=2, h=256, T_kv=5000, T_q=1000, chunk_kv=5000, chunk_q=1000),
+    # split products at d = 64 (one wavefront per SIMD): one posed-shape chunk, a
+    # ragged eight-chunk Muon scan (auto keeps the products split over more than four
+    # Muon chunks) and a rate per token and matrix
+    small("posed", name="posed-split", H=2, T_kv=16384, T_q=512, chunk_kv=16384, chunk_q=512,
+          products="split"),
+    small("posed", name="posed-split-scan", H=2, T_kv=8000, T_q=400, chunk_kv=1000, chunk_q=50,
+          products="auto"),
+    small("posed", name="posed-split-eta3", H=2, T_kv=3000, T_q=210, chunk_kv=1000, chunk_q=70,
+          opt="momentum", beta=0.9, eta_per_matrix=True, products="split"),
     # bf16 Muon with momentum at d = 64 (the Muon tail's momentum buffer)
     small("posed", name="posed-muon-momentum", H=2, T_kv=9000, T_q=256, chunk_kv=9000, chunk_q=256,
           beta=0.5),
