@@ -148,6 +148,9 @@ FULL = [
     ("million", [(0, 3), (0, 10)], {}),
     ("lm", [(0, 0), (2, 5), (5, 3), (7, 7)], {}),
     ("video", [(0, 0), (0, 13), (0, 26), (0, 39)], {}),
+    # split products at d = 64 (the route of long or short-chunk Muon scans) at full size
+    ("posed", [(0, 2), (0, 9)], {"products": "split"}),
+    ("million", [(0, 6)], {"products": "split"}),
     # the variants at full size
     ("posed", [(0, 5)], {"eta_per_matrix": True}),
     ("lm", [(2, 6)], {"norm": "keep"}),
