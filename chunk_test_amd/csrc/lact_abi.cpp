@@ -87,6 +87,7 @@ struct Plan {
   bool muon = false;
   bool split = false;  // bf16 inputs, ~fp32 derived operands
   bool linear = false; // linear fast net (one d x d matrix per pair)
+  bool pm = false;     // a learning rate per token and matrix
   int norm = 0;        // lact_norm_mode
 };
 
@@ -135,7 +136,7 @@ SplitRule linear_rule(const Plan& p) { return {static_cast<int64_t>(p.P), 1024, 
 // 32-bit offsets inside a pair's rows: they need aligned K, V and strides and
 // n d < 2^31.  With split products the d = 64 kernel runs one workgroup per
 // CU (one wavefront per SIMD).
-enum class GradKind { Generic, D64, D128 };
+enum class GradKind { Generic, D64, D128, D128W };
 
 // Above this many token splits the Muon tail's partial sum runs as a
 // separate all-CU kernel.
@@ -145,23 +146,28 @@ struct GradChoice {
   GradKind kind;
   int stage;        // token splits are multiples of this
   int wgs_per_cu;   // resident workgroups per CU
+  int hid_per_wg;   // hidden units per workgroup
 };
 
 GradChoice grad_choice(const Plan& p, bool aligned, int64_t n) {
   const bool fits = aligned && n * p.d < (static_cast<int64_t>(1) << 31);
   if (p.mfma && fits) {
-    if (lact::grad_d64_shape_ok(p.d, p.h)) return {GradKind::D64, 128, p.split ? 1 : 2};
+    if (lact::grad_d64_shape_ok(p.d, p.h)) return {GradKind::D64, 128, p.split ? 1 : 2, 128};
+    // d = 128 with bf16 products and one rate per token: 16 hidden units per
+    // wavefront, two wavefronts per SIMD
+    if (!p.split && !p.pm && lact::grad_d128w_shape_ok(p.d, p.h))
+      return {GradKind::D128W, lact::grad_d128w_stage_tokens(), 2, lact::grad_d128w_hidden_per_workgroup()};
     if (lact::grad_d128_shape_ok(p.d, p.h))
-      return {GradKind::D128, lact::grad_d128_stage_tokens(p.split), 1};
+      return {GradKind::D128, lact::grad_d128_stage_tokens(p.split), 1, 128};
   }
-  return {GradKind::Generic, 1, 0};
+  return {GradKind::Generic, 1, 0, 0};
 }
 
 // MFMA kernels: one workgroup per (split, 128 hidden units, pair), sized to
 // one round of resident workgroups on 256 CUs, rounding the split count
 // down so no second round is started.
 SplitRule mfma_rule(const Plan& p, const GradChoice& k) {
-  const int64_t per_split = static_cast<int64_t>(p.P) * (p.h / 128);
+  const int64_t per_split = static_cast<int64_t>(p.P) * (p.h / k.hid_per_wg);
   const int64_t resident = 256 * k.wgs_per_cu;
   int64_t target = (resident / per_split) * per_split;
   if (target < per_split) target = per_split;
@@ -233,6 +239,7 @@ int check_config(const lact_config* c, Plan* p) {
   p->muon = c->opt == LACT_OPT_MUON;
   p->split = p->bf16 && c->products == LACT_PRODUCTS_SPLIT;
   p->norm = c->norm_mode;
+  p->pm = c->eta_mode == LACT_ETA_PER_MATRIX;
   return LACT_OK;
 }
 
@@ -394,6 +401,7 @@ int launch_gradient(const lact_config* c, const Plan& p, const lact_state* st, c
   switch (gk.kind) {
     case GradKind::D64: e = lact::launch_grad_d64(g, p.split, s); break;
     case GradKind::D128: e = lact::launch_grad_d128(g, p.split, s); break;
+    case GradKind::D128W: e = lact::launch_grad_d128w(g, s); break;
     default: e = lact::launch_grad_simple(g, s); break;
   }
   if (e != hipSuccess) return hip_fail(e, "gradient kernel");
