@@ -1,5 +1,5 @@
 // Chunk gradient of the LaCT layer for d = 128 on bf16 MFMA (gfx950), bf16
-// products, two wavefronts per SIMD.
+// or near-fp32 "split" products, two wavefronts per SIMD.
 //
 // For one (pair, token split, 64-unit hidden slice) a workgroup of four
 // wavefronts (16 hidden units each) sums, over the split's tokens i,
@@ -33,6 +33,12 @@
 //   slot 4 t + r <-> token 16 t + 4 q + r, which is directly the hidden-side
 //   operand of the contractions; the token-side operands (K, V with tokens
 //   along k in the same slot order) come from LDS transpose reads.
+//
+// Split products: keys and values are exact bf16 inputs, so only the other
+// operand of every product is split, x = x_hi + x_lo (both bf16), and each
+// product is two MFMAs (~16 significant bits per operand).  The lo parts of
+// W1 and W3 sit in LDS (read per k-step), W2's in registers, and the stages
+// shrink to 32 tokens, which keeps two workgroups per CU (64.25 KiB each).
 #include "lact_device.h"
 #include "lact_internal.h"
 
@@ -50,16 +56,22 @@ constexpr int D = 128;
 constexpr int kThreads = 256;
 constexpr int kHidPerWave = 16;
 constexpr int kHidPerWG = 64;
-constexpr int TT = 64;             // tokens per LDS stage
-constexpr int SUB = TT / 32;       // 32-token sub-tiles per stage
 constexpr int KS = D / 32;         // k-steps of the projections
 constexpr int NT = D / 16;         // 16-wide d tiles of the contractions
 constexpr int ROW = 2 * D;         // bytes per token row (sixteen 16-byte chunks)
-constexpr int TILE = TT * ROW;     // one stage of K (or V)
-constexpr int OFF_K = 0;           // K[2]
-constexpr int OFF_V = 2 * TILE;    // V[2]
-constexpr int OFF_E = 4 * TILE;    // eta[2][TT]
-constexpr int LDS = OFF_E + 2 * TT * 4;
+
+template <bool SPLIT>
+struct Geo {
+  static constexpr int TT = SPLIT ? 32 : 64;   // tokens per LDS stage
+  static constexpr int SUB = TT / 32;          // 32-token sub-tiles per stage
+  static constexpr int TILE = TT * ROW;        // one stage of K (or V)
+  static constexpr int OFF_K = 0;              // K[2]
+  static constexpr int OFF_V = 2 * TILE;       // V[2]
+  static constexpr int OFF_E = 4 * TILE;       // eta[2][TT]
+  static constexpr int OFF_WLO = OFF_E + 2 * TT * 4;  // W1_lo, W3_lo operands [matrix][wave][ks][lane]
+  static constexpr int WLO_BYTES = SPLIT ? 2 * 4 * KS * 64 * 16 : 0;
+  static constexpr int LDS = OFF_WLO + WLO_BYTES;
+};
 
 // W1 enters pre-scaled by -log2(e) (sigmoid(h1) = 1 / (1 + 2^z), z = -log2(e) h1);
 // G, dH3 and dH1 then carry that factor, removed at the end (times -ln 2).
@@ -82,9 +94,17 @@ __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// lo bf16 part of a float given its hi part (the rounded remainder)
+__device__ __forceinline__ __bf16 lo_bf16(float x, __bf16 hi) {
+  return static_cast<__bf16>(x - static_cast<float>(hi));
+}
+
+template <bool SPLIT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_grad_d128w(GradArgs a, int hsl, int nbase) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS];
+  using G = Geo<SPLIT>;
+  constexpr int TT = G::TT, TILE = G::TILE, OFF_K = G::OFF_K, OFF_V = G::OFF_V, OFF_E = G::OFF_E;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[G::LDS];
 
   // XCD-aware block order: the hidden slices of one (pair, split) land on
   // the same XCD (block ids congruent mod 8) so their key/value reads share L2.
@@ -108,20 +128,33 @@ void k_grad_d128w(GradArgs a, int hsl, int nbase) {
   const int n0 = hs * kHidPerWG + wave * kHidPerWave;  // this wave's hidden units
 
   // ---- B operands of the projections: lane holds hidden unit n0 + l16,
-  // features 32 ks + 8 q .. +7
+  // features 32 ks + 8 q .. +7 (with split products the lo parts of W1 and
+  // W3 go to LDS, slot [matrix][wave][ks][lane], and W2's to registers)
   bf16x8_t w1b[KS], w3b[KS], w2b[KS];
+  bf16x8_t w2l[SPLIT ? KS : 1];
   {
     const float* W1 = a.W1 + pair * hd + static_cast<int64_t>(n0 + l16) * D;
     const float* W3 = a.W3 + pair * hd + static_cast<int64_t>(n0 + l16) * D;
     const float* W2 = a.W2 + pair * hd + n0 + l16;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+      bf16x8_t l1, l3;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int dd = 32 * ks + 8 * q + i;
-        w1b[ks][i] = static_cast<__bf16>(kNegLog2e * W1[dd]);
-        w3b[ks][i] = static_cast<__bf16>(W3[dd]);
-        w2b[ks][i] = static_cast<__bf16>(W2[static_cast<int64_t>(dd) * h]);
+        const float x1 = kNegLog2e * W1[dd], x3 = W3[dd], x2 = W2[static_cast<int64_t>(dd) * h];
+        w1b[ks][i] = static_cast<__bf16>(x1);
+        w3b[ks][i] = static_cast<__bf16>(x3);
+        w2b[ks][i] = static_cast<__bf16>(x2);
+        if constexpr (SPLIT) {
+          l1[i] = lo_bf16(x1, w1b[ks][i]);
+          l3[i] = lo_bf16(x3, w3b[ks][i]);
+          w2l[ks][i] = lo_bf16(x2, w2b[ks][i]);
+        }
+      }
+      if constexpr (SPLIT) {
+        *reinterpret_cast<bf16x8_t*>(lds + G::OFF_WLO + (((0 * 4 + wave) * KS + ks) * 64 + lane) * 16) = l1;
+        *reinterpret_cast<bf16x8_t*>(lds + G::OFF_WLO + (((1 * 4 + wave) * KS + ks) * 64 + lane) * 16) = l3;
       }
     }
   }
@@ -150,9 +183,9 @@ void k_grad_d128w(GradArgs a, int hsl, int nbase) {
   const int t_last = static_cast<int>(t_end - 1);
 
   // DMA of one stage into buffer b: 1 KiB pieces (4 rows each), wave wv
-  // moving pieces wv, wv + 4, wv + 8, wv + 12; lane l of a piece lands at its
-  // byte 16 l: row 4 piece + l / 16, physical chunk l % 16.  Wave 0 moves the
-  // stage's 64 rates.  Rows past the end re-read the split's last token
+  // moving pieces wv, wv + 4, ...; lane l of a piece lands at its
+  // byte 16 l: row 4 piece + l / 16, physical chunk l % 16.  Lanes 0 .. TT - 1
+  // of wave 0 move the stage's rates.  Rows past the end re-read the split's last token
   // (finite values); their eta is written as 0, so they add nothing.
   auto dma_stage = [&](int64_t t0, int b) {
     // (the lane-derived offsets are recomputed per stage: a few
@@ -170,7 +203,7 @@ void k_grad_d128w(GradArgs a, int hsl, int nbase) {
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Kg + off), (lds_ptr_t)(lds + OFF_K + b * TILE + 1024 * piece), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Vg + off), (lds_ptr_t)(lds + OFF_V + b * TILE + 1024 * piece), 16, 0, 0);
     }
-    if (wv == 0) {
+    if (wv == 0 && lane < TT) {
       const int tok = static_cast<int>(t0) + lane;
       unsigned char* dst = lds + OFF_E + b * TT * 4;
       if (tok <= t_last) {
@@ -214,7 +247,7 @@ void k_grad_d128w(GradArgs a, int hsl, int nbase) {
     const float* eb = reinterpret_cast<const float*>(lds + OFF_E + b * TT * 4);
 
 #pragma unroll
-    for (int st = 0; st < SUB; ++st) {
+    for (int st = 0; st < G::SUB; ++st) {
       // projections of 32 tokens (two 16-token tiles) x this wave's 16 hidden units
       f32x4_t c1[2], c3[2], cg[2];
 #pragma unroll
@@ -241,6 +274,16 @@ void k_grad_d128w(GradArgs a, int hsl, int nbase) {
           c3[t] = mfma16(ak[t], w3b[ks], c3[t]);
           cg[t] = mfma16(av[t], w2b[ks], cg[t]);
         }
+        if constexpr (SPLIT) {
+          const bf16x8_t l1 = *reinterpret_cast<const bf16x8_t*>(lds + G::OFF_WLO + (((0 * 4 + wave) * KS + ks) * 64 + lane) * 16);
+          const bf16x8_t l3 = *reinterpret_cast<const bf16x8_t*>(lds + G::OFF_WLO + (((1 * 4 + wave) * KS + ks) * 64 + lane) * 16);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            c1[t] = mfma16(ak[t], l1, c1[t]);
+            c3[t] = mfma16(ak[t], l3, c3[t]);
+            cg[t] = mfma16(av[t], w2l[ks], cg[t]);
+          }
+        }
       }
       // eta of this lane's eight tokens 32 st + 16 t + 4 q + r
       const f32x4_t e0 = *reinterpret_cast<const f32x4_t*>(eb + 32 * st + 4 * q);
@@ -252,7 +295,7 @@ void k_grad_d128w(GradArgs a, int hsl, int nbase) {
       //   dh1' = dg (g' + s t'),  t' = -log2(e) h3 - g'  (= -log2(e) dh1, since
       //   dh1 = dg h3 s (1 + h1 (1 - s)) = dg (g + s (h3 - g))),
       // and the contraction with v takes e g'.
-      bf16x8_t pg, pd1, pd3;
+      bf16x8_t pg, pd1, pd3, lg, ld1, ld3;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int t = i >> 2, r = i & 3;
@@ -262,10 +305,16 @@ void k_grad_d128w(GradArgs a, int hsl, int nbase) {
         const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(z));
         const float act = z * sg;
         const float gs = act * h3;
-        pg[i] = static_cast<__bf16>(ne * gs);
-        pd3[i] = static_cast<__bf16>(dg * act);
         const float tt = fmaf(h3, kNegLog2e, -gs);
-        pd1[i] = static_cast<__bf16>(dg * fmaf(sg, tt, gs));
+        const float vg = ne * gs, v3 = dg * act, v1 = dg * fmaf(sg, tt, gs);
+        pg[i] = static_cast<__bf16>(vg);
+        pd3[i] = static_cast<__bf16>(v3);
+        pd1[i] = static_cast<__bf16>(v1);
+        if constexpr (SPLIT) {
+          lg[i] = lo_bf16(vg, pg[i]);
+          ld3[i] = lo_bf16(v3, pd3[i]);
+          ld1[i] = lo_bf16(v1, pd1[i]);
+        }
       }
       // contractions over the 32 tokens (k), one 16-feature tile at a time
 #pragma unroll
@@ -282,6 +331,11 @@ void k_grad_d128w(GradArgs a, int hsl, int nbase) {
         aW1[nt] = mfma16(pd1, bk, aW1[nt]);
         aW3[nt] = mfma16(pd3, bk, aW3[nt]);
         aW2[nt] = mfma16(bv, pg, aW2[nt]);
+        if constexpr (SPLIT) {
+          aW1[nt] = mfma16(ld1, bk, aW1[nt]);
+          aW3[nt] = mfma16(ld3, bk, aW3[nt]);
+          aW2[nt] = mfma16(bv, lg, aW2[nt]);
+        }
       }
     }
   }
@@ -306,16 +360,20 @@ bool grad_d128w_shape_ok(int d, int h) {
   return d == D && h % kHidPerWG == 0 && h >= kHidPerWG && h <= 1024;
 }
 
-int grad_d128w_stage_tokens() { return TT; }
+int grad_d128w_stage_tokens(bool split) { return split ? Geo<true>::TT : Geo<false>::TT; }
 
 int grad_d128w_hidden_per_workgroup() { return kHidPerWG; }
 
-hipError_t launch_grad_d128w(const GradArgs& a, hipStream_t s) {
+hipError_t launch_grad_d128w(const GradArgs& a, bool split, hipStream_t s) {
   if (a.d != D || a.eta_mat != 0) return hipErrorInvalidValue;
   const int hsl = a.h / kHidPerWG;
   const int nbase = a.S * a.P;
   const int blocks = ((nbase + 7) / 8) * 8 * hsl;
-  hipLaunchKernelGGL(k_grad_d128w, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  if (split) {
+    hipLaunchKernelGGL(k_grad_d128w<true>, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  } else {
+    hipLaunchKernelGGL(k_grad_d128w<false>, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  }
   return hipGetLastError();
 }
 

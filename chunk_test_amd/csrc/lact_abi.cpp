@@ -153,10 +153,10 @@ GradChoice grad_choice(const Plan& p, bool aligned, int64_t n) {
   const bool fits = aligned && n * p.d < (static_cast<int64_t>(1) << 31);
   if (p.mfma && fits) {
     if (lact::grad_d64_shape_ok(p.d, p.h)) return {GradKind::D64, 128, p.split ? 1 : 2, 128};
-    // d = 128 with bf16 products and one rate per token: 16 hidden units per
-    // wavefront, two wavefronts per SIMD
-    if (!p.split && !p.pm && lact::grad_d128w_shape_ok(p.d, p.h))
-      return {GradKind::D128W, lact::grad_d128w_stage_tokens(), 2, lact::grad_d128w_hidden_per_workgroup()};
+    // d = 128 with one rate per token: 16 hidden units per wavefront, two
+    // wavefronts per SIMD (bf16 or split products)
+    if (!p.pm && lact::grad_d128w_shape_ok(p.d, p.h))
+      return {GradKind::D128W, lact::grad_d128w_stage_tokens(p.split), 2, lact::grad_d128w_hidden_per_workgroup()};
     if (lact::grad_d128_shape_ok(p.d, p.h))
       return {GradKind::D128, lact::grad_d128_stage_tokens(p.split), 1, 128};
   }
@@ -401,7 +401,7 @@ int launch_gradient(const lact_config* c, const Plan& p, const lact_state* st, c
   switch (gk.kind) {
     case GradKind::D64: e = lact::launch_grad_d64(g, p.split, s); break;
     case GradKind::D128: e = lact::launch_grad_d128(g, p.split, s); break;
-    case GradKind::D128W: e = lact::launch_grad_d128w(g, s); break;
+    case GradKind::D128W: e = lact::launch_grad_d128w(g, p.split, s); break;
     default: e = lact::launch_grad_simple(g, s); break;
   }
   if (e != hipSuccess) return hip_fail(e, "gradient kernel");

@@ -257,10 +257,10 @@ hipError_t launch_grad_d64(const GradArgs& a, bool split, hipStream_t s);
 bool grad_d128_shape_ok(int d, int h);  // d = 128, LDS-DMA staging, bf16 or split products
 int grad_d128_stage_tokens(bool split);
 hipError_t launch_grad_d128(const GradArgs& a, bool split, hipStream_t s);
-bool grad_d128w_shape_ok(int d, int h);  // d = 128, bf16 products, 16x16x32 tiles, two waves per SIMD
-int grad_d128w_stage_tokens();
+bool grad_d128w_shape_ok(int d, int h);  // d = 128, bf16 or split products, 16x16x32 tiles, two waves per SIMD
+int grad_d128w_stage_tokens(bool split);
 int grad_d128w_hidden_per_workgroup();
-hipError_t launch_grad_d128w(const GradArgs& a, hipStream_t s);
+hipError_t launch_grad_d128w(const GradArgs& a, bool split, hipStream_t s);
 bool ns_mfma_shape_ok(int d, int h);
 // Muon update tail of one chunk and the query read of the same chunk (from
 // the bf16 copy of its weights) in one launch, where h > d, both have
