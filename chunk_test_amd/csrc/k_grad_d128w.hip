@@ -60,15 +60,16 @@ constexpr int KS = D / 32;         // k-steps of the projections
 constexpr int NT = D / 16;         // 16-wide d tiles of the contractions
 constexpr int ROW = 2 * D;         // bytes per token row (sixteen 16-byte chunks)
 
-template <bool SPLIT>
+template <bool SPLIT, bool PM>
 struct Geo {
   static constexpr int TT = SPLIT ? 32 : 64;   // tokens per LDS stage
   static constexpr int SUB = TT / 32;          // 32-token sub-tiles per stage
   static constexpr int TILE = TT * ROW;        // one stage of K (or V)
   static constexpr int OFF_K = 0;              // K[2]
   static constexpr int OFF_V = 2 * TILE;       // V[2]
-  static constexpr int OFF_E = 4 * TILE;       // eta[2][TT]
-  static constexpr int OFF_WLO = OFF_E + 2 * TT * 4;  // W1_lo, W3_lo operands [matrix][wave][ks][lane]
+  static constexpr int NE = PM ? 3 : 1;        // rows of rates per stage (W1, W2, W3 with PM)
+  static constexpr int OFF_E = 4 * TILE;       // eta[2][NE][TT]
+  static constexpr int OFF_WLO = OFF_E + 2 * NE * TT * 4;  // W1_lo, W3_lo operands [matrix][wave][ks][lane]
   static constexpr int WLO_BYTES = SPLIT ? 2 * 4 * KS * 64 * 16 : 0;
   static constexpr int LDS = OFF_WLO + WLO_BYTES;
 };
@@ -99,10 +100,12 @@ __device__ __forceinline__ __bf16 lo_bf16(float x, __bf16 hi) {
   return static_cast<__bf16>(x - static_cast<float>(hi));
 }
 
-template <bool SPLIT>
+// PM: a learning rate per token and matrix (rows of rates for W1, W2, W3,
+// a.eta_mat elements apart); otherwise one rate per token.
+template <bool SPLIT, bool PM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_grad_d128w(GradArgs a, int hsl, int nbase) {
-  using G = Geo<SPLIT>;
+  using G = Geo<SPLIT, PM>;
   constexpr int TT = G::TT, TILE = G::TILE, OFF_K = G::OFF_K, OFF_V = G::OFF_V, OFF_E = G::OFF_E;
   __shared__ __attribute__((aligned(16))) unsigned char lds[G::LDS];
 
@@ -185,7 +188,7 @@ void k_grad_d128w(GradArgs a, int hsl, int nbase) {
   // DMA of one stage into buffer b: 1 KiB pieces (4 rows each), wave wv
   // moving pieces wv, wv + 4, ...; lane l of a piece lands at its
   // byte 16 l: row 4 piece + l / 16, physical chunk l % 16.  Lanes 0 .. TT - 1
-  // of wave 0 move the stage's rates.  Rows past the end re-read the split's last token
+  // of wave m move the stage's row m of rates (one row, or three with PM).  Rows past the end re-read the split's last token
   // (finite values); their eta is written as 0, so they add nothing.
   auto dma_stage = [&](int64_t t0, int b) {
     // (the lane-derived offsets are recomputed per stage: a few
@@ -203,11 +206,12 @@ void k_grad_d128w(GradArgs a, int hsl, int nbase) {
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Kg + off), (lds_ptr_t)(lds + OFF_K + b * TILE + 1024 * piece), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(Vg + off), (lds_ptr_t)(lds + OFF_V + b * TILE + 1024 * piece), 16, 0, 0);
     }
-    if (wv == 0 && lane < TT) {
+    if (wv < G::NE && lane < TT) {
       const int tok = static_cast<int>(t0) + lane;
-      unsigned char* dst = lds + OFF_E + b * TT * 4;
+      unsigned char* dst = lds + OFF_E + (b * G::NE + wv) * TT * 4;
       if (tok <= t_last) {
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(etag + static_cast<unsigned>(tok)), (lds_ptr_t)dst, 4, 0, 0);
+        const float* src = etag + (PM ? wv * a.eta_mat : 0) + static_cast<unsigned>(tok);
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)dst, 4, 0, 0);
       } else {
         *reinterpret_cast<float*>(dst + 4 * lane) = 0.f;
       }
@@ -244,7 +248,8 @@ void k_grad_d128w(GradArgs a, int hsl, int nbase) {
 
     const unsigned char* kb = lds + OFF_K + b * TILE;
     const unsigned char* vb = lds + OFF_V + b * TILE;
-    const float* eb = reinterpret_cast<const float*>(lds + OFF_E + b * TT * 4);
+    // rates of this stage (with PM rows for W1, W2, W3)
+    const float* eb = reinterpret_cast<const float*>(lds + OFF_E + b * G::NE * TT * 4);
 
 #pragma unroll
     for (int st = 0; st < G::SUB; ++st) {
@@ -285,9 +290,18 @@ void k_grad_d128w(GradArgs a, int hsl, int nbase) {
           }
         }
       }
-      // eta of this lane's eight tokens 32 st + 16 t + 4 q + r
-      const f32x4_t e0 = *reinterpret_cast<const f32x4_t*>(eb + 32 * st + 4 * q);
-      const f32x4_t e1 = *reinterpret_cast<const f32x4_t*>(eb + 32 * st + 16 + 4 * q);
+      // rates of this lane's eight tokens 32 st + 16 t + 4 q + r: the one of W2
+      // (g), and with PM those of W1 (x1) and W3 (x3)
+      const float* e2b = eb + (PM ? TT : 0);
+      const f32x4_t e0 = *reinterpret_cast<const f32x4_t*>(e2b + 32 * st + 4 * q);
+      const f32x4_t e1 = *reinterpret_cast<const f32x4_t*>(e2b + 32 * st + 16 + 4 * q);
+      f32x4_t x10, x11, x30, x31;
+      if constexpr (PM) {
+        x10 = *reinterpret_cast<const f32x4_t*>(eb + 32 * st + 4 * q);
+        x11 = *reinterpret_cast<const f32x4_t*>(eb + 32 * st + 16 + 4 * q);
+        x30 = *reinterpret_cast<const f32x4_t*>(eb + 2 * TT + 32 * st + 4 * q);
+        x31 = *reinterpret_cast<const f32x4_t*>(eb + 2 * TT + 32 * st + 16 + 4 * q);
+      }
       // SwiGLU forward and backward on the eight values.  With
       // z = -log2(e) h1, s = sigmoid(h1) = 1 / (1 + 2^z), a = silu(h1),
       // g = a h3, e = -eta and dg = e dG':
@@ -301,12 +315,15 @@ void k_grad_d128w(GradArgs a, int hsl, int nbase) {
         const int t = i >> 2, r = i & 3;
         const float ne = -((t == 0) ? e0[r] : e1[r]);
         const float z = c1[t][r], h3 = c3[t][r];
+        // dG of the losses W1 and W3 follow (the same one without PM)
         const float dg = ne * cg[t][r];
+        const float dg1 = PM ? -((t == 0) ? x10[r] : x11[r]) * cg[t][r] : dg;
+        const float dg3 = PM ? -((t == 0) ? x30[r] : x31[r]) * cg[t][r] : dg;
         const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(z));
         const float act = z * sg;
         const float gs = act * h3;
         const float tt = fmaf(h3, kNegLog2e, -gs);
-        const float vg = ne * gs, v3 = dg * act, v1 = dg * fmaf(sg, tt, gs);
+        const float vg = ne * gs, v3 = dg3 * act, v1 = dg1 * fmaf(sg, tt, gs);
         pg[i] = static_cast<__bf16>(vg);
         pd3[i] = static_cast<__bf16>(v3);
         pd1[i] = static_cast<__bf16>(v1);
@@ -356,23 +373,30 @@ void k_grad_d128w(GradArgs a, int hsl, int nbase) {
 
 }  // namespace
 
+bool d128_mfma_shape_ok(int d, int h) { return d == D && h % 128 == 0 && h >= 128 && h <= 1024; }
+
 bool grad_d128w_shape_ok(int d, int h) {
   return d == D && h % kHidPerWG == 0 && h >= kHidPerWG && h <= 1024;
 }
 
-int grad_d128w_stage_tokens(bool split) { return split ? Geo<true>::TT : Geo<false>::TT; }
+int grad_d128w_stage_tokens(bool split) { return split ? Geo<true, false>::TT : Geo<false, false>::TT; }
 
 int grad_d128w_hidden_per_workgroup() { return kHidPerWG; }
 
 hipError_t launch_grad_d128w(const GradArgs& a, bool split, hipStream_t s) {
-  if (a.d != D || a.eta_mat != 0) return hipErrorInvalidValue;
+  if (a.d != D) return hipErrorInvalidValue;
   const int hsl = a.h / kHidPerWG;
   const int nbase = a.S * a.P;
   const int blocks = ((nbase + 7) / 8) * 8 * hsl;
-  if (split) {
-    hipLaunchKernelGGL(k_grad_d128w<true>, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  const bool pm = a.eta_mat != 0;
+  if (split && pm) {
+    hipLaunchKernelGGL((k_grad_d128w<true, true>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  } else if (split) {
+    hipLaunchKernelGGL((k_grad_d128w<true, false>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+  } else if (pm) {
+    hipLaunchKernelGGL((k_grad_d128w<false, true>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
   } else {
-    hipLaunchKernelGGL(k_grad_d128w<false>, dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
+    hipLaunchKernelGGL((k_grad_d128w<false, false>), dim3(blocks), dim3(kThreads), 0, s, a, hsl, nbase);
   }
   return hipGetLastError();
 }

@@ -135,8 +135,9 @@ SplitRule linear_rule(const Plan& p) { return {static_cast<int64_t>(p.P), 1024, 
 // Which chunk-gradient kernel runs.  The MFMA kernels read 16-byte rows with
 // 32-bit offsets inside a pair's rows: they need aligned K, V and strides and
 // n d < 2^31.  With split products the d = 64 kernel runs one workgroup per
-// CU (one wavefront per SIMD).
-enum class GradKind { Generic, D64, D128, D128W };
+// CU (one wavefront per SIMD); the d = 128 kernel two workgroups of 64-unit
+// hidden slices per CU.
+enum class GradKind { Generic, D64, D128W };
 
 // Above this many token splits the Muon tail's partial sum runs as a
 // separate all-CU kernel.
@@ -153,17 +154,14 @@ GradChoice grad_choice(const Plan& p, bool aligned, int64_t n) {
   const bool fits = aligned && n * p.d < (static_cast<int64_t>(1) << 31);
   if (p.mfma && fits) {
     if (lact::grad_d64_shape_ok(p.d, p.h)) return {GradKind::D64, 128, p.split ? 1 : 2, 128};
-    // d = 128 with one rate per token: 16 hidden units per wavefront, two
-    // wavefronts per SIMD (bf16 or split products)
-    if (!p.pm && lact::grad_d128w_shape_ok(p.d, p.h))
+    // d = 128: 16 hidden units per wavefront, two wavefronts per SIMD
+    if (lact::grad_d128w_shape_ok(p.d, p.h))
       return {GradKind::D128W, lact::grad_d128w_stage_tokens(p.split), 2, lact::grad_d128w_hidden_per_workgroup()};
-    if (lact::grad_d128_shape_ok(p.d, p.h))
-      return {GradKind::D128, lact::grad_d128_stage_tokens(p.split), 1, 128};
   }
   return {GradKind::Generic, 1, 0, 0};
 }
 
-// MFMA kernels: one workgroup per (split, 128 hidden units, pair), sized to
+// MFMA kernels: one workgroup per (split, hidden slice, pair), sized to
 // one round of resident workgroups on 256 CUs, rounding the split count
 // down so no second round is started.
 SplitRule mfma_rule(const Plan& p, const GradChoice& k) {
@@ -400,7 +398,6 @@ int launch_gradient(const lact_config* c, const Plan& p, const lact_state* st, c
   hipError_t e;
   switch (gk.kind) {
     case GradKind::D64: e = lact::launch_grad_d64(g, p.split, s); break;
-    case GradKind::D128: e = lact::launch_grad_d128(g, p.split, s); break;
     case GradKind::D128W: e = lact::launch_grad_d128w(g, p.split, s); break;
     default: e = lact::launch_grad_simple(g, s); break;
   }
@@ -1089,7 +1086,7 @@ void lact_config_default(lact_config* c) {
 
 int lact_mfma_path(int32_t d, int32_t h, int32_t io_dtype) {
   if (!lact::simple_shape_ok(d, h)) return -1;
-  return (io_dtype == LACT_BF16 && (lact::grad_d64_shape_ok(d, h) || lact::grad_d128_shape_ok(d, h))) ? 1 : 0;
+  return (io_dtype == LACT_BF16 && (lact::grad_d64_shape_ok(d, h) || lact::d128_mfma_shape_ok(d, h))) ? 1 : 0;
 }
 
 size_t lact_workspace_bytes(const lact_config* cfg, int64_t max_chunk_kv, int64_t max_chunk_q) {

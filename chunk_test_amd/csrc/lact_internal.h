@@ -254,9 +254,7 @@ bool simple_shape_ok(int d, int h);
 // ---- bf16 MFMA kernels (gfx950) ----
 bool grad_d64_shape_ok(int d, int h);  // d = 64, LDS-DMA staging
 hipError_t launch_grad_d64(const GradArgs& a, bool split, hipStream_t s);
-bool grad_d128_shape_ok(int d, int h);  // d = 128, LDS-DMA staging, bf16 or split products
-int grad_d128_stage_tokens(bool split);
-hipError_t launch_grad_d128(const GradArgs& a, bool split, hipStream_t s);
+bool d128_mfma_shape_ok(int d, int h);  // d = 128 shapes of the matrix-core path (h a multiple of 128)
 bool grad_d128w_shape_ok(int d, int h);  // d = 128, bf16 or split products, 16x16x32 tiles, two waves per SIMD
 int grad_d128w_stage_tokens(bool split);
 int grad_d128w_hidden_per_workgroup();
