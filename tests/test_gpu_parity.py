@@ -77,6 +77,11 @@ SMALL_CASES = [
     small("lm", name="lm-h384-ragged", B=1, H=2, h=384, T_kv=3000, T_q=600, chunk_kv=1500,
           chunk_q=300),
     small("lm", name="lm-h128", B=2, H=1, h=128, T_kv=2048, T_q=512, chunk_kv=1024, chunk_q=256),
+    # chunks shorter than one LDS stage of the d = 128 kernel (64 keys with bf16 products,
+    # 32 with split products; Muon over ten 20-key chunks takes split products)
+    small("lm", name="lm-tiny-chunks", B=1, H=2, T_kv=300, T_q=60, chunk_kv=30, chunk_q=6),
+    small("video", name="video-tiny-chunks", H=2, T_kv=200, T_q=40, chunk_kv=20, chunk_q=4,
+          products="auto"),
     # rows kept at their length (norm_mode LACT_NORM_KEEP) through every update tail:
     # fp32 GD / momentum (row-wise tail), fp32 Muon (step-and-normalise kernel), bf16
     # momentum (16-byte row-group tail), bf16 Muon at d = 64 and split-product Muon at
