@@ -11,7 +11,7 @@
 // and nonlinear memory work together").  The chunk is a set, so the sum is
 // split over tokens across workgroups and reduced afterwards in fixed order.
 //
-// Why a second d = 128 kernel: with 32 hidden units per wavefront the dW
+// Why 16 hidden units per wavefront: with 32 (the d = 64 geometry) the dW
 // tiles take 192 fp32 per lane and the kernel runs one wavefront per SIMD,
 // which leaves nothing to issue while a wavefront waits on its own LDS reads
 // and product chains.  Here every product is a 16x16x32 MFMA and a wavefront
