@@ -1,7 +1,7 @@
 // Chunk gradient of the LaCT layer for d = 128 on bf16 MFMA (gfx950), bf16
 // or near-fp32 "split" products, two wavefronts per SIMD.
 //
-// For one (pair, token split, 64-unit hidden slice) a workgroup of four
+// For one (pair, token split, 128-unit hidden slice) a workgroup of eight
 // wavefronts (16 hidden units each) sums, over the split's tokens i,
 //   dW1 += dh1_i k_i^T,  dW3 += dh3_i k_i^T,  dW2 += v_i (-eta_i g_i)^T
 // with h1 = W1 k, h3 = W3 k, a = silu(h1), g = a * h3, dg = -eta_i W2^T v_i,
@@ -16,7 +16,10 @@
 // which leaves nothing to issue while a wavefront waits on its own LDS reads
 // and product chains.  Here every product is a 16x16x32 MFMA and a wavefront
 // owns 16 hidden units: 96 fp32 of dW tiles per lane, about 250 registers in
-// all, so two workgroups share a CU (two wavefronts per SIMD).
+// all, so two wavefronts share each SIMD.  A workgroup of eight wavefronts
+// (128 hidden units, one per CU) shares each key / value stage among all
+// eight: half the LDS-DMA writes and L2 reads of two four-wavefront
+// workgroups, and 1-1.5 % faster in the LM and video scans.
 //
 // Staging as in the other gradient kernels: keys, values and eta of the next
 // 64-token stage move from HBM straight into LDS (global_load_lds, no
@@ -38,7 +41,7 @@
 // operand of every product is split, x = x_hi + x_lo (both bf16), and each
 // product is two MFMAs (~16 significant bits per operand).  The lo parts of
 // W1 and W3 sit in LDS (read per k-step), W2's in registers, and the stages
-// shrink to 32 tokens, which keeps two workgroups per CU (64.25 KiB each).
+// shrink to 32 tokens (96.25 KiB of LDS per workgroup).
 #include "lact_device.h"
 #include "lact_internal.h"
 
@@ -53,9 +56,10 @@ typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 typedef __attribute__((address_space(3))) s16x4_t* lds_s16x4_t;
 
 constexpr int D = 128;
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;                      // wavefronts per workgroup
+constexpr int kThreads = 64 * kWaves;
 constexpr int kHidPerWave = 16;
-constexpr int kHidPerWG = 64;
+constexpr int kHidPerWG = 16 * kWaves;
 constexpr int KS = D / 32;         // k-steps of the projections
 constexpr int NT = D / 16;         // 16-wide d tiles of the contractions
 constexpr int ROW = 2 * D;         // bytes per token row (sixteen 16-byte chunks)
@@ -70,7 +74,7 @@ struct Geo {
   static constexpr int NE = PM ? 3 : 1;        // rows of rates per stage (W1, W2, W3 with PM)
   static constexpr int OFF_E = 4 * TILE;       // eta[2][NE][TT]
   static constexpr int OFF_WLO = OFF_E + 2 * NE * TT * 4;  // W1_lo, W3_lo operands [matrix][wave][ks][lane]
-  static constexpr int WLO_BYTES = SPLIT ? 2 * 4 * KS * 64 * 16 : 0;
+  static constexpr int WLO_BYTES = SPLIT ? 2 * kWaves * KS * 64 * 16 : 0;
   static constexpr int LDS = OFF_WLO + WLO_BYTES;
 };
 
@@ -156,8 +160,8 @@ void k_grad_d128w(GradArgs a, int hsl, int nbase) {
         }
       }
       if constexpr (SPLIT) {
-        *reinterpret_cast<bf16x8_t*>(lds + G::OFF_WLO + (((0 * 4 + wave) * KS + ks) * 64 + lane) * 16) = l1;
-        *reinterpret_cast<bf16x8_t*>(lds + G::OFF_WLO + (((1 * 4 + wave) * KS + ks) * 64 + lane) * 16) = l3;
+        *reinterpret_cast<bf16x8_t*>(lds + G::OFF_WLO + (((0 * kWaves + wave) * KS + ks) * 64 + lane) * 16) = l1;
+        *reinterpret_cast<bf16x8_t*>(lds + G::OFF_WLO + (((1 * kWaves + wave) * KS + ks) * 64 + lane) * 16) = l3;
       }
     }
   }
@@ -186,18 +190,19 @@ void k_grad_d128w(GradArgs a, int hsl, int nbase) {
   const int t_last = static_cast<int>(t_end - 1);
 
   // DMA of one stage into buffer b: 1 KiB pieces (4 rows each), wave wv
-  // moving pieces wv, wv + 4, ...; lane l of a piece lands at its
-  // byte 16 l: row 4 piece + l / 16, physical chunk l % 16.  Lanes 0 .. TT - 1
-  // of wave m move the stage's row m of rates (one row, or three with PM).  Rows past the end re-read the split's last token
-  // (finite values); their eta is written as 0, so they add nothing.
+  // moving pieces wv, wv + kWaves, ...; lane l of a piece lands at its byte
+  // 16 l: row 4 piece + l / 16, physical chunk l % 16.  Lanes 0 .. TT - 1 of
+  // wave m move the stage's row m of rates (one row, or three with PM).  Rows
+  // past the end re-read the split's last token (finite values); their eta is
+  // written as 0, so they add nothing.
   auto dma_stage = [&](int64_t t0, int b) {
     // (the lane-derived offsets are recomputed per stage: a few
     // instructions, where keeping them live would take registers)
     int lane = threadIdx.x & 63;
     asm volatile("" : "+v"(lane));
 #pragma unroll
-    for (int k = 0; k < TT / 16; ++k) {
-      const int piece = 4 * k + wv;
+    for (int k = 0; k < TT / (4 * kWaves); ++k) {
+      const int piece = kWaves * k + wv;
       const int r = 4 * piece + (lane >> 4);
       const int cl = (lane & 15) ^ swz(r);
       const int tok = static_cast<int>(t0) + r;
@@ -280,8 +285,8 @@ void k_grad_d128w(GradArgs a, int hsl, int nbase) {
           cg[t] = mfma16(av[t], w2b[ks], cg[t]);
         }
         if constexpr (SPLIT) {
-          const bf16x8_t l1 = *reinterpret_cast<const bf16x8_t*>(lds + G::OFF_WLO + (((0 * 4 + wave) * KS + ks) * 64 + lane) * 16);
-          const bf16x8_t l3 = *reinterpret_cast<const bf16x8_t*>(lds + G::OFF_WLO + (((1 * 4 + wave) * KS + ks) * 64 + lane) * 16);
+          const bf16x8_t l1 = *reinterpret_cast<const bf16x8_t*>(lds + G::OFF_WLO + (((0 * kWaves + wave) * KS + ks) * 64 + lane) * 16);
+          const bf16x8_t l3 = *reinterpret_cast<const bf16x8_t*>(lds + G::OFF_WLO + (((1 * kWaves + wave) * KS + ks) * 64 + lane) * 16);
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             c1[t] = mfma16(ak[t], l1, c1[t]);
@@ -382,6 +387,8 @@ bool grad_d128w_shape_ok(int d, int h) {
 int grad_d128w_stage_tokens(bool split) { return split ? Geo<true, false>::TT : Geo<false, false>::TT; }
 
 int grad_d128w_hidden_per_workgroup() { return kHidPerWG; }
+
+int grad_d128w_workgroups_per_cu() { return 8 / kWaves; }
 
 hipError_t launch_grad_d128w(const GradArgs& a, bool split, hipStream_t s) {
   if (a.d != D) return hipErrorInvalidValue;

@@ -135,8 +135,8 @@ SplitRule linear_rule(const Plan& p) { return {static_cast<int64_t>(p.P), 1024, 
 // Which chunk-gradient kernel runs.  The MFMA kernels read 16-byte rows with
 // 32-bit offsets inside a pair's rows: they need aligned K, V and strides and
 // n d < 2^31.  With split products the d = 64 kernel runs one workgroup per
-// CU (one wavefront per SIMD); the d = 128 kernel two workgroups of 64-unit
-// hidden slices per CU.
+// CU (one wavefront per SIMD); the d = 128 kernel one workgroup of eight
+// wavefronts (a 128-unit hidden slice) per CU.
 enum class GradKind { Generic, D64, D128W };
 
 // Above this many token splits the Muon tail's partial sum runs as a
@@ -156,7 +156,8 @@ GradChoice grad_choice(const Plan& p, bool aligned, int64_t n) {
     if (lact::grad_d64_shape_ok(p.d, p.h)) return {GradKind::D64, 128, p.split ? 1 : 2, 128};
     // d = 128: 16 hidden units per wavefront, two wavefronts per SIMD
     if (lact::grad_d128w_shape_ok(p.d, p.h))
-      return {GradKind::D128W, lact::grad_d128w_stage_tokens(p.split), 2, lact::grad_d128w_hidden_per_workgroup()};
+      return {GradKind::D128W, lact::grad_d128w_stage_tokens(p.split), lact::grad_d128w_workgroups_per_cu(),
+              lact::grad_d128w_hidden_per_workgroup()};
   }
   return {GradKind::Generic, 1, 0, 0};
 }

@@ -258,6 +258,7 @@ bool d128_mfma_shape_ok(int d, int h);  // d = 128 shapes of the matrix-core pat
 bool grad_d128w_shape_ok(int d, int h);  // d = 128, bf16 or split products, 16x16x32 tiles, two waves per SIMD
 int grad_d128w_stage_tokens(bool split);
 int grad_d128w_hidden_per_workgroup();
+int grad_d128w_workgroups_per_cu();
 hipError_t launch_grad_d128w(const GradArgs& a, bool split, hipStream_t s);
 bool ns_mfma_shape_ok(int d, int h);
 // Muon update tail of one chunk and the query read of the same chunk (from
