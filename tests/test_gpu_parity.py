@@ -72,8 +72,8 @@ SMALL_CASES = [
     # bf16 at d = 128 with four 128-unit hidden slices, ragged chunks
     small("lm", name="lm-h512-ragged", B=1, H=2, h=512, T_kv=3000, T_q=600, chunk_kv=1500,
           chunk_q=300),
-    # d = 128 with bf16 products on the two-wavefront kernel (64-unit hidden slices): six
-    # slices (h = 384) with ragged chunks, and two (h = 128)
+    # d = 128 with bf16 products on the two-wavefront kernel (128-unit hidden slices): three
+    # slices (h = 384) with ragged chunks, and one (h = 128)
     small("lm", name="lm-h384-ragged", B=1, H=2, h=384, T_kv=3000, T_q=600, chunk_kv=1500,
           chunk_q=300),
     small("lm", name="lm-h128", B=2, H=1, h=128, T_kv=2048, T_q=512, chunk_kv=1024, chunk_q=256),
